@@ -1,0 +1,182 @@
+"""Python binding of libfrontier_bfs.so: level-synchronous, frontier-based BFS
+over an int32 CSR graph on one MI355X (gfx950).
+
+Argument marshalling only: every step of the search runs in the library's HIP
+kernels.  The functions mirror the C ABI in ``include/frontier_bfs.h``; PyTorch
+supplies device memory (int32 CUDA tensors) and streams.  There is no CPU
+fallback: if the library is not built, or no GPU is present, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfrontier_bfs.so")
+
+BFS_EINVAL, BFS_EHIP, BFS_ENOMEM, BFS_EDEVICE = -1, -2, -3, -4
+DIR_AUTO, DIR_PUSH, DIR_PULL = 0, 1, 2
+ADV_AUTO, ADV_BINNED, ADV_EDGE = 0, 1, 2
+LOOP_DEVICE, LOOP_HOST = 0, 1
+
+EXPORTS = ("bfs_graph_create", "bfs_run", "bfs_graph_destroy", "bfs_last_error",
+           "bfs_set_policy", "bfs_last_run_stats", "bfs_graph_info")
+
+_lib = None
+
+
+class BfsError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+def load():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        lib.bfs_graph_create.argtypes = [i32, P, P]
+        lib.bfs_graph_create.restype = P
+        lib.bfs_run.argtypes = [P, i32, P, P, P, P]
+        lib.bfs_run.restype = i32
+        lib.bfs_graph_destroy.argtypes = [P]
+        lib.bfs_graph_destroy.restype = None
+        lib.bfs_last_error.argtypes = []
+        lib.bfs_last_error.restype = ctypes.c_char_p
+        lib.bfs_set_policy.argtypes = [P, i32, i32, i32]
+        lib.bfs_set_policy.restype = i32
+        lib.bfs_last_run_stats.argtypes = [P, i32, P, P]
+        lib.bfs_last_run_stats.restype = i32
+        lib.bfs_graph_info.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        lib.bfs_graph_info.restype = i32
+        _lib = lib
+    return _lib
+
+
+def bfs_last_error() -> str:
+    return load().bfs_last_error().decode()
+
+
+def _dev_i32(t, name, numel=None):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 tensor")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} needs at least {numel} elements, has {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr() if t.numel() else None)
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def bfs_graph_create(n, row_ptr, col_idx):
+    """Wrap an int32 CSR graph held in CUDA tensors; returns a raw handle.
+    The tensors are borrowed and must outlive the handle."""
+    rp = _dev_i32(row_ptr, "row_ptr", n + 1)
+    ci = _dev_i32(col_idx, "col_idx")
+    h = load().bfs_graph_create(int(n), rp, ci)
+    if not h:
+        raise BfsError(BFS_EINVAL, bfs_last_error())
+    return h
+
+
+def bfs_run(g, source, dist, parent=None, level_sizes=None, stream=None):
+    """One BFS from `source` into the int32 CUDA tensors; returns L."""
+    L = load().bfs_run(g, int(source), _dev_i32(dist, "dist"), _dev_i32(parent, "parent"),
+                       _dev_i32(level_sizes, "level_sizes"), _stream_handle(stream))
+    if L < 0:
+        raise BfsError(L, bfs_last_error())
+    return L
+
+
+def bfs_graph_destroy(g):
+    if g:
+        load().bfs_graph_destroy(g)
+
+
+def bfs_set_policy(g, direction=DIR_AUTO, advance=ADV_AUTO, loop=LOOP_DEVICE):
+    rc = load().bfs_set_policy(g, int(direction), int(advance), int(loop))
+    if rc < 0:
+        raise BfsError(rc, bfs_last_error())
+
+
+def bfs_last_run_stats(g, cap=1 << 22):
+    """(L, dir[int8, per level: 0 top-down, 1 bottom-up], frontier_edges[int64])."""
+    L0 = load().bfs_last_run_stats(g, 0, None, None)
+    if L0 < 0:
+        raise BfsError(L0, bfs_last_error())
+    cnt = min(L0, cap)
+    d = np.zeros(cnt, np.int8)
+    fe = np.zeros(cnt, np.int64)
+    L = load().bfs_last_run_stats(g, cnt, d.ctypes.data_as(ctypes.c_void_p),
+                                  fe.ctypes.data_as(ctypes.c_void_p))
+    if L < 0:
+        raise BfsError(L, bfs_last_error())
+    return L, d, fe
+
+
+def bfs_graph_info(g):
+    m, srt, sym, mx = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    rc = load().bfs_graph_info(g, ctypes.byref(m), ctypes.byref(srt), ctypes.byref(sym),
+                               ctypes.byref(mx))
+    if rc < 0:
+        raise BfsError(rc, bfs_last_error())
+    return {"m": m.value, "sorted_rows": bool(srt.value), "symmetric": bool(sym.value),
+            "max_degree": mx.value}
+
+
+class BfsGraph:
+    """Owns a handle and keeps the borrowed CSR tensors alive with it."""
+
+    def __init__(self, row_ptr, col_idx):
+        self.row_ptr = row_ptr
+        self.col_idx = col_idx
+        self.n = int(row_ptr.numel() - 1)
+        self.handle = bfs_graph_create(self.n, row_ptr, col_idx)
+
+    def run(self, source, dist, parent=None, level_sizes=None, stream=None):
+        return bfs_run(self.handle, source, dist, parent, level_sizes, stream)
+
+    def set_policy(self, direction=DIR_AUTO, advance=ADV_AUTO, loop=LOOP_DEVICE):
+        bfs_set_policy(self.handle, direction, advance, loop)
+
+    def stats(self):
+        return bfs_last_run_stats(self.handle)
+
+    def info(self):
+        return bfs_graph_info(self.handle)
+
+    def close(self):
+        if self.handle:
+            bfs_graph_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,364 @@
+// C ABI of the gfx950 BFS library: graph handle, validation, workspace and
+// the device-resident level loop.  The interface is documented in
+// include/frontier_bfs.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "bfs_internal.h"
+#include "frontier_bfs.h"
+
+using namespace fbfs;
+
+namespace {
+
+thread_local std::string g_err;
+
+void set_error(const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+}
+
+struct HostCtl {
+    int32_t done, L, err, err_info;
+};
+
+}  // namespace
+
+struct bfs_graph {
+    int device = 0;
+    int32_t n = 0;
+    int32_t m = 0;
+    const int32_t *row_ptr = nullptr;
+    const int32_t *col_idx = nullptr;
+    int32_t sorted = 0, symmetric = 0, max_degree = 0;
+    int grid = 0;
+    uint32_t *visited = nullptr, *vis_init = nullptr, *fbm0 = nullptr, *fbm1 = nullptr;
+    Seg *q0 = nullptr, *q1 = nullptr, *t0 = nullptr, *t1 = nullptr;
+    int32_t *ts0 = nullptr, *ts1 = nullptr;
+    int64_t qcap = 0, tcap = 0, tscap = 0;
+    unsigned long long *ctr = nullptr;
+    Ctl *ctl = nullptr;
+    int8_t *st_dir = nullptr;
+    int64_t *st_fdeg = nullptr;
+    int32_t st_cap = 0;
+    HostCtl *host_ctl = nullptr;   // pinned
+    GraphFacts *facts = nullptr;   // device, create only
+    int32_t pol_dir = BFS_DIR_AUTO, pol_adv = BFS_ADV_AUTO, pol_loop = BFS_LOOP_DEVICE;
+    int32_t last_L = 0;
+};
+
+namespace {
+
+#define HIP_TRY(expr, code)                                                              \
+    do {                                                                                 \
+        hipError_t e_ = (expr);                                                          \
+        if (e_ != hipSuccess) {                                                          \
+            set_error("%s failed: %s", #expr, hipGetErrorString(e_));                   \
+            return code;                                                                 \
+        }                                                                                \
+    } while (0)
+
+template <typename T>
+hipError_t dalloc(T **p, size_t count) {
+    if (count == 0) count = 1;
+    return hipMalloc(reinterpret_cast<void **>(p), count * sizeof(T));
+}
+
+void free_all(bfs_graph *g) {
+    void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->q0, g->q1, g->t0, g->t1,
+                    g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts};
+    for (void *p : ptrs)
+        if (p) (void)hipFree(p);
+    if (g->host_ctl) (void)hipHostFree(g->host_ctl);
+}
+
+int alloc_workspace(bfs_graph *g) {
+    const int64_t n = g->n, m = g->m;
+    const int64_t nwp = (n + 63) / 64;
+    g->qcap = n;
+    g->tcap = m / TILE + m / T_WG + 1;
+    g->tscap = m / EB_TE + 2;
+    g->st_cap = (int32_t)((n + 1) < (1 << 22) ? (n + 1) : (1 << 22));
+    struct {
+        hipError_t e;
+        const char *what;
+    } r[] = {
+        {dalloc(&g->visited, 2 * nwp), "visited bitmap"},
+        {dalloc(&g->vis_init, 2 * nwp), "visited template"},
+        {dalloc(&g->fbm0, 2 * nwp), "frontier bitmap"},
+        {dalloc(&g->fbm1, 2 * nwp), "frontier bitmap"},
+        {dalloc(&g->q0, (size_t)STRIPES * g->qcap), "frontier queue"},
+        {dalloc(&g->q1, (size_t)STRIPES * g->qcap), "frontier queue"},
+        {dalloc(&g->t0, (size_t)STRIPES * g->tcap), "tile queue"},
+        {dalloc(&g->t1, (size_t)STRIPES * g->tcap), "tile queue"},
+        {dalloc(&g->ts0, (size_t)NLISTS * STRIPES * g->tscap), "tile start table"},
+        {dalloc(&g->ts1, (size_t)NLISTS * STRIPES * g->tscap), "tile start table"},
+        {dalloc(&g->ctr, (size_t)NSLOTS * NCTR * CTR_STRIDE), "counters"},
+        {dalloc(&g->ctl, 1), "control block"},
+        {dalloc(&g->st_dir, (size_t)g->st_cap), "level stats"},
+        {dalloc(&g->st_fdeg, (size_t)g->st_cap), "level stats"},
+    };
+    for (auto &x : r) {
+        if (x.e != hipSuccess) {
+            set_error("allocating the %s for n=%d m=%d failed: %s", x.what, g->n, g->m,
+                      hipGetErrorString(x.e));
+            return x.e == hipErrorOutOfMemory ? BFS_ENOMEM : BFS_EHIP;
+        }
+    }
+    HIP_TRY(hipMemset(g->ctr, 0, (size_t)NSLOTS * NCTR * CTR_STRIDE * sizeof(unsigned long long)),
+            BFS_EHIP);
+    HIP_TRY(hipMemset(g->ctl, 0, sizeof(Ctl)), BFS_EHIP);
+    HIP_TRY(hipHostMalloc(reinterpret_cast<void **>(&g->host_ctl), sizeof(HostCtl), hipHostMallocDefault),
+            BFS_EHIP);
+    return 0;
+}
+
+int validate_and_classify(bfs_graph *g) {
+    const int32_t n = g->n;
+    int32_t rp0 = -1, rpn = -1;
+    HIP_TRY(hipMemcpy(&rp0, g->row_ptr, sizeof(int32_t), hipMemcpyDeviceToHost), BFS_EHIP);
+    HIP_TRY(hipMemcpy(&rpn, g->row_ptr + n, sizeof(int32_t), hipMemcpyDeviceToHost), BFS_EHIP);
+    if (rp0 != 0) {
+        set_error("invalid CSR: row_ptr[0] = %d, expected 0", rp0);
+        return BFS_EINVAL;
+    }
+    if (rpn < 0) {
+        set_error("invalid CSR: row_ptr[%d] = %d is negative", n, rpn);
+        return BFS_EINVAL;
+    }
+    g->m = rpn;
+    if (g->m > 0 && !g->col_idx) {
+        set_error("col_idx must be a device pointer when row_ptr[n] = %d > 0", g->m);
+        return BFS_EINVAL;
+    }
+    HIP_TRY(dalloc(&g->facts, 1), BFS_ENOMEM);
+    GraphFacts h;
+    std::memset(&h, 0, sizeof(h));
+    h.bad_row = ~0ull;
+    h.bad_col = ~0ull;
+    HIP_TRY(hipMemcpy(g->facts, &h, sizeof(h), hipMemcpyHostToDevice), BFS_EHIP);
+    HIP_TRY(launch_check_rows(g->row_ptr, n, g->facts, 0), BFS_EHIP);
+    HIP_TRY(hipMemcpy(&h, g->facts, sizeof(h), hipMemcpyDeviceToHost), BFS_EHIP);
+    if (h.bad_row != ~0ull) {
+        set_error("invalid CSR: row_ptr is decreasing at index %llu (row_ptr[i] > row_ptr[i+1])",
+                  (unsigned long long)h.bad_row);
+        return BFS_EINVAL;
+    }
+    g->max_degree = h.max_degree;
+    if (g->m > 0) {
+        HIP_TRY(launch_check_cols(g->row_ptr, g->col_idx, n, g->facts, 0), BFS_EHIP);
+        HIP_TRY(hipMemcpy(&h, g->facts, sizeof(h), hipMemcpyDeviceToHost), BFS_EHIP);
+        if (h.bad_col != ~0ull) {
+            set_error("invalid CSR: col_idx[%llu] is outside [0, %d)", (unsigned long long)h.bad_col, n);
+            return BFS_EINVAL;
+        }
+    }
+    g->sorted = h.unsorted ? 0 : 1;
+    g->symmetric = 0;
+    if (g->sorted) {
+        if (g->m > 0) {
+            HIP_TRY(launch_check_symmetry(g->row_ptr, g->col_idx, n, g->facts, 0), BFS_EHIP);
+            HIP_TRY(hipMemcpy(&h, g->facts, sizeof(h), hipMemcpyDeviceToHost), BFS_EHIP);
+        }
+        g->symmetric = h.asymmetric ? 0 : 1;
+    }
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bfs_last_error(void) { return g_err.c_str(); }
+
+bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *col_idx) {
+    g_err.clear();
+    if (n < 1) {
+        set_error("n = %d: need at least one vertex", n);
+        return nullptr;
+    }
+    if (!row_ptr) {
+        set_error("row_ptr must be a device pointer (got NULL)");
+        return nullptr;
+    }
+    bfs_graph *g = new (std::nothrow) bfs_graph();
+    if (!g) {
+        set_error("host allocation failed");
+        return nullptr;
+    }
+    g->n = n;
+    g->row_ptr = row_ptr;
+    g->col_idx = col_idx;
+    if (hipGetDevice(&g->device) != hipSuccess) {
+        set_error("no HIP device");
+        delete g;
+        return nullptr;
+    }
+    int rc = validate_and_classify(g);
+    if (rc == 0) rc = alloc_workspace(g);
+    if (rc == 0) {
+        hipError_t e = launch_build_vis_init(row_ptr, n, g->symmetric, g->vis_init, 0);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) {
+            set_error("building the visited template failed: %s", hipGetErrorString(e));
+            rc = BFS_EHIP;
+        }
+    }
+    if (rc == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, g->device) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        g->grid = cus * level_kernel_blocks_per_cu();
+    }
+    if (rc != 0) {
+        free_all(g);
+        delete g;
+        return nullptr;
+    }
+    return g;
+}
+
+void bfs_graph_destroy(bfs_graph *g) {
+    if (!g) return;
+    (void)hipSetDevice(g->device);
+    (void)hipDeviceSynchronize();
+    free_all(g);
+    delete g;
+}
+
+int32_t bfs_set_policy(bfs_graph *g, int32_t direction, int32_t advance, int32_t loop) {
+    if (!g) {
+        set_error("NULL graph handle");
+        return BFS_EINVAL;
+    }
+    if (direction < BFS_DIR_AUTO || direction > BFS_DIR_PULL || advance < BFS_ADV_AUTO ||
+        advance > BFS_ADV_EDGE || loop < BFS_LOOP_DEVICE || loop > BFS_LOOP_HOST) {
+        set_error("unknown policy (direction %d, advance %d, loop %d)", direction, advance, loop);
+        return BFS_EINVAL;
+    }
+    if (direction == BFS_DIR_PULL && !g->symmetric) {
+        set_error("pull-only needs a symmetric graph with sorted rows (this graph is not)");
+        return BFS_EINVAL;
+    }
+    g->pol_dir = direction;
+    g->pol_adv = advance;
+    g->pol_loop = loop;
+    return 0;
+}
+
+int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent_out,
+                int32_t *level_sizes_out, hipStream_t stream) {
+    g_err.clear();
+    if (!g) {
+        set_error("NULL graph handle");
+        return BFS_EINVAL;
+    }
+    if (!dist_out) {
+        set_error("dist_out is required");
+        return BFS_EINVAL;
+    }
+    if (source < 0 || source >= g->n) {
+        set_error("source %d is outside [0, %d)", source, g->n);
+        return BFS_EINVAL;
+    }
+    HIP_TRY(hipSetDevice(g->device), BFS_EHIP);
+    Params P;
+    std::memset(&P, 0, sizeof(P));
+    P.row_ptr = g->row_ptr;
+    P.col_idx = g->col_idx;
+    P.n = g->n;
+    P.m = g->m;
+    P.nwp = (int32_t)(((int64_t)g->n + 63) / 64);
+    P.source = source;
+    P.dist = dist_out;
+    P.parent = parent_out;
+    P.level_sizes = level_sizes_out;
+    P.visited = g->visited;
+    P.vis_init = g->vis_init;
+    P.fbm0 = g->fbm0;
+    P.fbm1 = g->fbm1;
+    P.q0 = g->q0;
+    P.q1 = g->q1;
+    P.t0 = g->t0;
+    P.t1 = g->t1;
+    P.ts0 = g->ts0;
+    P.ts1 = g->ts1;
+    P.qcap = g->qcap;
+    P.tcap = g->tcap;
+    P.tscap = g->tscap;
+    P.ctr = g->ctr;
+    P.ctl = g->ctl;
+    P.st_dir = g->st_dir;
+    P.st_fdeg = g->st_fdeg;
+    P.st_cap = g->st_cap;
+    P.symmetric = g->symmetric;
+    P.pol_dir = g->pol_dir;
+    P.pol_adv = g->pol_adv;
+
+    HIP_TRY(launch_init(P, g->grid, stream), BFS_EHIP);
+    const bool host_loop = g->pol_loop == BFS_LOOP_HOST;
+    int64_t k = 0;
+    int64_t batch = host_loop ? 1 : 8;
+    const int64_t kmax = (int64_t)g->n + 1;   // L <= n, so level n finds an empty frontier
+    for (;;) {
+        for (int64_t i = 0; i < batch && k <= kmax; ++i, ++k)
+            HIP_TRY(launch_level(P, (int32_t)k, g->grid, stream), BFS_EHIP);
+        HIP_TRY(hipMemcpyAsync(g->host_ctl, g->ctl, sizeof(HostCtl), hipMemcpyDeviceToHost, stream),
+                BFS_EHIP);
+        HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+        const HostCtl h = *g->host_ctl;
+        if (h.err) {
+            set_error("device reported internal error %d (info %d)", h.err, h.err_info);
+            return BFS_EDEVICE;
+        }
+        if (h.done) {
+            g->last_L = h.L;
+            return h.L;
+        }
+        if (k > kmax) {
+            set_error("search did not terminate after %lld levels", (long long)k);
+            return BFS_EDEVICE;
+        }
+        if (!host_loop && batch < 1024) batch *= 2;
+    }
+}
+
+int32_t bfs_last_run_stats(const bfs_graph *g, int32_t cap, int8_t *dir, int64_t *frontier_edges) {
+    if (!g || cap < 0) {
+        set_error("NULL graph handle or negative capacity");
+        return BFS_EINVAL;
+    }
+    int64_t cnt = g->last_L;
+    if (cnt > cap) cnt = cap;
+    if (cnt > g->st_cap) cnt = g->st_cap;
+    if (cnt > 0 && dir)
+        HIP_TRY(hipMemcpy(dir, g->st_dir, (size_t)cnt, hipMemcpyDeviceToHost), BFS_EHIP);
+    if (cnt > 0 && frontier_edges)
+        HIP_TRY(hipMemcpy(frontier_edges, g->st_fdeg, (size_t)cnt * sizeof(int64_t), hipMemcpyDeviceToHost),
+                BFS_EHIP);
+    return g->last_L;
+}
+
+int32_t bfs_graph_info(const bfs_graph *g, int64_t *m, int32_t *sorted_rows, int32_t *symmetric,
+                       int32_t *max_degree) {
+    if (!g) {
+        set_error("NULL graph handle");
+        return BFS_EINVAL;
+    }
+    if (m) *m = g->m;
+    if (sorted_rows) *sorted_rows = g->sorted;
+    if (symmetric) *symmetric = g->symmetric;
+    if (max_degree) *max_degree = g->max_degree;
+    return 0;
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Internal layout shared by the gfx950 kernels (bfs_device.hip) and the C ABI
+// layer (bfs_api.hip).  Not installed; the public interface is
+// include/frontier_bfs.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fbfs {
+
+// ---- launch geometry and bin thresholds (gfx950: 64-lane wavefronts) -------
+constexpr int WAVE = 64;
+constexpr int BLOCK = 512;               // threads per workgroup
+constexpr int WAVES = BLOCK / WAVE;      // wavefronts per workgroup
+constexpr int STRIPES = 8;               // counter / queue stripes (spread atomics)
+constexpr int T_LANE = 32;               // degree < T_LANE: one lane walks the list
+constexpr int T_WG = BLOCK;              // T_LANE <= degree < T_WG: one wavefront
+constexpr int TILE = 4 * BLOCK;          // degree >= T_WG: split into tiles of TILE edges,
+                                         // one workgroup per tile
+constexpr int CAP = 2048;                // LDS staging capacity for new frontier vertices
+constexpr int EB_TE = 2048;              // edges per tile of the edge-balanced advance
+constexpr int BU_LANE_SCAN = 32;         // bottom-up: entries a lane scans alone before
+                                         // its list is handed to the whole wavefront
+
+// lists of a frontier queue
+constexpr int L_SMALL = 0;               // degree in [1, T_LANE)
+constexpr int L_MID = 1;                 // degree in [T_LANE, T_WG)
+constexpr int L_TILE = 2;                // pieces of vertices with degree >= T_WG
+constexpr int NLISTS = 3;
+
+// counters of one level slot: NLISTS*STRIPES list counters, then STRIPES
+// vertex counters; each 64-bit counter sits alone in 256 bytes.
+constexpr int NCTR = 32;
+constexpr int CTR_STRIDE = 32;           // in uint64 units
+constexpr int VC_BASE = NLISTS * STRIPES;
+constexpr int NSLOTS = 4;                // ring of level slots
+
+// direction codes stored per level
+constexpr int DIR_TD = 0;
+constexpr int DIR_BU = 1;
+
+// One frontier segment: vertex v's adjacency piece col_idx[beg, beg+len), and
+// off = the exclusive prefix of len over its list stripe (the frontier-degree
+// scan used by the edge-balanced advance).
+struct __align__(16) Seg {
+    int32_t v, beg, len, off;
+};
+
+// Per-level scalars, written once per level by workgroup 0.
+struct SlotInfo {
+    int32_t dir;          // direction this level ran in
+    int32_t wbits;        // this level's new vertices were also set in the next bitmap
+    int32_t input_bm;     // this level's frontier came as a bitmap only
+    int32_t pad;
+    int64_t reached_before;  // vertices in levels < this one
+};
+
+struct Ctl {
+    int32_t done;         // set by the kernel that finds an empty frontier
+    int32_t L;            // number of non-empty levels
+    int32_t err;          // nonzero: internal limit exceeded (see ERR_*)
+    int32_t err_info;
+    SlotInfo slot[NSLOTS];
+};
+
+constexpr int ERR_QUEUE_OVERFLOW = 1;
+constexpr int ERR_TILE_OVERFLOW = 2;
+constexpr int ERR_TSTART_OVERFLOW = 3;
+
+struct Params {
+    const int32_t *row_ptr;
+    const int32_t *col_idx;
+    int32_t n;
+    int32_t m;
+    int32_t nwp;              // 64-vertex word pairs: ceil(n / 64)
+    int32_t source;
+    int32_t *dist;
+    int32_t *parent;          // may be null
+    int32_t *level_sizes;     // may be null
+    uint32_t *visited;        // 2*nwp words
+    const uint32_t *vis_init; // 2*nwp words: isolated vertices (symmetric graphs) + padding
+    uint32_t *fbm0, *fbm1;    // frontier bitmaps, 2*nwp words each
+    Seg *q0, *q1;             // STRIPES regions of qcap segments (small from the front,
+                              // mid from the back)
+    Seg *t0, *t1;             // STRIPES regions of tcap tiles
+    int32_t *ts0, *ts1;       // edge-balanced tile starts: NLISTS*STRIPES regions of tscap
+    int64_t qcap, tcap, tscap;
+    unsigned long long *ctr;  // NSLOTS * NCTR counters, CTR_STRIDE apart
+    Ctl *ctl;
+    int8_t *st_dir;           // per-level stats, st_cap entries
+    int64_t *st_fdeg;
+    int32_t st_cap;
+    int32_t symmetric;
+    int32_t pol_dir;          // BFS_DIR_*
+    int32_t pol_adv;          // BFS_ADV_*
+};
+
+// host-side launch helpers (bfs_device.hip)
+hipError_t launch_init(const Params &P, int grid, hipStream_t s);
+hipError_t launch_level(const Params &P, int32_t level, int grid, hipStream_t s);
+int level_kernel_blocks_per_cu();
+
+// graph validation / classification (bfs_device.hip)
+struct GraphFacts {
+    unsigned long long bad_row;   // first index i with row_ptr[i] > row_ptr[i+1], or ~0
+    unsigned long long bad_col;   // first entry e with col_idx[e] outside [0,n), or ~0
+    uint32_t unsorted;            // some row is not ascending
+    uint32_t asymmetric;          // some entry u->v has no v->u (sorted rows only)
+    int32_t max_degree;
+    int32_t pad;
+};
+hipError_t launch_check_rows(const int32_t *row_ptr, int32_t n, GraphFacts *f, hipStream_t s);
+hipError_t launch_check_cols(const int32_t *row_ptr, const int32_t *col_idx, int32_t n,
+                             GraphFacts *f, hipStream_t s);
+hipError_t launch_check_symmetry(const int32_t *row_ptr, const int32_t *col_idx, int32_t n,
+                                 GraphFacts *f, hipStream_t s);
+hipError_t launch_build_vis_init(const int32_t *row_ptr, int32_t n, int32_t mark_isolated,
+                                 uint32_t *vis_init, hipStream_t s);
+
+}  // namespace fbfs

@@ -1,0 +1,136 @@
+/*
+ * frontier_bfs.h -- level-synchronous, frontier-based BFS over an int32 CSR
+ * graph on one MI355X (gfx950), behind a plain C ABI.
+ *
+ * What is computed.  Level 0 is {source}; level k+1 holds the vertices not yet
+ * reached that are out-neighbours of level k; the search stops at the first
+ * empty level ("Day 38 - Graph traversal on a GPU", section "What a
+ * level-synchronous search actually launches"; PMPP ch.15 notes, section 15.2).
+ * The graph is CSR: the neighbours of u are col_idx[row_ptr[u] .. row_ptr[u+1])
+ * (PMPP ch.15 notes, section 15.1).  Edges are followed in CSR direction, so a
+ * directed graph is allowed; self-loops and duplicate entries are allowed and
+ * change nothing.
+ *
+ * Memory.  Every array argument is DEVICE memory of the current HIP device
+ * (for example a torch tensor's data_ptr()), int32, contiguous.  The graph
+ * arrays are borrowed: they must stay alive and unmodified until
+ * bfs_graph_destroy.  The library owns its workspace (queues, bitmaps,
+ * counters), allocated at bfs_graph_create and freed at bfs_graph_destroy.
+ *
+ * Streams.  bfs_run enqueues all its work on `stream` (0 = the null stream)
+ * and returns after that work has finished.  One handle runs one search at a
+ * time; separate handles may run concurrently on separate streams.
+ *
+ * Errors.  Functions never exit the process.  On failure they return NULL or a
+ * negative code, and bfs_last_error() (thread-local) describes the first
+ * problem found, naming the offending index where there is one.
+ */
+#ifndef FRONTIER_BFS_H
+#define FRONTIER_BFS_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes of bfs_run / bfs_set_policy / bfs_last_run_stats. */
+#define BFS_EINVAL  (-1)  /* bad argument: NULL handle/output, source out of range, bad policy */
+#define BFS_EHIP    (-2)  /* a HIP call failed; the message carries hipGetErrorString      */
+#define BFS_ENOMEM  (-3)  /* device allocation failed                                        */
+#define BFS_EDEVICE (-4)  /* a kernel reported an internal limit or a corrupted graph        */
+
+typedef struct bfs_graph bfs_graph;   /* opaque handle */
+
+/*
+ * Wraps a CSR graph for searching.
+ *   n        number of vertices, 1 <= n < 2^31
+ *   row_ptr  device, n+1 entries: row_ptr[0] = 0, non-decreasing,
+ *            row_ptr[n] = number of CSR entries m < 2^31
+ *   col_idx  device, m entries, each in [0, n) (may be NULL when m = 0)
+ * The arrays are validated on the device (the first bad index is named in
+ * bfs_last_error), and the graph is classified: rows sorted or not, and
+ * symmetric or not.  The bottom-up (pull) pass is enabled only on symmetric
+ * graphs, because pulling needs in-edges (Gunrock reading guide, question 3).
+ * Returns NULL on invalid input or allocation failure.  Uses the current
+ * device and the null stream; synchronises before returning.
+ */
+bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *col_idx);
+
+/*
+ * One breadth-first search from `source`.
+ *   dist_out         device, n entries, required: hop count from source, -1 if
+ *                    unreached (the sentinel of Chapter 22 and bfs.cu).
+ *   parent_out       device, n entries, or NULL to skip: parent[source] =
+ *                    source; for a reached v, a vertex p with dist[p] =
+ *                    dist[v]-1 and v in adj(p) (any such p: which one may
+ *                    vary between runs); -1 if unreached.
+ *   level_sizes_out  device, capacity n entries, or NULL: entry k = number of
+ *                    vertices at distance k, for k < L; entries from L on are
+ *                    left untouched.
+ *   stream           HIP stream for all work (0 = null stream).
+ * Returns L >= 1, the number of non-empty levels (= max dist + 1), or a
+ * negative BFS_E* code.  On BFS_EINVAL the outputs are untouched.
+ */
+int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent_out,
+                int32_t *level_sizes_out, hipStream_t stream);
+
+/* Frees the workspace.  NULL is a no-op.  Synchronises the device first. */
+void bfs_graph_destroy(bfs_graph *g);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char *bfs_last_error(void);
+
+/* ---- measurement and test hooks (results never depend on them) --------- */
+
+/* Direction policy: automatic switching, push (top-down) only, pull
+ * (bottom-up) only.  Pull needs a symmetric graph. */
+#define BFS_DIR_AUTO 0
+#define BFS_DIR_PUSH 1
+#define BFS_DIR_PULL 2
+/* Top-down advance: automatic, degree-binned (lane / wavefront / workgroup,
+ * hubs split across workgroups), edge-balanced (frontier-degree scan plus
+ * tile partition by search over the scan). */
+#define BFS_ADV_AUTO   0
+#define BFS_ADV_BINNED 1
+#define BFS_ADV_EDGE   2
+
+/* Level loop: device-resident (level launches are enqueued ahead in growing
+ * batches and read the frontier size from device memory; the host waits once
+ * per batch), or host-driven (the host waits for every level's count before
+ * the next launch, as bfs.cu's runBfs in the Day 38 program does). */
+#define BFS_LOOP_DEVICE 0
+#define BFS_LOOP_HOST   1
+
+/*
+ * Forces a policy for later bfs_run calls on this handle.  dist, L and the
+ * level sizes are the same under every policy; only speed differs.
+ * Returns 0, or BFS_EINVAL (unknown value, or pull on a graph that is not
+ * symmetric).
+ */
+int32_t bfs_set_policy(bfs_graph *g, int32_t direction, int32_t advance, int32_t loop);
+
+/*
+ * Per-level record of the last bfs_run on this handle, for the byte model and
+ * tests.  For k < min(L, cap): dir[k] = 0 for a top-down level, 1 for a
+ * bottom-up level; frontier_edges[k] = sum of degrees of level k's vertices.
+ * Either array may be NULL.  Host memory.  Returns L of that run (0 if none
+ * yet), or a negative code.
+ */
+int32_t bfs_last_run_stats(const bfs_graph *g, int32_t cap, int8_t *dir,
+                           int64_t *frontier_edges);
+
+/*
+ * Graph facts found by bfs_graph_create (host memory, any may be NULL):
+ * CSR entry count, rows-sorted flag, symmetric flag, maximum degree.
+ * Returns 0 or BFS_EINVAL.
+ */
+int32_t bfs_graph_info(const bfs_graph *g, int64_t *m, int32_t *sorted_rows,
+                       int32_t *symmetric, int32_t *max_degree);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FRONTIER_BFS_H */

@@ -1,0 +1,136 @@
+"""HIP path vs the oracle, through the C ABI: dist, L and level sizes
+bit-exact; parents valid BFS parents; every policy (direction x advance x
+loop).  Graphs: the pages' worked graphs, tiny random graphs, closed forms,
+scaled-down and full-size workloads."""
+import numpy as np
+import pytest
+
+import graphgen as gg
+import oracle
+from gpu_util import check_graph, run_hip, sorted_rows_copy, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_chapter22_graph():
+    g = gg.chapter22_graph()
+    check_graph(g, sources=range(g.n))
+
+
+def test_pmpp_graph():
+    g = gg.pmpp_graph()
+    check_graph(g, sources=range(g.n))
+
+
+@pytest.mark.parametrize("block", range(6))
+def test_tiny_random(block):
+    for seed in range(block * 50, block * 50 + 50):
+        g = gg.tiny_random(seed)
+        check_graph(g, label=f"tiny seed {seed}")
+        if g.symmetric:
+            check_graph(sorted_rows_copy(g), label=f"tiny seed {seed} sorted")
+
+
+def test_closed_forms():
+    for g in (gg.path_graph(1), gg.path_graph(2), gg.path_graph(3000), gg.star_graph(5000),
+              gg.complete_graph(300), gg.grid_full(97, 61),
+              gg.disjoint_union(gg.path_graph(50), gg.complete_graph(40))):
+        check_graph(g)
+
+
+def test_directed_random():
+    for n, deg, seed in ((1000, 3, 1), (20000, 8, 2), (5000, 40, 3)):
+        check_graph(gg.random_directed(n, deg, seed))
+
+
+@pytest.mark.parametrize("scale", [10, 14, 17])
+def test_rmat_scaled(scale):
+    g = gg.rmat(scale, 16, seed=100 + scale, nsrc=3)
+    check_graph(g)
+
+
+def test_hub_source():
+    """Source of maximum degree on an R-MAT graph: tiles split over workgroups."""
+    g = gg.rmat(16, 16, seed=7, nsrc=1)
+    s = int(np.argmax(np.diff(g.row_ptr)))
+    check_graph(g, sources=[s])
+
+
+def test_c1_workload():
+    g = gg.c1_chung_lu()
+    check_graph(g, sources=list(g.sources) + [0, g.n - 1])
+
+
+def test_c2_workload_sampled():
+    g = gg.c2_rmat20(nsrc=64)
+    check_graph(g, sources=g.sources[:4])
+    check_graph(g, sources=g.sources[4:12], policies=["auto"])
+
+
+def test_optional_outputs():
+    import torch
+    import frontier_bfs_csr_amd as fb
+    g = gg.rmat(12, 16, seed=3, nsrc=2)
+    rp, ci = to_dev(g)
+    with fb.BfsGraph(rp, ci) as bg:
+        for wp, ws in ((False, False), (True, False), (False, True)):
+            L, dist, parent, sizes = run_hip(bg, g.n, g.sources[0], wp, ws)
+            ref = oracle.bfs(g.row_ptr, g.col_idx, int(g.sources[0]))
+            assert L == ref[3] and (dist == ref[0]).all()
+
+
+def test_repeated_runs_and_two_handles():
+    import torch
+    import frontier_bfs_csr_amd as fb
+    g1 = gg.rmat(13, 16, seed=21, nsrc=3)
+    g2 = gg.grid_full(50, 40)
+    r1, c1 = to_dev(g1)
+    r2, c2 = to_dev(g2)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with fb.BfsGraph(r1, c1) as b1, fb.BfsGraph(r2, c2) as b2:
+        for rep in range(3):
+            for s in g1.sources:
+                d1 = torch.empty(g1.n, dtype=torch.int32, device="cuda")
+                d2 = torch.empty(g2.n, dtype=torch.int32, device="cuda")
+                with torch.cuda.stream(s1):
+                    L1 = b1.run(int(s), d1, stream=s1)
+                with torch.cuda.stream(s2):
+                    L2 = b2.run(0, d2, stream=s2)
+                torch.cuda.synchronize()
+                ref1 = oracle.bfs(g1.row_ptr, g1.col_idx, int(s))
+                assert L1 == ref1[3] and (d1.cpu().numpy() == ref1[0]).all()
+                assert L2 == 50 + 40 - 1
+                rr, cc = np.divmod(np.arange(g2.n), 50)
+                assert (d2.cpu().numpy() == rr + cc).all()
+
+
+def test_invalid_graphs_rejected():
+    import torch
+    import frontier_bfs_csr_amd as fb
+    cases = [
+        (np.array([1, 2, 3], np.int32), np.array([0, 1, 0], np.int32), "row_ptr[0]"),
+        (np.array([0, 2, 1, 3], np.int32), np.array([1, 2, 0], np.int32), "decreasing at index 1"),
+        (np.array([0, 1, 2], np.int32), np.array([1, 5], np.int32), "col_idx[1]"),
+        (np.array([0, 1, 2], np.int32), np.array([-1, 0], np.int32), "col_idx[0]"),
+    ]
+    for rp, ci, msg in cases:
+        with pytest.raises(fb.BfsError) as ei:
+            fb.bfs_graph_create(rp.shape[0] - 1, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda())
+        assert msg in str(ei.value), (msg, str(ei.value))
+
+
+def test_run_argument_errors():
+    import torch
+    import frontier_bfs_csr_amd as fb
+    g = gg.chapter22_graph()
+    rp, ci = to_dev(g)
+    with fb.BfsGraph(rp, ci) as bg:
+        d = torch.full((g.n,), 9, dtype=torch.int32, device="cuda")
+        for bad in (-1, g.n):
+            with pytest.raises(fb.BfsError) as ei:
+                bg.run(bad, d)
+            assert ei.value.code == fb.BFS_EINVAL
+        assert (d.cpu().numpy() == 9).all()   # untouched on EINVAL
+        with pytest.raises(fb.BfsError):
+            bg.set_policy(fb.DIR_PULL)         # directed graph: no pull
+        assert not bg.info()["symmetric"]
