@@ -1,0 +1,234 @@
+"""Benchmark: level-synchronous BFS over an int32 CSR graph on one MI355X.
+
+One step = one complete search (initialisation plus every level) from the next
+source of the workload's source list, with the graph already resident in HBM.
+Prints ONE JSON line:
+
+  value       GTEPS = sum over timed steps of the undirected edges in the
+              source's component / wall time of the timed steps
+  roofline    for the dominant kernel (the per-level kernel): algorithmic bytes
+              of all its launches (byte model in
+              frontier_bfs_csr_amd/csrc/bytemodel.c) / its summed launch time
+              from HIP events on the search stream, against 8 TB/s of HBM3E
+  cpu_baseline  the CPU oracle (serial FIFO BFS, one core) on a bounded sample
+              of the same sources, same GTEPS definition
+
+Usage: python bench.py [--gpus 1] [--steps 64] [--warmup 4] [--workload c5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD_DESC = {
+    "c1": "chung_lu_3485: Chung-Lu power-law (exponent 2.1), largest component, max-eccentricity source",
+    "c2": "rmat20_ef16: R-MAT scale 20, edge factor 16, (0.57,0.19,0.19,0.05), symmetrised, deduplicated",
+    "c3": "er_4M_deg16: Erdos-Renyi 4,194,304 vertices, 8n uniform pairs symmetrised",
+    "c4": "grid4096_del5: 4096x4096 4-neighbour grid, 5% edges deleted, largest component, corner source",
+    "c5": "rmat24_ef16: R-MAT scale 24, edge factor 16, (0.57,0.19,0.19,0.05), symmetrised, deduplicated",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_kernel_traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for fn in ("bfs_device.hip", "bfs_internal.h"):
+        with open(os.path.join(ROOT, "frontier_bfs_csr_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per level-kernel launch from the committed PMC summary, if it
+    was taken on the current kernel source for this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def component_edges(deg, dist):
+    """Undirected edges of the source's component: half the reached degrees."""
+    return int(deg[dist >= 0].sum()) // 2
+
+
+def copy_calibration(nbytes):
+    """A plain device copy of known size, for scaling PMC byte counters."""
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOAD_DESC))
+    ap.add_argument("--direction", type=int, default=0, help="0 auto, 1 push, 2 pull")
+    ap.add_argument("--advance", type=int, default=0, help="0 auto, 1 binned, 2 edge-balanced")
+    ap.add_argument("--loop", type=int, default=0, help="0 device-resident, 1 host-driven")
+    ap.add_argument("--no-parent", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="budget of the CPU-oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this BFS build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import torch
+
+    import frontier_bfs_csr_amd as fb
+    import graphgen as gg
+    from frontier_bfs_csr_amd import bytemodel
+
+    t0 = time.time()
+    g = gg.WORKLOADS[args.workload]()
+    print(f"[bench] {args.workload}: n={g.n} m={g.m} sources={len(g.sources)} "
+          f"generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    deg = g.degrees()
+    dev = torch.device("cuda:0")
+    rp = torch.from_numpy(g.row_ptr).to(dev)
+    ci = torch.from_numpy(g.col_idx).to(dev)
+    stream = torch.cuda.current_stream()
+    bg = fb.BfsGraph(rp, ci)
+    bg.set_policy(args.direction, args.advance, args.loop)
+    bg.set_timing(True)
+    dist = torch.empty(g.n, dtype=torch.int32, device=dev)
+    parent = None if args.no_parent else torch.empty(g.n, dtype=torch.int32, device=dev)
+    sizes = torch.empty(g.n, dtype=torch.int32, device=dev)
+    sources = [int(s) for s in g.sources]
+
+    def step(i):
+        return bg.run(sources[i % len(sources)], dist, parent, sizes, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    per_step = []
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ts = time.perf_counter()
+        L = step(i)
+        per_step.append((sources[i % len(sources)], L, time.perf_counter() - ts, *bg.timing()))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    print(f"[bench] timed {args.steps} searches in {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
+
+    # per distinct source: result, directions, byte model, component edges
+    model = {}
+    gpu_dist = {}
+    for s in sorted({p[0] for p in per_step}):
+        L = bg.run(s, dist, parent, sizes, stream)
+        Ls, dirs, _ = bg.stats()
+        d = dist.cpu().numpy()
+        init_b, lvl_b = bytemodel.alg_bytes(g.row_ptr, g.col_idx, d, dirs, with_parent=parent is not None)
+        model[s] = {"L": L, "init": init_b, "levels": int(lvl_b.sum()), "medges": component_edges(deg, d),
+                    "dirs": "".join("TB"[x] for x in dirs)}
+        gpu_dist[s] = d if len(gpu_dist) < 8 else None
+
+    edges = sum(model[s]["medges"] for s, *_ in per_step)
+    value = edges / wall / 1e9
+    level_ms = sum(p[4] for p in per_step)
+    init_ms = sum(p[3] for p in per_step)
+    launches = sum(p[5] for p in per_step)
+    bytes_levels = sum(model[s]["levels"] for s, *_ in per_step)
+    bytes_init = sum(model[s]["init"] for s, *_ in per_step)
+    achieved = bytes_levels / (level_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload)
+    step_gteps = [model[s]["medges"] / t / 1e9 for s, L, t, *_ in per_step]
+
+    cpu = None
+    parity_sample = None
+    if not args.no_cpu_baseline:
+        import oracle   # the CPU baseline leg: the oracle, timed as it stands
+        spent, cedges, cnt, ok = 0.0, 0, 0, True
+        for s in sources:
+            ts = time.perf_counter()
+            ref = oracle.bfs(g.row_ptr, g.col_idx, s)
+            spent += time.perf_counter() - ts
+            cedges += component_edges(deg, ref[0])
+            cnt += 1
+            if s in gpu_dist and gpu_dist[s] is not None:
+                ok = ok and bool((gpu_dist[s] == ref[0]).all())
+            if spent >= args.cpu_seconds:
+                break
+        cpu = {"value": cedges / spent / 1e9, "unit": "GTEPS", "cores": 1, "kind": "oracle",
+               "sample": f"{cnt} of the {len(sources)} sources of the same graph, serial FIFO BFS "
+                         f"(gcc -O2), {spent:.1f} s",
+               "ms_per_bfs": spent / cnt * 1e3}
+        parity_sample = {"sources_compared": sum(1 for s in sources[:cnt] if gpu_dist.get(s) is not None),
+                         "dist_equal": ok}
+
+    s0 = per_step[0][0]
+    out = {
+        "metric": "GTEPS on one MI355X (R-MAT scale 24) + % HBM roofline; ms per BFS",
+        "value": round(value, 4),
+        "unit": "GTEPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_DESC[args.workload], "n": g.n, "m_csr_entries": g.m,
+                   "sources": len(sources), "parent_out": parent is not None,
+                   "policy": {"direction": args.direction, "advance": args.advance, "loop": args.loop}},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "bfs_level_kernel",
+                     "bytes_per_launch": round(bytes_levels / launches),
+                     "avg_launch_us": round(level_ms / launches * 1e3, 3),
+                     "launches": launches},
+        "cpu_baseline": cpu,
+        "detail": {
+            "ms_per_bfs_median": round(float(np.median([p[2] for p in per_step])) * 1e3, 4),
+            "gteps_hmean": round(len(step_gteps) / sum(1.0 / x for x in step_gteps), 4),
+            "init_kernel_us_avg": round(init_ms / args.steps * 1e3, 2),
+            "level_kernels_ms_avg": round(level_ms / args.steps, 4),
+            "alg_GB_per_bfs": round((bytes_levels + bytes_init) / args.steps / 1e9, 4),
+            "whole_bfs_alg_GBps": round((bytes_levels + bytes_init) / wall / 1e9, 1),
+            "levels_first_source": model[s0]["L"],
+            "directions_first_source": model[s0]["dirs"],
+            "parity_sample": parity_sample,
+        },
+    }
+    bg.close()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

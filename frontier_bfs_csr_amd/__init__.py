@@ -22,7 +22,8 @@ ADV_AUTO, ADV_BINNED, ADV_EDGE = 0, 1, 2
 LOOP_DEVICE, LOOP_HOST = 0, 1
 
 EXPORTS = ("bfs_graph_create", "bfs_run", "bfs_graph_destroy", "bfs_last_error",
-           "bfs_set_policy", "bfs_last_run_stats", "bfs_graph_info")
+           "bfs_set_policy", "bfs_last_run_stats", "bfs_set_timing", "bfs_last_run_timing",
+           "bfs_graph_info")
 
 _lib = None
 
@@ -57,6 +58,11 @@ def load():
         lib.bfs_graph_info.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i32),
                                        ctypes.POINTER(i32), ctypes.POINTER(i32)]
         lib.bfs_graph_info.restype = i32
+        lib.bfs_set_timing.argtypes = [P, i32]
+        lib.bfs_set_timing.restype = i32
+        lib.bfs_last_run_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float),
+                                            ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+        lib.bfs_last_run_timing.restype = i32
         _lib = lib
     return _lib
 
@@ -133,6 +139,21 @@ def bfs_last_run_stats(g, cap=1 << 22):
     return L, d, fe
 
 
+def bfs_set_timing(g, on=True):
+    rc = load().bfs_set_timing(g, 1 if on else 0)
+    if rc < 0:
+        raise BfsError(rc, bfs_last_error())
+
+
+def bfs_last_run_timing(g):
+    """(init_ms, level_ms, level_launches) of the last timed run."""
+    a, b, c = ctypes.c_float(), ctypes.c_float(), ctypes.c_int32()
+    rc = load().bfs_last_run_timing(g, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    if rc < 0:
+        raise BfsError(rc, bfs_last_error())
+    return a.value, b.value, c.value
+
+
 def bfs_graph_info(g):
     m, srt, sym, mx = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     rc = load().bfs_graph_info(g, ctypes.byref(m), ctypes.byref(srt), ctypes.byref(sym),
@@ -163,6 +184,12 @@ class BfsGraph:
 
     def info(self):
         return bfs_graph_info(self.handle)
+
+    def set_timing(self, on=True):
+        bfs_set_timing(self.handle, on)
+
+    def timing(self):
+        return bfs_last_run_timing(self.handle)
 
     def close(self):
         if self.handle:

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "bfs_internal.h"
 #include "frontier_bfs.h"
@@ -53,6 +54,12 @@ struct bfs_graph {
     GraphFacts *facts = nullptr;   // device, create only
     int32_t pol_dir = BFS_DIR_AUTO, pol_adv = BFS_ADV_AUTO, pol_loop = BFS_LOOP_DEVICE;
     int32_t last_L = 0;
+    // timing hook
+    int32_t timing = 0;
+    int32_t last_timed = 0;
+    float last_init_ms = 0.f, last_level_ms = 0.f;
+    int32_t last_launches = 0;
+    std::vector<hipEvent_t> events;   // [0,1] init, then pairs per batch
 };
 
 namespace {
@@ -78,6 +85,18 @@ void free_all(bfs_graph *g) {
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     if (g->host_ctl) (void)hipHostFree(g->host_ctl);
+    for (hipEvent_t e : g->events) (void)hipEventDestroy(e);
+    g->events.clear();
+}
+
+hipError_t ensure_events(bfs_graph *g, size_t count) {
+    while (g->events.size() < count) {
+        hipEvent_t e;
+        hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) return r;
+        g->events.push_back(e);
+    }
+    return hipSuccess;
 }
 
 int alloc_workspace(bfs_graph *g) {
@@ -304,17 +323,38 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.pol_dir = g->pol_dir;
     P.pol_adv = g->pol_adv;
 
+    const bool timing = g->timing != 0;
+    g->last_timed = 0;
+    if (timing) {
+        HIP_TRY(ensure_events(g, 4), BFS_EHIP);
+        HIP_TRY(hipEventRecord(g->events[0], stream), BFS_EHIP);
+    }
     HIP_TRY(launch_init(P, g->grid, stream), BFS_EHIP);
+    if (timing) HIP_TRY(hipEventRecord(g->events[1], stream), BFS_EHIP);
     const bool host_loop = g->pol_loop == BFS_LOOP_HOST;
     int64_t k = 0;
     int64_t batch = host_loop ? 1 : 8;
+    size_t nbatch = 0;
+    float level_ms = 0.f;
     const int64_t kmax = (int64_t)g->n + 1;   // L <= n, so level n finds an empty frontier
     for (;;) {
+        if (timing) {
+            HIP_TRY(ensure_events(g, 2 + 2 * (nbatch + 1)), BFS_EHIP);
+            HIP_TRY(hipEventRecord(g->events[2 + 2 * nbatch], stream), BFS_EHIP);
+        }
         for (int64_t i = 0; i < batch && k <= kmax; ++i, ++k)
             HIP_TRY(launch_level(P, (int32_t)k, g->grid, stream), BFS_EHIP);
+        if (timing) HIP_TRY(hipEventRecord(g->events[3 + 2 * nbatch], stream), BFS_EHIP);
         HIP_TRY(hipMemcpyAsync(g->host_ctl, g->ctl, sizeof(HostCtl), hipMemcpyDeviceToHost, stream),
                 BFS_EHIP);
         HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+        if (timing) {
+            float ms = 0.f;
+            HIP_TRY(hipEventElapsedTime(&ms, g->events[2 + 2 * nbatch], g->events[3 + 2 * nbatch]),
+                    BFS_EHIP);
+            level_ms += ms;
+        }
+        ++nbatch;
         const HostCtl h = *g->host_ctl;
         if (h.err) {
             set_error("device reported internal error %d (info %d)", h.err, h.err_info);
@@ -322,6 +362,14 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
         }
         if (h.done) {
             g->last_L = h.L;
+            if (timing) {
+                float ms = 0.f;
+                HIP_TRY(hipEventElapsedTime(&ms, g->events[0], g->events[1]), BFS_EHIP);
+                g->last_init_ms = ms;
+                g->last_level_ms = level_ms;
+                g->last_launches = (int32_t)k;
+                g->last_timed = 1;
+            }
             return h.L;
         }
         if (k > kmax) {
@@ -346,6 +394,27 @@ int32_t bfs_last_run_stats(const bfs_graph *g, int32_t cap, int8_t *dir, int64_t
         HIP_TRY(hipMemcpy(frontier_edges, g->st_fdeg, (size_t)cnt * sizeof(int64_t), hipMemcpyDeviceToHost),
                 BFS_EHIP);
     return g->last_L;
+}
+
+int32_t bfs_set_timing(bfs_graph *g, int32_t on) {
+    if (!g) {
+        set_error("NULL graph handle");
+        return BFS_EINVAL;
+    }
+    g->timing = on ? 1 : 0;
+    return 0;
+}
+
+int32_t bfs_last_run_timing(const bfs_graph *g, float *init_ms, float *level_ms,
+                            int32_t *level_launches) {
+    if (!g || !g->last_timed) {
+        set_error(g ? "the last run was not timed (bfs_set_timing)" : "NULL graph handle");
+        return BFS_EINVAL;
+    }
+    if (init_ms) *init_ms = g->last_init_ms;
+    if (level_ms) *level_ms = g->last_level_ms;
+    if (level_launches) *level_launches = g->last_launches;
+    return 0;
 }
 
 int32_t bfs_graph_info(const bfs_graph *g, int64_t *m, int32_t *sorted_rows, int32_t *symmetric,

@@ -15,8 +15,12 @@
 //   * bottom-up (pull): every unvisited vertex scans its list for a neighbour
 //     in the frontier bitmap (PMPP ch.15 notes, sections 15.3 and 15.7; Gunrock
 //     reading guide, step 6: dense frontier, no atomics, no duplicates).
-// The switch follows the PMPP ch.15 notes, section 15.7 rule: pull when
-// |F| * (m/n) > |U|.
+// The PMPP ch.15 notes (section 15.7) switch to pull when |F| * (m/n) > |U|.
+// Counting vertices misjudges power-law frontiers, whose few hubs carry most
+// of the edges, so the switch here counts edges, which the frontier counters
+// give exactly: pull when sum deg(F) > (edges of unvisited vertices) / ALPHA,
+// back to push when |F| < n / BETA and shrinking (Beamer, Asanovic and
+// Patterson, "Direction-Optimizing Breadth-First Search", SC 2012).
 //
 // Top-down advance (PMPP ch.15 notes, section 15.7 and Gunrock reading guide,
 // step 4: degree classes of one thread / one warp / one block):
@@ -89,6 +93,8 @@ struct LevelShared {
     int32_t buf[CAP];                 // staged new frontier vertices
     int32_t work[WORK_INTS];
     int32_t big_v[BLOCK], big_beg[BLOCK], big_len[BLOCK];
+    int32_t tstart[CAP], toff[CAP];   // flush: piece start / edge offset of each staged slot
+    int32_t ntiles;
     uint64_t scan_tmp[3][WAVES];
     unsigned long long list_base[NLISTS];
     int32_t cnt;                      // staged count (may exceed CAP: overflow spilled)
@@ -98,7 +104,7 @@ struct LevelShared {
     int32_t mode;                     // 0 exit, 1 finish, 2 run
     int32_t dir, input_bm, wbits, clear_bm, adv_eb;
     int32_t fsize;
-    int64_t fdeg, reached_before;
+    int64_t fdeg, reached_before, edges_before;
     int32_t lcount[NLISTS * STRIPES];  // segments per (list, stripe)
     int32_t ledges[NLISTS * STRIPES];  // edges per (list, stripe)
     int32_t uprefix[NLISTS * STRIPES + 1];  // unit prefix (binned or edge-balanced)
@@ -134,31 +140,36 @@ __device__ __forceinline__ void set_err(const Params &P, int code, int info) {
     P.ctl->err_info = info;
 }
 
+// Writes one segment (vertex v, adjacency piece [pb, pb+pl), edge offset po)
+// at index si of list l and records the edge-balanced tiles whose first edge
+// falls inside it.
+__device__ __forceinline__ void write_piece(const Ctx &c, int l, int64_t si, int v, int pb, int pl,
+                                            int64_t po) {
+    const Params &P = *c.P;
+    const int64_t cap = (l == L_TILE) ? P.tcap : P.qcap;
+    if (si >= cap) { set_err(P, l == L_TILE ? ERR_TILE_OVERFLOW : ERR_QUEUE_OVERFLOW, (int)l); return; }
+    Seg sg;
+    sg.v = v; sg.beg = pb; sg.len = pl; sg.off = (int32_t)po;
+    *seg_slot(P, c.nq, c.nt, l, c.stripe, si) = sg;
+    int32_t *ts = c.nts + (size_t)(l * STRIPES + c.stripe) * P.tscap;
+    int64_t t0 = (po + EB_TE - 1) / EB_TE;
+    const int64_t t1 = (po + pl - 1) / EB_TE;
+    for (; t0 <= t1; ++t0) {
+        if (t0 >= P.tscap) { set_err(P, ERR_TSTART_OVERFLOW, (int)l); return; }
+        ts[t0] = (int32_t)si;
+    }
+}
+
 // Writes the segments of one new frontier vertex v (adjacency [beg, beg+len),
 // cut into TILE pieces for list L_TILE) at segment index `idx` and edge
-// offset `eoff` of list l, and records edge-balanced tile starts.
+// offset `eoff` of list l.
 __device__ __forceinline__ void write_vertex_segments(const Ctx &c, int l, int v, int beg, int len,
-                                      int64_t idx, int64_t eoff) {
-    const Params &P = *c.P;
+                                                      int64_t idx, int64_t eoff) {
     const int nseg = (l == L_TILE) ? (len + TILE - 1) / TILE : 1;
-    const int64_t cap = (l == L_TILE) ? P.tcap : P.qcap;
-    int32_t *ts = c.nts + (size_t)(l * STRIPES + c.stripe) * P.tscap;
     for (int j = 0; j < nseg; ++j) {
-        const int64_t si = idx + j;
         const int pb = (l == L_TILE) ? beg + j * TILE : beg;
         const int pl = (l == L_TILE) ? min(TILE, len - j * TILE) : len;
-        const int64_t po = eoff + (int64_t)j * TILE;
-        if (si >= cap) { set_err(P, l == L_TILE ? ERR_TILE_OVERFLOW : ERR_QUEUE_OVERFLOW, (int)l); return; }
-        Seg sg;
-        sg.v = v; sg.beg = pb; sg.len = pl; sg.off = (int32_t)po;
-        *seg_slot(P, c.nq, c.nt, l, c.stripe, si) = sg;
-        // edge-balanced tiles whose first edge falls inside this segment
-        int64_t t0 = (po + EB_TE - 1) / EB_TE;
-        const int64_t t1 = (po + pl - 1) / EB_TE;
-        for (; t0 <= t1; ++t0) {
-            if (t0 >= P.tscap) { set_err(P, ERR_TSTART_OVERFLOW, (int)l); return; }
-            ts[t0] = (int32_t)si;
-        }
+        write_piece(c, l, idx + j, v, pb, pl, eoff + (int64_t)j * TILE);
     }
 }
 
@@ -277,18 +288,50 @@ __device__ __forceinline__ void flush(Ctx &c) {
                                         (unsigned long long)all);
     }
     __syncthreads();
+    // small and mid vertices: one segment each, written by their thread; big
+    // vertices: record where their pieces start, then the whole workgroup
+    // writes the pieces (a hub can have hundreds)
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
         const int l = li[j];
-        if (l >= 0) {
+        const int i = threadIdx.x * EPT + j;
+        if (l == L_SMALL || l == L_MID) {
             const uint64_t base = sh.list_base[l];
-            const uint64_t pos = (l == 0 ? excl[0] : (l == 1 ? excl[1] : excl[2]));
-            write_vertex_segments(c, l, vv[j], bb[j], ll[j],
-                                  (int64_t)((base >> 32) + (pos >> 32)),
-                                  (int64_t)((base & 0xffffffffull) + (pos & 0xffffffffull)));
-            const int nseg = (l == L_TILE) ? (ll[j] + TILE - 1) / TILE : 1;
-            const uint64_t x = ((uint64_t)nseg << 32) | (uint32_t)ll[j];
-            if (l == 0) excl[0] += x; else if (l == 1) excl[1] += x; else excl[2] += x;
+            const uint64_t pos = (l == L_SMALL) ? excl[0] : excl[1];
+            write_piece(c, l, (int64_t)((base >> 32) + (pos >> 32)), vv[j], bb[j], ll[j],
+                        (int64_t)((base & 0xffffffffull) + (pos & 0xffffffffull)));
+            const uint64_t x = (1ull << 32) | (uint32_t)ll[j];
+            if (l == L_SMALL) excl[0] += x; else excl[1] += x;
+        }
+        if (i < CAP) {
+            sh.tstart[i] = (int32_t)(excl[2] >> 32);
+            sh.toff[i] = (int32_t)(excl[2] & 0xffffffffull);
+        }
+        if (l == L_TILE) {
+            const int nseg = (ll[j] + TILE - 1) / TILE;
+            excl[2] += ((uint64_t)nseg << 32) | (uint32_t)ll[j];
+        }
+    }
+    if (threadIdx.x == BLOCK - 1) sh.ntiles = (int32_t)(excl[2] >> 32);
+    __syncthreads();
+    const int ntiles = sh.ntiles;
+    if (ntiles > 0) {
+        const uint64_t base = sh.list_base[L_TILE];
+        const int64_t tbase = (int64_t)(base >> 32);
+        const int64_t ebase = (int64_t)(base & 0xffffffffull);
+        for (int gt = threadIdx.x; gt < ntiles; gt += BLOCK) {
+            // last staged slot whose pieces start at or before gt
+            int lo = 0, hi = cnt;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (sh.tstart[mid] <= gt) lo = mid; else hi = mid;
+            }
+            const int v = sh.buf[lo];
+            const int beg = P.row_ptr[v];
+            const int len = P.row_ptr[v + 1] - beg;
+            const int pcs = gt - sh.tstart[lo];
+            write_piece(c, L_TILE, tbase + gt, v, beg + pcs * TILE, min(TILE, len - pcs * TILE),
+                        ebase + sh.toff[lo] + (int64_t)pcs * TILE);
         }
     }
     __syncthreads();
@@ -501,10 +544,21 @@ __device__ __forceinline__ void bottom_up(Ctx &c, const uint32_t *cbm, uint32_t 
             beg = P.row_ptr[v];
             end_e = P.row_ptr[v + 1];
             const int lim = min(end_e, beg + BU_LANE_SCAN);
-            for (e = beg; e < lim; ++e) {
-                const int u = P.col_idx[e];
-                if ((cbm[u >> 5] >> (u & 31)) & 1u) { found = true; par = u; break; }
+            // BU_Q entries per step: their loads and bitmap probes are issued
+            // together; the first hit in CSR order wins
+            for (e = beg; e < lim && !found; e += BU_Q) {
+                int us[BU_Q];
+                uint32_t w[BU_Q];
+#pragma unroll
+                for (int q = 0; q < BU_Q; ++q) us[q] = (e + q < lim) ? P.col_idx[e + q] : -1;
+#pragma unroll
+                for (int q = 0; q < BU_Q; ++q) w[q] = (us[q] >= 0) ? cbm[us[q] >> 5] : 0u;
+#pragma unroll
+                for (int q = BU_Q - 1; q >= 0; --q) {
+                    if (us[q] >= 0 && ((w[q] >> (us[q] & 31)) & 1u)) { found = true; par = us[q]; }
+                }
             }
+            if (!found) e = lim;
         }
         // long lists: the whole wavefront scans 64 entries at a time; the first
         // hit in CSR order is the lowest set lane of the first chunk with one
@@ -572,7 +626,8 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
             P.ctl->done = 0; P.ctl->L = 0; P.ctl->err = 0; P.ctl->err_info = 0;
             for (int k = 0; k < NSLOTS; ++k) {
                 P.ctl->slot[k].dir = 0; P.ctl->slot[k].wbits = 0;
-                P.ctl->slot[k].input_bm = 0; P.ctl->slot[k].reached_before = 0;
+                P.ctl->slot[k].input_bm = 0; P.ctl->slot[k].fsize = 0;
+                P.ctl->slot[k].reached_before = 0; P.ctl->slot[k].edges_before = 0;
             }
         }
         __syncthreads();
@@ -619,22 +674,32 @@ __global__ __launch_bounds__(BLOCK) void bfs_level_kernel(Params P, int32_t k) {
                 sh.mode = 1;
             } else {
                 sh.mode = 2;
-                const SlotInfo prev = (k > 0) ? P.ctl->slot[(k + NSLOTS - 1) % NSLOTS] : SlotInfo{0, 0, 0, 0, 0};
+                const SlotInfo prev = (k > 0) ? P.ctl->slot[(k + NSLOTS - 1) % NSLOTS] : SlotInfo{0, 0, 0, 0, 0, 0};
                 const int64_t reached_before = (k > 0) ? P.ctl->slot[slot].reached_before : 0;
+                const int64_t edges_before = (k > 0) ? P.ctl->slot[slot].edges_before : 0;
                 const bool has_queue = (k == 0) || prev.dir == DIR_TD;
                 const bool has_bm = (k == 0) || prev.dir == DIR_BU || prev.wbits;
-                const int64_t U = (int64_t)P.n - reached_before - fsize;
                 bool want_pull;
-                if (P.pol_dir == BFS_DIR_PULL) want_pull = true;
-                else if (P.pol_dir == BFS_DIR_PUSH) want_pull = false;
-                else want_pull = fsize * (int64_t)P.m > U * (int64_t)P.n;
+                if (P.pol_dir == BFS_DIR_PULL) {
+                    want_pull = true;
+                } else if (P.pol_dir == BFS_DIR_PUSH) {
+                    want_pull = false;
+                } else if (k == 0 || prev.dir == DIR_TD) {
+                    // edges still to be explored from unvisited vertices
+                    const int64_t m_u = (int64_t)P.m - edges_before - fdeg;
+                    want_pull = fdeg * ALPHA > m_u;
+                } else {
+                    want_pull = !(fsize * BETA < (int64_t)P.n && fsize < prev.fsize);
+                }
                 const int dir = (want_pull && P.symmetric && has_bm) ? DIR_BU : DIR_TD;
                 sh.dir = dir;
                 sh.reached_before = reached_before;
+                sh.edges_before = edges_before;
                 sh.input_bm = (dir == DIR_TD) && !has_queue;
                 sh.clear_bm = (dir == DIR_TD) && has_queue && has_bm;
-                sh.wbits = (dir == DIR_TD) && has_queue && P.symmetric && P.pol_dir == BFS_DIR_AUTO &&
-                           fdeg * (int64_t)P.m > (U - fdeg) * (int64_t)P.n;
+                // a top-down level from a queue also sets its new vertices in the
+                // next bitmap whenever the next level may pull
+                sh.wbits = (dir == DIR_TD) && has_queue && P.symmetric && P.pol_dir == BFS_DIR_AUTO;
                 sh.adv_eb = (dir == DIR_TD) && has_queue &&
                             (P.pol_adv == BFS_ADV_EDGE || (P.pol_adv == BFS_ADV_AUTO && fsize >= 4096));
             }
@@ -670,7 +735,9 @@ __global__ __launch_bounds__(BLOCK) void bfs_level_kernel(Params P, int32_t k) {
             P.ctl->slot[slot].dir = sh.dir;
             P.ctl->slot[slot].wbits = sh.wbits;
             P.ctl->slot[slot].input_bm = sh.input_bm;
+            P.ctl->slot[slot].fsize = sh.fsize;
             P.ctl->slot[(k + 1) % NSLOTS].reached_before = sh.reached_before + sh.fsize;
+            P.ctl->slot[(k + 1) % NSLOTS].edges_before = sh.edges_before + sh.fdeg;
         }
         if (threadIdx.x < NCTR) *ctr_at(P, (k + 2) % NSLOTS, threadIdx.x) = 0ull;
     }

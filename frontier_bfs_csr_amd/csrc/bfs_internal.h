@@ -20,6 +20,12 @@ constexpr int CAP = 2048;                // LDS staging capacity for new frontie
 constexpr int EB_TE = 2048;              // edges per tile of the edge-balanced advance
 constexpr int BU_LANE_SCAN = 32;         // bottom-up: entries a lane scans alone before
                                          // its list is handed to the whole wavefront
+constexpr int BU_Q = 8;                  // bottom-up: entries a lane loads per step
+// direction switching (edge-based, as in Beamer et al. SC'12): go bottom-up
+// when the frontier's edges exceed 1/ALPHA of the unexplored vertices' edges;
+// come back top-down when the frontier is under n/BETA and shrinking
+constexpr int ALPHA = 14;
+constexpr int BETA = 24;
 
 // lists of a frontier queue
 constexpr int L_SMALL = 0;               // degree in [1, T_LANE)
@@ -50,8 +56,9 @@ struct SlotInfo {
     int32_t dir;          // direction this level ran in
     int32_t wbits;        // this level's new vertices were also set in the next bitmap
     int32_t input_bm;     // this level's frontier came as a bitmap only
-    int32_t pad;
+    int32_t fsize;        // this level's frontier size
     int64_t reached_before;  // vertices in levels < this one
+    int64_t edges_before;    // sum of degrees of the vertices in levels < this one
 };
 
 struct Ctl {

@@ -122,6 +122,24 @@ int32_t bfs_last_run_stats(const bfs_graph *g, int32_t cap, int8_t *dir,
                            int64_t *frontier_edges);
 
 /*
+ * Timing hook.  When on, bfs_run records HIP events on its stream before and
+ * after the initialisation launch and around every batch of level launches.
+ * Returns 0 or BFS_EINVAL.
+ */
+int32_t bfs_set_timing(bfs_graph *g, int32_t on);
+
+/*
+ * Milliseconds of the last timed bfs_run (host memory, any may be NULL):
+ * init_ms = the initialisation launch; level_ms = the level launches, summed
+ * over batches (host waits between batches excluded); level_launches = level
+ * launches issued (including the one that found the empty frontier and any
+ * that exited at once after it).  Returns 0, or BFS_EINVAL if the last run was
+ * not timed.
+ */
+int32_t bfs_last_run_timing(const bfs_graph *g, float *init_ms, float *level_ms,
+                            int32_t *level_launches);
+
+/*
  * Graph facts found by bfs_graph_create (host memory, any may be NULL):
  * CSR entry count, rows-sorted flag, symmetric flag, maximum degree.
  * Returns 0 or BFS_EINVAL.
