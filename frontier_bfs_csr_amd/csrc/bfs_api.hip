@@ -320,6 +320,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.st_fdeg = g->st_fdeg;
     P.st_cap = g->st_cap;
     P.symmetric = g->symmetric;
+    P.col_vec = (reinterpret_cast<uintptr_t>(g->col_idx) % 16) == 0;
     P.pol_dir = g->pol_dir;
     P.pol_adv = g->pol_adv;
 

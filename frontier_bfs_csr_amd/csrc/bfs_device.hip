@@ -90,10 +90,19 @@ constexpr int FLIST_CAP = 4 * BLOCK;     // from-bitmap pass: 4 word pairs per w
 static_assert(FLIST_CAP <= WORK_INTS, "work area too small");
 
 struct LevelShared {
-    int32_t buf[CAP];                 // staged new frontier vertices
-    int32_t work[WORK_INTS];
-    int32_t big_v[BLOCK], big_beg[BLOCK], big_len[BLOCK];
-    int32_t tstart[CAP], toff[CAP];   // flush: piece start / edge offset of each staged slot
+    union {
+        struct {                          // top-down passes
+            int32_t buf[CAP];             // staged new frontier vertices
+            int32_t work[WORK_INTS];
+            int32_t big_v[BLOCK], big_beg[BLOCK], big_len[BLOCK];
+            int32_t tstart[CAP], toff[CAP];   // flush: piece start / edge offset of each staged slot
+        };
+        struct {                          // bottom-up pass, per wavefront
+            int32_t bu_lst[WAVES][BU_GP * 64];     // unvisited vertices of the group
+            unsigned long long bu_fm[WAVES][BU_GP];  // found masks per word pair
+            unsigned long long bu_vis[WAVES][BU_GP]; // visited words per word pair
+        };
+    };
     int32_t ntiles;
     uint64_t scan_tmp[3][WAVES];
     unsigned long long list_base[NLISTS];
@@ -235,84 +244,76 @@ __device__ __forceinline__ void claim(Ctx &c, int v, int u) {
 
 // Workgroup flush of the staged vertices: one global atomic per list per
 // flush (exclusive scans of (segments, edges) give every vertex its place).
+// Two passes over the thread's staged slots -- tally, then write -- keep
+// few registers live; the second pass re-reads row_ptr entries the first one
+// just loaded.
 __device__ __forceinline__ void flush(Ctx &c) {
     LevelShared &sh = *c.sh;
     const Params &P = *c.P;
     __syncthreads();
     const int cnt = min(sh.cnt, CAP);
     constexpr int EPT = CAP / BLOCK;
-    int vv[EPT], bb[EPT], ll[EPT], li[EPT];
-    uint64_t tot[NLISTS] = {0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int i = threadIdx.x * EPT + j;
-        li[j] = -1; vv[j] = 0; bb[j] = 0; ll[j] = 0;
-        if (i < cnt) {
-            const int v = sh.buf[i];
-            const int beg = P.row_ptr[v];
-            const int len = P.row_ptr[v + 1] - beg;
-            vv[j] = v; bb[j] = beg; ll[j] = len;
-            li[j] = list_of(len);
-            c.fcnt += 1;
-            c.fdeg += len;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        if (li[j] >= 0) {
-            const int nseg = (li[j] == L_TILE) ? (ll[j] + TILE - 1) / TILE : 1;
-            const uint64_t x = ((uint64_t)nseg << 32) | (uint32_t)ll[j];
-            if (li[j] == 0) tot[0] += x; else if (li[j] == 1) tot[1] += x; else tot[2] += x;
-        }
+    const int i0 = threadIdx.x * EPT;
+    uint64_t tot0 = 0, tot1 = 0, tot2 = 0;
+    for (int i = i0; i < min(i0 + EPT, cnt); ++i) {
+        const int v = sh.buf[i];
+        const int beg = P.row_ptr[v];
+        const int len = P.row_ptr[v + 1] - beg;
+        c.fcnt += 1;
+        c.fdeg += len;
+        const int l = list_of(len);
+        if (l == L_SMALL) tot0 += (1ull << 32) | (uint32_t)len;
+        else if (l == L_MID) tot1 += (1ull << 32) | (uint32_t)len;
+        else if (l == L_TILE) tot2 += ((uint64_t)((len + TILE - 1) / TILE) << 32) | (uint32_t)len;
     }
     // exclusive scans of the per-thread totals, one per list
-    uint64_t incl[NLISTS];
-#pragma unroll
-    for (int l = 0; l < NLISTS; ++l) {
-        incl[l] = wave_incl_scan_u64(tot[l]);
-        if (lane_id() == WAVE - 1) sh.scan_tmp[l][wave_id()] = incl[l];
+    const uint64_t in0 = wave_incl_scan_u64(tot0);
+    const uint64_t in1 = wave_incl_scan_u64(tot1);
+    const uint64_t in2 = wave_incl_scan_u64(tot2);
+    if (lane_id() == WAVE - 1) {
+        sh.scan_tmp[0][wave_id()] = in0;
+        sh.scan_tmp[1][wave_id()] = in1;
+        sh.scan_tmp[2][wave_id()] = in2;
     }
     __syncthreads();
-    uint64_t excl[NLISTS];
-#pragma unroll
-    for (int l = 0; l < NLISTS; ++l) {
-        uint64_t before = 0, all = 0;
-        for (int w = 0; w < WAVES; ++w) {
-            const uint64_t t = sh.scan_tmp[l][w];
-            if (w < wave_id()) before += t;
-            all += t;
-        }
-        excl[l] = before + incl[l] - tot[l];
-        if ((int)threadIdx.x == l && all != 0)
-            sh.list_base[l] = atomicAdd(ctr_at(P, c.nslot, l * STRIPES + c.stripe),
-                                        (unsigned long long)all);
+    uint64_t ex0 = in0 - tot0, ex1 = in1 - tot1, ex2 = in2 - tot2;
+    for (int w = 0; w < wave_id(); ++w) {
+        ex0 += sh.scan_tmp[0][w];
+        ex1 += sh.scan_tmp[1][w];
+        ex2 += sh.scan_tmp[2][w];
+    }
+    if (threadIdx.x < NLISTS) {
+        const int l = threadIdx.x;
+        uint64_t all = 0;
+        for (int w = 0; w < WAVES; ++w) all += sh.scan_tmp[l][w];
+        if (all != 0)
+            sh.list_base[l] = atomicAdd(ctr_at(P, c.nslot, l * STRIPES + c.stripe), (unsigned long long)all);
+        if (l == L_TILE) sh.ntiles = (int32_t)(all >> 32);
     }
     __syncthreads();
     // small and mid vertices: one segment each, written by their thread; big
     // vertices: record where their pieces start, then the whole workgroup
     // writes the pieces (a hub can have hundreds)
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int l = li[j];
-        const int i = threadIdx.x * EPT + j;
-        if (l == L_SMALL || l == L_MID) {
-            const uint64_t base = sh.list_base[l];
-            const uint64_t pos = (l == L_SMALL) ? excl[0] : excl[1];
-            write_piece(c, l, (int64_t)((base >> 32) + (pos >> 32)), vv[j], bb[j], ll[j],
-                        (int64_t)((base & 0xffffffffull) + (pos & 0xffffffffull)));
-            const uint64_t x = (1ull << 32) | (uint32_t)ll[j];
-            if (l == L_SMALL) excl[0] += x; else excl[1] += x;
-        }
-        if (i < CAP) {
-            sh.tstart[i] = (int32_t)(excl[2] >> 32);
-            sh.toff[i] = (int32_t)(excl[2] & 0xffffffffull);
-        }
-        if (l == L_TILE) {
-            const int nseg = (ll[j] + TILE - 1) / TILE;
-            excl[2] += ((uint64_t)nseg << 32) | (uint32_t)ll[j];
+    const uint64_t b0 = sh.list_base[L_SMALL], b1 = sh.list_base[L_MID];
+    for (int i = i0; i < min(i0 + EPT, cnt); ++i) {
+        const int v = sh.buf[i];
+        const int beg = P.row_ptr[v];
+        const int len = P.row_ptr[v + 1] - beg;
+        const int l = list_of(len);
+        sh.tstart[i] = (int32_t)(ex2 >> 32);
+        sh.toff[i] = (int32_t)(ex2 & 0xffffffffull);
+        if (l == L_SMALL) {
+            write_piece(c, l, (int64_t)((b0 >> 32) + (ex0 >> 32)), v, beg, len,
+                        (int64_t)((b0 & 0xffffffffull) + (ex0 & 0xffffffffull)));
+            ex0 += (1ull << 32) | (uint32_t)len;
+        } else if (l == L_MID) {
+            write_piece(c, l, (int64_t)((b1 >> 32) + (ex1 >> 32)), v, beg, len,
+                        (int64_t)((b1 & 0xffffffffull) + (ex1 & 0xffffffffull)));
+            ex1 += (1ull << 32) | (uint32_t)len;
+        } else if (l == L_TILE) {
+            ex2 += ((uint64_t)((len + TILE - 1) / TILE) << 32) | (uint32_t)len;
         }
     }
-    if (threadIdx.x == BLOCK - 1) sh.ntiles = (int32_t)(excl[2] >> 32);
     __syncthreads();
     const int ntiles = sh.ntiles;
     if (ntiles > 0) {
@@ -522,79 +523,116 @@ __device__ __forceinline__ void td_from_bitmap(Ctx &c, uint32_t *cbm, uint32_t *
 // Every unvisited vertex looks for a parent in the frontier bitmap, in CSR
 // order; a wavefront owns 64 consecutive vertices, so __ballot(found) is the
 // next bitmap's 64-bit word and the visited word update needs no atomics.
+__device__ __forceinline__ void wave_lds_sync() {
+    // order this wavefront's LDS traffic between lanes (no workgroup barrier)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 __device__ __forceinline__ void bottom_up(Ctx &c, const uint32_t *cbm, uint32_t *nbm) {
     const Params &P = *c.P;
+    LevelShared &sh = *c.sh;
     const int per = (P.nwp + gridDim.x - 1) / gridDim.x;
     const int start = blockIdx.x * per;
     const int end = min(P.nwp, start + per);
     const int lane = lane_id();
+    const int wv = wave_id();
     uint64_t *vis64 = reinterpret_cast<uint64_t *>(P.visited);
     uint64_t *nbm64 = reinterpret_cast<uint64_t *>(nbm);
-    for (int wp = start + wave_id(); wp < end; wp += WAVES) {
-        const uint64_t vis = vis64[wp];
-        if (vis == ~0ull) {
-            if (lane == 0) nbm64[wp] = 0ull;
-            continue;
+    int32_t *lst = sh.bu_lst[wv];
+    // a wavefront takes BU_GP word pairs (BU_GP*64 vertices) at a time,
+    // gathers their unvisited vertices into a dense LDS list, and scans them
+    // 64 at a time: every lane has a vertex whatever share is visited
+    for (int g0 = start + wv * BU_GP; g0 < end; g0 += WAVES * BU_GP) {
+        const int ng = min(BU_GP, end - g0);
+        int cnt = 0;
+        for (int j = 0; j < ng; ++j) {
+            const uint64_t vis = vis64[g0 + j];
+            const bool act = !((vis >> lane) & 1ull);   // padding bits are set
+            const uint64_t m = __ballot(act);
+            if (act) lst[cnt + mbcnt64(m)] = (g0 + j) * 64 + lane;
+            if (lane == 0) { sh.bu_vis[wv][j] = vis; sh.bu_fm[wv][j] = 0ull; }
+            cnt += __popcll(m);
         }
-        const int v = wp * 64 + lane;
-        const bool active = !((vis >> lane) & 1ull);   // padding bits are set
-        bool found = false;
-        int par = -1, beg = 0, end_e = 0, e = 0;
-        if (active) {
-            beg = P.row_ptr[v];
-            end_e = P.row_ptr[v + 1];
-            const int lim = min(end_e, beg + BU_LANE_SCAN);
-            // BU_Q entries per step: their loads and bitmap probes are issued
-            // together; the first hit in CSR order wins
-            for (e = beg; e < lim && !found; e += BU_Q) {
-                int us[BU_Q];
-                uint32_t w[BU_Q];
+        wave_lds_sync();
+        for (int b0 = 0; b0 < cnt; b0 += WAVE) {
+            const bool act = b0 + lane < cnt;
+            const int v = act ? lst[b0 + lane] : 0;
+            const int beg = act ? P.row_ptr[v] : 0;
+            const int eend = act ? P.row_ptr[v + 1] : 0;
+            const int lim = min(eend, beg + BU_LANE_SCAN);
+            int e = beg, par = -1;
+            bool fnd = false;
+            // lane scan: each step covers the aligned 8-entry block holding
+            // the scan position, fetched as two 16-byte loads, then probes the
+            // block's entries inside [e, lim); the first hit in CSR order wins
+            for (int step = 0; step <= BU_LANE_SCAN / 8; ++step) {
+                const bool go = act && e < lim;
+                if (!__ballot(go)) break;
+                const int blk = e & ~7;
+                int x[8];
+                if (go && P.col_vec && blk + 8 <= P.m) {
+                    const int4 a = *reinterpret_cast<const int4 *>(P.col_idx + blk);
+                    const int4 b = *reinterpret_cast<const int4 *>(P.col_idx + blk + 4);
+                    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+                    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+                } else {
 #pragma unroll
-                for (int q = 0; q < BU_Q; ++q) us[q] = (e + q < lim) ? P.col_idx[e + q] : -1;
+                    for (int q = 0; q < 8; ++q)
+                        x[q] = (go && blk + q >= e && blk + q < lim) ? P.col_idx[blk + q] : -1;
+                }
+                uint32_t w[8];
 #pragma unroll
-                for (int q = 0; q < BU_Q; ++q) w[q] = (us[q] >= 0) ? cbm[us[q] >> 5] : 0u;
+                for (int q = 0; q < 8; ++q) {
+                    if (!(go && blk + q >= e && blk + q < lim)) x[q] = -1;
+                    w[q] = (x[q] >= 0) ? cbm[x[q] >> 5] : 0u;
+                }
 #pragma unroll
-                for (int q = BU_Q - 1; q >= 0; --q) {
-                    if (us[q] >= 0 && ((w[q] >> (us[q] & 31)) & 1u)) { found = true; par = us[q]; }
+                for (int q = 7; q >= 0; --q)
+                    if (x[q] >= 0 && ((w[q] >> (x[q] & 31)) & 1u)) { fnd = true; par = x[q]; }
+                if (go) e = fnd ? lim : min(blk + 8, lim);
+            }
+            if (!fnd) e = lim;
+            // long lists: the whole wavefront scans 64 entries at a time; the
+            // first hit in CSR order is the lowest set lane of the first chunk
+            uint64_t pm = __ballot(act && !fnd && e < eend);
+            while (pm) {
+                const int src = __ffsll((unsigned long long)pm) - 1;
+                pm &= pm - 1;
+                const int sb = readlane_i(e, src), se = readlane_i(eend, src);
+                for (int c0 = sb; c0 < se; c0 += WAVE) {
+                    const int ee = c0 + lane;
+                    int u = 0;
+                    bool hit = false;
+                    if (ee < se) {
+                        u = P.col_idx[ee];
+                        hit = (cbm[u >> 5] >> (u & 31)) & 1u;
+                    }
+                    const uint64_t hm = __ballot(hit);
+                    if (hm) {
+                        const int first = __ffsll((unsigned long long)hm) - 1;
+                        const int pu = readlane_i(u, first);
+                        if (lane == src) { fnd = true; par = pu; }
+                        break;
+                    }
                 }
             }
-            if (!found) e = lim;
-        }
-        // long lists: the whole wavefront scans 64 entries at a time; the first
-        // hit in CSR order is the lowest set lane of the first chunk with one
-        uint64_t pm = __ballot(active && !found && e < end_e);
-        while (pm) {
-            const int src = __ffsll((unsigned long long)pm) - 1;
-            pm &= pm - 1;
-            const int sb = readlane_i(e, src), se = readlane_i(end_e, src);
-            for (int b0 = sb; b0 < se; b0 += WAVE) {
-                const int ee = b0 + lane;
-                int u = 0;
-                bool hit = false;
-                if (ee < se) {
-                    u = P.col_idx[ee];
-                    hit = (cbm[u >> 5] >> (u & 31)) & 1u;
-                }
-                const uint64_t hm = __ballot(hit);
-                if (hm) {
-                    const int first = __ffsll((unsigned long long)hm) - 1;
-                    const int pu = readlane_i(u, first);
-                    if (lane == src) { found = true; par = pu; }
-                    break;
-                }
+            if (fnd) {
+                P.dist[v] = c.level + 1;
+                if (P.parent) P.parent[v] = par;
+                atomicOr(&sh.bu_fm[wv][(v >> 6) - g0], 1ull << (v & 63));
+                c.fcnt += 1;
+                c.fdeg += eend - beg;
             }
         }
-        const uint64_t fm = __ballot(found);
-        if (lane == 0) {
-            nbm64[wp] = fm;
-            if (fm) vis64[wp] = vis | fm;
+        wave_lds_sync();
+        // the group's next-bitmap words (every word written) and visited words
+        if (lane < ng) {
+            const uint64_t fm = sh.bu_fm[wv][lane];
+            nbm64[g0 + lane] = fm;
+            if (fm) vis64[g0 + lane] = sh.bu_vis[wv][lane] | fm;
         }
-        if (found) {
-            P.dist[v] = c.level + 1;
-            if (P.parent) P.parent[v] = par;
-            c.fcnt += 1;
-            c.fdeg += end_e - beg;
-        }
+        wave_lds_sync();
     }
 }
 

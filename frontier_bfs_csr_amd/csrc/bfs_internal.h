@@ -20,7 +20,7 @@ constexpr int CAP = 2048;                // LDS staging capacity for new frontie
 constexpr int EB_TE = 2048;              // edges per tile of the edge-balanced advance
 constexpr int BU_LANE_SCAN = 32;         // bottom-up: entries a lane scans alone before
                                          // its list is handed to the whole wavefront
-constexpr int BU_Q = 8;                  // bottom-up: entries a lane loads per step
+constexpr int BU_GP = 8;                 // bottom-up: word pairs a wavefront gathers at a time
 // direction switching (edge-based, as in Beamer et al. SC'12): go bottom-up
 // when the frontier's edges exceed 1/ALPHA of the unexplored vertices' edges;
 // come back top-down when the frontier is under n/BETA and shrinking
@@ -97,6 +97,7 @@ struct Params {
     int64_t *st_fdeg;
     int32_t st_cap;
     int32_t symmetric;
+    int32_t col_vec;          // col_idx is 16-byte aligned: 16-byte loads allowed
     int32_t pol_dir;          // BFS_DIR_*
     int32_t pol_adv;          // BFS_ADV_*
 };

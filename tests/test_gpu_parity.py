@@ -134,3 +134,24 @@ def test_run_argument_errors():
         with pytest.raises(fb.BfsError):
             bg.set_policy(fb.DIR_PULL)         # directed graph: no pull
         assert not bg.info()["symmetric"]
+
+
+def test_unaligned_col_idx():
+    """col_idx starting 4 bytes past a 16-byte boundary (the bottom-up scan
+    then takes its scalar-load path)."""
+    import torch
+    import frontier_bfs_csr_amd as fb
+    g = gg.rmat(13, 16, seed=31, nsrc=3)
+    rp = torch.from_numpy(g.row_ptr).cuda()
+    buf = torch.zeros(g.m + 1, dtype=torch.int32, device="cuda")
+    buf[1:] = torch.from_numpy(g.col_idx).cuda()
+    ci = buf[1:]
+    assert ci.data_ptr() % 16 != 0
+    with fb.BfsGraph(rp, ci) as bg:
+        for pol in ((2, 0, 0), (0, 0, 0)):
+            bg.set_policy(*pol)
+            for s in g.sources:
+                L, dist, parent, sizes = run_hip(bg, g.n, s)
+                ref = oracle.bfs(g.row_ptr, g.col_idx, int(s))
+                oracle.assert_bfs_ok(g.row_ptr, g.col_idx, int(s), ref, dist, parent, L, sizes[:L],
+                                     label=f"unaligned s={s} {pol}")
