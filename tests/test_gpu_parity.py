@@ -67,6 +67,25 @@ def test_c2_workload_sampled():
     check_graph(g, sources=g.sources[4:12], policies=["auto"])
 
 
+def test_c3_workload_sampled():
+    g = gg.c3_er(nsrc=64)
+    check_graph(g, sources=g.sources[:2], policies=["auto", "push_binned", "push_edge"])
+
+
+def test_c4_workload():
+    """The damaged 4096 x 4096 grid from a corner: thousands of levels."""
+    g = gg.c4_grid()
+    check_graph(g, policies=["auto", "push_edge"])
+
+
+def test_c5_workload_sampled():
+    """R-MAT scale 24 at full size, in the benchmark's configuration (auto
+    policy, parents and level sizes written), on a sample of its sources."""
+    g = gg.c5_rmat24(nsrc=64)
+    check_graph(g, sources=g.sources[:2], policies=["auto"])
+    check_graph(g, sources=g.sources[2:3], policies=["push_binned", "pull"])
+
+
 def test_optional_outputs():
     import torch
     import frontier_bfs_csr_amd as fb
