@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libfrontier_bfs.so")
 BFS_EINVAL, BFS_EHIP, BFS_ENOMEM, BFS_EDEVICE = -1, -2, -3, -4
 DIR_AUTO, DIR_PUSH, DIR_PULL = 0, 1, 2
 ADV_AUTO, ADV_BINNED, ADV_EDGE = 0, 1, 2
-LOOP_DEVICE, LOOP_HOST = 0, 1
+LOOP_DEVICE, LOOP_HOST, LOOP_CHAIN = 0, 1, 2
 
 EXPORTS = ("bfs_graph_create", "bfs_run", "bfs_graph_destroy", "bfs_last_error",
            "bfs_set_policy", "bfs_last_run_stats", "bfs_set_timing", "bfs_last_run_timing",

@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -53,6 +54,7 @@ struct bfs_graph {
     HostCtl *host_ctl = nullptr;   // pinned
     GraphFacts *facts = nullptr;   // device, create only
     int32_t pol_dir = BFS_DIR_AUTO, pol_adv = BFS_ADV_AUTO, pol_loop = BFS_LOOP_DEVICE;
+    uint32_t barrier_ticks = 200000000u;   // 2 s at 100 MHz
     int32_t last_L = 0;
     // timing hook
     int32_t timing = 0;
@@ -231,6 +233,10 @@ bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *co
             rc = BFS_EHIP;
         }
     }
+    if (const char *t = getenv("FBFS_BARRIER_TIMEOUT_US")) {
+        const long long us = atoll(t);
+        if (us >= 0) g->barrier_ticks = (uint32_t)(us * 100 < 4000000000LL ? us * 100 : 4000000000LL);
+    }
     if (rc == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, g->device) != hipSuccess ||
@@ -260,7 +266,7 @@ int32_t bfs_set_policy(bfs_graph *g, int32_t direction, int32_t advance, int32_t
         return BFS_EINVAL;
     }
     if (direction < BFS_DIR_AUTO || direction > BFS_DIR_PULL || advance < BFS_ADV_AUTO ||
-        advance > BFS_ADV_EDGE || loop < BFS_LOOP_DEVICE || loop > BFS_LOOP_HOST) {
+        advance > BFS_ADV_EDGE || loop < BFS_LOOP_DEVICE || loop > BFS_LOOP_CHAIN) {
         set_error("unknown policy (direction %d, advance %d, loop %d)", direction, advance, loop);
         return BFS_EINVAL;
     }
@@ -323,6 +329,8 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.col_vec = (reinterpret_cast<uintptr_t>(g->col_idx) % 16) == 0;
     P.pol_dir = g->pol_dir;
     P.pol_adv = g->pol_adv;
+    P.small_mode = g->pol_loop == BFS_LOOP_DEVICE;
+    P.barrier_ticks = g->barrier_ticks;
 
     const bool timing = g->timing != 0;
     g->last_timed = 0;
@@ -337,14 +345,16 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     int64_t batch = host_loop ? 1 : 8;
     size_t nbatch = 0;
     float level_ms = 0.f;
-    const int64_t kmax = (int64_t)g->n + 1;   // L <= n, so level n finds an empty frontier
+    // every launch runs at least one level or finds the empty frontier, and
+    // L <= n, so launch n has found it
+    const int64_t kmax = (int64_t)g->n + 1;
     for (;;) {
         if (timing) {
             HIP_TRY(ensure_events(g, 2 + 2 * (nbatch + 1)), BFS_EHIP);
             HIP_TRY(hipEventRecord(g->events[2 + 2 * nbatch], stream), BFS_EHIP);
         }
         for (int64_t i = 0; i < batch && k <= kmax; ++i, ++k)
-            HIP_TRY(launch_level(P, (int32_t)k, g->grid, stream), BFS_EHIP);
+            HIP_TRY(launch_level(P, (int32_t)k, g->grid, stream), BFS_EHIP);   // k = launch index
         if (timing) HIP_TRY(hipEventRecord(g->events[3 + 2 * nbatch], stream), BFS_EHIP);
         HIP_TRY(hipMemcpyAsync(g->host_ctl, g->ctl, sizeof(HostCtl), hipMemcpyDeviceToHost, stream),
                 BFS_EHIP);
@@ -358,7 +368,10 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
         ++nbatch;
         const HostCtl h = *g->host_ctl;
         if (h.err) {
-            set_error("device reported internal error %d (info %d)", h.err, h.err_info);
+            if (h.err == ERR_BARRIER_TIMEOUT)
+                set_error("small-frontier barrier wait exceeded its limit (%u ticks)", g->barrier_ticks);
+            else
+                set_error("device reported internal error %d (info %d)", h.err, h.err_info);
             return BFS_EDEVICE;
         }
         if (h.done) {

@@ -111,7 +111,7 @@ struct LevelShared {
     int32_t fcnt;                     // from-bitmap list count
     // decision, identical in every workgroup
     int32_t mode;                     // 0 exit, 1 finish, 2 run
-    int32_t dir, input_bm, wbits, clear_bm, adv_eb;
+    int32_t dir, input_bm, wbits, clear_bm, adv_eb, small;
     int32_t fsize;
     int64_t fdeg, reached_before, edges_before;
     int32_t lcount[NLISTS * STRIPES];  // segments per (list, stripe)
@@ -124,6 +124,7 @@ struct Ctx {
     const Params *P;
     LevelShared *sh;
     int32_t level;          // k: new vertices get k+1
+    int32_t wg, G;          // this workgroup's index among the G taking part
     int32_t stripe;         // counter / queue stripe of this workgroup
     int32_t nslot;          // slot of level k+1
     int32_t wbits;
@@ -186,7 +187,8 @@ __device__ __forceinline__ int list_of(int len) {
     return len <= 0 ? -1 : (len < T_LANE ? L_SMALL : (len < T_WG ? L_MID : L_TILE));
 }
 
-// One vertex, one lane: used when the LDS staging buffer is full.
+// One vertex, one lane: used when the LDS staging buffer is full (the
+// expansion loops flush often enough that this is rare).
 __device__ __forceinline__ void emit_single(Ctx &c, int v) {
     const Params &P = *c.P;
     const int beg = P.row_ptr[v];
@@ -215,31 +217,61 @@ __device__ __forceinline__ void stage(Ctx &c, bool win, int v) {
         if (slot < CAP) c.sh->buf[slot] = v;
         else spill = true;
     }
-    uint64_t sm = __ballot(spill);
-    while (sm) {
-        const int src = __ffsll((unsigned long long)sm) - 1;
-        sm &= sm - 1;
-        if (lane_id() == src) emit_single(c, v);
-    }
+    // the lanes that found the buffer full append their vertex directly
+    if (spill) emit_single(c, v);
 }
 
-// Claim v (reached from u) for level k+1: filter on a plain load of the
-// visited word, then one atomicOr decides the single winner.
-__device__ __forceinline__ void claim(Ctx &c, int v, int u) {
+// Claim up to N targets (v[q] valid where ok[q], reached from u[q]) for
+// level k+1: filter on plain loads of the visited words, then one atomicOr per
+// remaining target decides its single winner.  The N loads and the N atomics
+// are each issued before any result is used, so a lane keeps N claims in
+// flight instead of one.
+constexpr int CB = 4;
+
+template <int N>
+__device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const bool (&ok)[N],
+                                            const int (&u)[N]) {
+    constexpr int CB = N;
     const Params &P = *c.P;
-    const uint32_t bit = 1u << (v & 31);
-    uint32_t *wp = P.visited + (v >> 5);
-    bool win = false;
-    if (!(*wp & bit)) {
-        const uint32_t old = atomicOr(wp, bit);
-        win = !(old & bit);
+    uint32_t w[CB];
+#pragma unroll
+    for (int q = 0; q < CB; ++q) w[q] = ok[q] ? P.visited[v[q] >> 5] : ~0u;
+    bool tryq[CB];
+#pragma unroll
+    for (int q = 0; q < CB; ++q) tryq[q] = ok[q] && !((w[q] >> (v[q] & 31)) & 1u);
+    uint32_t old[CB];
+#pragma unroll
+    for (int q = 0; q < CB; ++q)
+        old[q] = tryq[q] ? atomicOr(P.visited + (v[q] >> 5), 1u << (v[q] & 31)) : ~0u;
+    bool win[CB];
+#pragma unroll
+    for (int q = 0; q < CB; ++q) {
+        win[q] = tryq[q] && !((old[q] >> (v[q] & 31)) & 1u);
+        if (win[q]) {
+            P.dist[v[q]] = c.level + 1;
+            if (P.parent) P.parent[v[q]] = u[q];
+            if (c.wbits) atomicOr(c.nbm + (v[q] >> 5), 1u << (v[q] & 31));
+        }
     }
-    if (win) {
-        P.dist[v] = c.level + 1;
-        if (P.parent) P.parent[v] = u;
-        if (c.wbits) atomicOr(c.nbm + (v >> 5), bit);
+#pragma unroll
+    for (int q = 0; q < CB; ++q) stage(c, win[q], v[q]);
+}
+
+// Claims for entries e0, e0+stride, ... (N of them) of col_idx below `end`.
+template <int N = CB>
+__device__ __forceinline__ void claim_run(Ctx &c, int e0, int stride, int end, int u) {
+    constexpr int CB = N;
+    const Params &P = *c.P;
+    int v[CB], uu[CB];
+    bool ok[CB];
+#pragma unroll
+    for (int q = 0; q < CB; ++q) {
+        const int e = e0 + q * stride;
+        ok[q] = e < end;
+        v[q] = ok[q] ? P.col_idx[e] : 0;
+        uu[q] = u;
     }
-    stage(c, win, v);
+    claim_batch(c, v, ok, uu);
 }
 
 // Workgroup flush of the staged vertices: one global atomic per list per
@@ -353,19 +385,18 @@ __device__ __forceinline__ void maybe_flush(Ctx &c) {
 // Expand the segments held by the threads of the workgroup (at most one per
 // thread): lane, wavefront or workgroup mapping by length.  Ends with a barrier.
 __device__ __forceinline__ void expand_segments(Ctx &c, bool has, int v, int beg, int len) {
-    const Params &P = *c.P;
     LevelShared &sh = *c.sh;
-    // lane bin
+    // lane bin: CB consecutive entries per step
     if (has && len < T_LANE) {
-        for (int e = beg; e < beg + len; ++e) claim(c, P.col_idx[e], v);
+        for (int e = beg; e < beg + len; e += CB) claim_run(c, e, 1, beg + len, v);
     }
-    // wavefront bin
+    // wavefront bin: lanes stride the list, CB entries per lane per step
     uint64_t mm = __ballot(has && len >= T_LANE && len < T_WG);
     while (mm) {
         const int src = __ffsll((unsigned long long)mm) - 1;
         mm &= mm - 1;
         const int sv = readlane_i(v, src), sb = readlane_i(beg, src), sl = readlane_i(len, src);
-        for (int e = lane_id(); e < sl; e += WAVE) claim(c, P.col_idx[sb + e], sv);
+        for (int e = lane_id(); e < sl; e += CB * WAVE) claim_run(c, sb + e, WAVE, sb + sl, sv);
     }
     // workgroup bin
     if (has && len >= T_WG) {
@@ -376,7 +407,13 @@ __device__ __forceinline__ void expand_segments(Ctx &c, bool has, int v, int beg
     const int nbig = sh.nbig;
     for (int i = 0; i < nbig; ++i) {
         const int bv = sh.big_v[i], bb = sh.big_beg[i], bl = sh.big_len[i];
-        for (int e = (int)threadIdx.x; e < bl; e += BLOCK) claim(c, P.col_idx[bb + e], bv);
+        // steps of STEP_CLAIMS entries, each followed by a flush check: a
+        // hub cannot overfill the staging buffer
+        for (int e0 = 0; e0 < bl; e0 += STEP_CLAIMS) {
+            __syncthreads();    // the previous step's staging is done
+            maybe_flush(c);
+            claim_run<STEP_CLAIMS / BLOCK>(c, bb + e0 + (int)threadIdx.x, BLOCK, bb + bl, bv);
+        }
     }
     __syncthreads();
     if (threadIdx.x == 0) sh.nbig = 0;
@@ -390,7 +427,7 @@ __device__ __forceinline__ void td_binned(Ctx &c, const Seg *cq, const Seg *ct, 
     const Params &P = *c.P;
     LevelShared &sh = *c.sh;
     const int total = sh.uprefix[NLISTS * STRIPES];
-    for (int u = blockIdx.x; u < total; u += gridDim.x) {
+    for (int u = c.wg; u < total; u += c.G) {
         // find (list, stripe) region of unit u
         int r = 0;
         while (sh.uprefix[r + 1] <= u) ++r;
@@ -429,7 +466,7 @@ __device__ __forceinline__ void td_edge_balanced(Ctx &c, const Seg *cq, const Se
     int32_t *s_v = sh.work + (EB_TE + 1);
     int32_t *s_beg = sh.work + 2 * (EB_TE + 1);
     const int total = sh.uprefix[NLISTS * STRIPES];
-    for (int u = blockIdx.x; u < total; u += gridDim.x) {
+    for (int u = c.wg; u < total; u += c.G) {
         int r = 0;
         while (sh.uprefix[r + 1] <= u) ++r;
         const int l = r / STRIPES, s = r % STRIPES;
@@ -437,7 +474,7 @@ __device__ __forceinline__ void td_edge_balanced(Ctx &c, const Seg *cq, const Se
         const int E = sh.ledges[r];
         const int N = sh.lcount[r];
         const int a = t * EB_TE;
-        const int b = min(a + EB_TE, E);
+        const int b = min(a + EB_TE, E);   // at most STEP_CLAIMS winners
         const int32_t *ts = cts + (size_t)r * P.tscap;
         const int i0 = ts[t];
         const int i1 = (a + EB_TE < E) ? ts[t + 1] : N - 1;
@@ -452,14 +489,26 @@ __device__ __forceinline__ void td_edge_balanced(Ctx &c, const Seg *cq, const Se
             if (sh.clear_bm) cbm[sg.v >> 5] = 0u;
         }
         __syncthreads();
-        for (int e = a + (int)threadIdx.x; e < b; e += BLOCK) {
-            // last j with s_off[j] <= e
-            int lo = 0, hi = ns;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (s_off[mid] <= e) lo = mid; else hi = mid;
+        static_assert(EB_TE % BLOCK == 0 && EB_TE <= STEP_CLAIMS, "one step per tile");
+        constexpr int NB = EB_TE / BLOCK;
+        {
+            const int e0 = a + (int)threadIdx.x;
+            int tv[NB], owner[NB];
+            bool ok[NB];
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+                const int e = e0 + q * BLOCK;
+                ok[q] = e < b;
+                // last j with s_off[j] <= e
+                int lo = 0, hi = ns;
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_off[mid] <= e) lo = mid; else hi = mid;
+                }
+                owner[q] = s_v[lo];
+                tv[q] = ok[q] ? P.col_idx[s_beg[lo] + (e - s_off[lo])] : 0;
             }
-            claim(c, P.col_idx[s_beg[lo] + (e - s_off[lo])], s_v[lo]);
+            claim_batch(c, tv, ok, owner);
         }
         __syncthreads();
         maybe_flush(c);
@@ -474,8 +523,8 @@ __device__ __forceinline__ void td_from_bitmap(Ctx &c, uint32_t *cbm, uint32_t *
     const Params &P = *c.P;
     LevelShared &sh = *c.sh;
     int32_t *flist = sh.work;
-    const int per = (P.nwp + gridDim.x - 1) / gridDim.x;
-    const int start = blockIdx.x * per;
+    const int per = (P.nwp + c.G - 1) / c.G;
+    const int start = c.wg * per;
     const int end = min(P.nwp, start + per);
     constexpr int R = FLIST_CAP / BLOCK;   // word pairs per wave per round
     for (int base = start; base < end; base += WAVES * R) {
@@ -532,8 +581,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ void bottom_up(Ctx &c, const uint32_t *cbm, uint32_t *nbm) {
     const Params &P = *c.P;
     LevelShared &sh = *c.sh;
-    const int per = (P.nwp + gridDim.x - 1) / gridDim.x;
-    const int start = blockIdx.x * per;
+    const int per = (P.nwp + c.G - 1) / c.G;
+    const int start = c.wg * per;
     const int end = min(P.nwp, start + per);
     const int lane = lane_id();
     const int wv = wave_id();
@@ -662,6 +711,8 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
             P.ctr[(size_t)i * CTR_STRIDE] = 0ull;
         if (threadIdx.x == 0) {
             P.ctl->done = 0; P.ctl->L = 0; P.ctl->err = 0; P.ctl->err_info = 0;
+            P.ctl->lvl[0] = 0; P.ctl->lvl[1] = 0;
+            P.ctl->bar_count = 0; P.ctl->bar_gen = 0;
             for (int k = 0; k < NSLOTS; ++k) {
                 P.ctl->slot[k].dir = 0; P.ctl->slot[k].wbits = 0;
                 P.ctl->slot[k].input_bm = 0; P.ctl->slot[k].fsize = 0;
@@ -671,7 +722,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
         __syncthreads();
         if (threadIdx.x == 0) {
             Ctx c;
-            c.P = &P; c.sh = nullptr; c.level = -1; c.stripe = 0; c.nslot = 0; c.wbits = 0;
+            c.P = &P; c.sh = nullptr; c.level = -1; c.wg = 0; c.G = 1; c.stripe = 0; c.nslot = 0; c.wbits = 0;
             c.nbm = nullptr; c.nq = P.q0; c.nt = P.t0; c.nts = P.ts0; c.fcnt = 0; c.fdeg = 0;
             const int beg = P.row_ptr[s];
             const int len = P.row_ptr[s + 1] - beg;
@@ -687,69 +738,100 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
     }
 }
 
-__global__ __launch_bounds__(BLOCK) void bfs_level_kernel(Params P, int32_t k) {
-    __shared__ LevelShared sh;
+// Decision for level k, taken by wavefront 0 of every workgroup from the
+// counters the previous level left (identical in every workgroup); the
+// caller synchronises before reading it.
+__device__ __forceinline__ void decide(const Params &P, LevelShared &sh, int k) {
     const int lane = lane_id();
     const int slot = k % NSLOTS;
-    if (threadIdx.x < WAVE) {
-        // wave 0 reads the level's counters and takes the decision
-        const int done = P.ctl->done;
-        unsigned long long cv = 0;
-        if (lane < NCTR) cv = *ctr_at(P, slot, lane);
-        const bool is_vc = lane >= VC_BASE && lane < NCTR;
-        const int64_t fsize = wave_sum<int64_t>(is_vc ? (int64_t)(cv >> 32) : 0);
-        const int64_t fdeg = wave_sum<int64_t>(is_vc ? (int64_t)(cv & 0xffffffffull) : 0);
-        if (lane < VC_BASE) {
-            sh.lcount[lane] = (int32_t)(cv >> 32);
-            sh.ledges[lane] = (int32_t)(cv & 0xffffffffull);
-        }
-        if (lane == 0) {
-            sh.cnt = 0; sh.nbig = 0; sh.fcnt = 0;
-            sh.fsize = (int32_t)fsize; sh.fdeg = fdeg;
-            if (done || P.ctl->err) {
-                sh.mode = 0;
-            } else if (fsize == 0) {
-                sh.mode = 1;
+    const int done = P.ctl->done;
+    unsigned long long cv = 0;
+    if (lane < NCTR) cv = *ctr_at(P, slot, lane);
+    const bool is_vc = lane >= VC_BASE && lane < NCTR;
+    const int64_t fsize = wave_sum<int64_t>(is_vc ? (int64_t)(cv >> 32) : 0);
+    const int64_t fdeg = wave_sum<int64_t>(is_vc ? (int64_t)(cv & 0xffffffffull) : 0);
+    if (lane < VC_BASE) {
+        sh.lcount[lane] = (int32_t)(cv >> 32);
+        sh.ledges[lane] = (int32_t)(cv & 0xffffffffull);
+    }
+    if (lane == 0) {
+        sh.cnt = 0; sh.nbig = 0; sh.fcnt = 0;
+        sh.fsize = (int32_t)fsize; sh.fdeg = fdeg;
+        sh.small = 0;
+        if (done || P.ctl->err) {
+            sh.mode = 0;
+        } else if (fsize == 0) {
+            sh.mode = 1;
+        } else {
+            sh.mode = 2;
+            const SlotInfo prev = (k > 0) ? P.ctl->slot[(k + NSLOTS - 1) % NSLOTS] : SlotInfo{0, 0, 0, 0, 0, 0};
+            const int64_t reached_before = (k > 0) ? P.ctl->slot[slot].reached_before : 0;
+            const int64_t edges_before = (k > 0) ? P.ctl->slot[slot].edges_before : 0;
+            const bool has_queue = (k == 0) || prev.dir == DIR_TD;
+            const bool has_bm = (k == 0) || prev.dir == DIR_BU || prev.wbits;
+            bool want_pull;
+            if (P.pol_dir == BFS_DIR_PULL) {
+                want_pull = true;
+            } else if (P.pol_dir == BFS_DIR_PUSH) {
+                want_pull = false;
+            } else if (k == 0 || prev.dir == DIR_TD) {
+                // edges still to be explored from unvisited vertices
+                const int64_t m_u = (int64_t)P.m - edges_before - fdeg;
+                want_pull = fdeg * ALPHA > m_u;
             } else {
-                sh.mode = 2;
-                const SlotInfo prev = (k > 0) ? P.ctl->slot[(k + NSLOTS - 1) % NSLOTS] : SlotInfo{0, 0, 0, 0, 0, 0};
-                const int64_t reached_before = (k > 0) ? P.ctl->slot[slot].reached_before : 0;
-                const int64_t edges_before = (k > 0) ? P.ctl->slot[slot].edges_before : 0;
-                const bool has_queue = (k == 0) || prev.dir == DIR_TD;
-                const bool has_bm = (k == 0) || prev.dir == DIR_BU || prev.wbits;
-                bool want_pull;
-                if (P.pol_dir == BFS_DIR_PULL) {
-                    want_pull = true;
-                } else if (P.pol_dir == BFS_DIR_PUSH) {
-                    want_pull = false;
-                } else if (k == 0 || prev.dir == DIR_TD) {
-                    // edges still to be explored from unvisited vertices
-                    const int64_t m_u = (int64_t)P.m - edges_before - fdeg;
-                    want_pull = fdeg * ALPHA > m_u;
-                } else {
-                    want_pull = !(fsize * BETA < (int64_t)P.n && fsize < prev.fsize);
+                want_pull = !(fsize * BETA < (int64_t)P.n && fsize < prev.fsize);
+            }
+            const int dir = (want_pull && P.symmetric && has_bm) ? DIR_BU : DIR_TD;
+            sh.dir = dir;
+            sh.reached_before = reached_before;
+            sh.edges_before = edges_before;
+            sh.input_bm = (dir == DIR_TD) && !has_queue;
+            sh.clear_bm = (dir == DIR_TD) && has_queue && has_bm;
+            // a top-down level from a queue also sets its new vertices in the
+            // next bitmap whenever the next level may pull
+            sh.wbits = (dir == DIR_TD) && has_queue && P.symmetric && P.pol_dir == BFS_DIR_AUTO;
+            // edge-balanced unless the binned advance is forced: its tiles
+            // spread even a small frontier over several workgroups and
+            // bound the winners between flushes
+            sh.adv_eb = (dir == DIR_TD) && has_queue && P.pol_adv != BFS_ADV_BINNED;
+            sh.small = P.small_mode && (dir == DIR_TD) && has_queue && fsize <= SMALL_F && fdeg <= SMALL_E;
+        }
+    }
+}
+
+// Barrier among the G workgroups of the small-frontier mode (all resident:
+// the others exit at once).  Release before arriving, acquire after leaving,
+// both at device scope so queues, bitmaps and counters written before it are
+// seen after it.  The wait is bounded: past the limit it records
+// ERR_BARRIER_TIMEOUT and returns, and every workgroup then leaves its loop.
+__device__ __forceinline__ void small_barrier(const Params &P, int G) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        const uint32_t gen = __hip_atomic_load(&P.ctl->bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t arrived = atomicAdd(&P.ctl->bar_count, 1u);
+        if (arrived == (uint32_t)G - 1) {
+            __hip_atomic_store(&P.ctl->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&P.ctl->bar_gen, gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            while (__hip_atomic_load(&P.ctl->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+                __builtin_amdgcn_s_sleep(2);
+                if (__builtin_amdgcn_s_memrealtime() - t0 > P.barrier_ticks) {
+                    atomicCAS(&P.ctl->err, 0, ERR_BARRIER_TIMEOUT);
+                    break;
                 }
-                const int dir = (want_pull && P.symmetric && has_bm) ? DIR_BU : DIR_TD;
-                sh.dir = dir;
-                sh.reached_before = reached_before;
-                sh.edges_before = edges_before;
-                sh.input_bm = (dir == DIR_TD) && !has_queue;
-                sh.clear_bm = (dir == DIR_TD) && has_queue && has_bm;
-                // a top-down level from a queue also sets its new vertices in the
-                // next bitmap whenever the next level may pull
-                sh.wbits = (dir == DIR_TD) && has_queue && P.symmetric && P.pol_dir == BFS_DIR_AUTO;
-                sh.adv_eb = (dir == DIR_TD) && has_queue &&
-                            (P.pol_adv == BFS_ADV_EDGE || (P.pol_adv == BFS_ADV_AUTO && fsize >= 4096));
             }
         }
+        __threadfence();
     }
     __syncthreads();
-    const int mode = sh.mode;
-    if (mode == 0) return;
-    if (mode == 1) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) { P.ctl->L = k; P.ctl->done = 1; }
-        return;
-    }
+}
+
+// One level on the G workgroups taking part (this one is number wg).
+__device__ __forceinline__ void run_level(const Params &P, LevelShared &sh, int k, int wg, int G) {
+    const int lane = lane_id();
+    const int slot = k % NSLOTS;
     // unit prefix tables
     if (threadIdx.x == 0) {
         int acc = 0;
@@ -766,7 +848,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_level_kernel(Params P, int32_t k) {
         sh.uprefix[NLISTS * STRIPES] = acc;
     }
     // bookkeeping of level k by workgroup 0
-    if (blockIdx.x == 0) {
+    if (wg == 0) {
         if (threadIdx.x == 0) {
             if (P.level_sizes) P.level_sizes[k] = sh.fsize;
             if (k < P.st_cap) { P.st_dir[k] = (int8_t)sh.dir; P.st_fdeg[k] = sh.fdeg; }
@@ -785,7 +867,9 @@ __global__ __launch_bounds__(BLOCK) void bfs_level_kernel(Params P, int32_t k) {
     c.P = &P;
     c.sh = &sh;
     c.level = k;
-    c.stripe = blockIdx.x % STRIPES;
+    c.wg = wg;
+    c.G = G;
+    c.stripe = wg % STRIPES;
     c.nslot = (k + 1) % NSLOTS;
     c.wbits = sh.wbits;
     const int cur = k & 1;
@@ -825,6 +909,39 @@ __global__ __launch_bounds__(BLOCK) void bfs_level_kernel(Params P, int32_t k) {
         for (int w = 0; w < WAVES; ++w) { tc += sh.scan_tmp[0][w]; td += sh.scan_tmp[1][w]; }
         if (tc) atomicAdd(ctr_at(P, c.nslot, VC_BASE + c.stripe), (unsigned long long)((tc << 32) | td));
     }
+}
+
+// One launch: runs the level lvl[launch & 1] on the whole grid, or, when that
+// level is small, runs levels on the first SMALL_G workgroups until one is
+// not small; then records where the next launch starts.
+__global__ __launch_bounds__(BLOCK, 4) void bfs_level_kernel(Params P, int32_t launch) {
+    __shared__ LevelShared sh;
+    int k = P.ctl->lvl[launch & 1];
+    if (threadIdx.x < WAVE) decide(P, sh, k);
+    __syncthreads();
+    if (sh.mode == 0) return;
+    if (sh.mode == 1) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) { P.ctl->L = k; P.ctl->done = 1; }
+        return;
+    }
+    const bool small = sh.small;
+    if (small && blockIdx.x >= SMALL_G) return;
+    const int G = small ? min((int)gridDim.x, SMALL_G) : (int)gridDim.x;
+    for (;;) {
+        run_level(P, sh, k, blockIdx.x, G);
+        ++k;
+        if (!small) break;
+        small_barrier(P, G);
+        if (threadIdx.x < WAVE) decide(P, sh, k);
+        __syncthreads();
+        if (sh.mode == 0) return;    // an error was recorded
+        if (sh.mode == 1) {
+            if (blockIdx.x == 0 && threadIdx.x == 0) { P.ctl->L = k; P.ctl->done = 1; }
+            return;
+        }
+        if (!sh.small) break;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) P.ctl->lvl[(launch + 1) & 1] = k;
 }
 
 // ------------------------------------------------- graph validation --------
@@ -910,8 +1027,8 @@ hipError_t launch_init(const Params &P, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_level(const Params &P, int32_t level, int grid, hipStream_t s) {
-    hipLaunchKernelGGL(bfs_level_kernel, dim3(grid), dim3(BLOCK), 0, s, P, level);
+hipError_t launch_level(const Params &P, int32_t launch_index, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(bfs_level_kernel, dim3(grid), dim3(BLOCK), 0, s, P, launch_index);
     return hipGetLastError();
 }
 

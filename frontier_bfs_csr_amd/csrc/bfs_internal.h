@@ -17,7 +17,9 @@ constexpr int T_WG = BLOCK;              // T_LANE <= degree < T_WG: one wavefro
 constexpr int TILE = 4 * BLOCK;          // degree >= T_WG: split into tiles of TILE edges,
                                          // one workgroup per tile
 constexpr int CAP = 2048;                // LDS staging capacity for new frontier vertices
-constexpr int EB_TE = 2048;              // edges per tile of the edge-balanced advance
+constexpr int STEP_CLAIMS = CAP / 2;     // claims between flush checks: a flush starts at
+                                         // CAP / 2 staged, so a step never overfills
+constexpr int EB_TE = 1024;              // edges per tile of the edge-balanced advance
 constexpr int BU_LANE_SCAN = 32;         // bottom-up: entries a lane scans alone before
                                          // its list is handed to the whole wavefront
 constexpr int BU_GP = 8;                 // bottom-up: word pairs a wavefront gathers at a time
@@ -66,12 +68,26 @@ struct Ctl {
     int32_t L;            // number of non-empty levels
     int32_t err;          // nonzero: internal limit exceeded (see ERR_*)
     int32_t err_info;
+    int32_t lvl[2];       // level the launch with index i starts at: lvl[i & 1]
+    int32_t pad0[2];
     SlotInfo slot[NSLOTS];
+    // barrier of the small-frontier mode, each word alone in 128 bytes
+    alignas(128) uint32_t bar_count;
+    alignas(128) uint32_t bar_gen;
+    alignas(128) uint32_t pad1;
 };
 
 constexpr int ERR_QUEUE_OVERFLOW = 1;
 constexpr int ERR_TILE_OVERFLOW = 2;
 constexpr int ERR_TSTART_OVERFLOW = 3;
+constexpr int ERR_BARRIER_TIMEOUT = 4;
+
+// small-frontier mode: a top-down level whose frontier has at most SMALL_F
+// vertices and SMALL_E edges runs on the first SMALL_G workgroups only, and
+// those keep going level after level with a barrier among themselves
+constexpr int SMALL_G = 32;
+constexpr int SMALL_F = SMALL_G * BLOCK;
+constexpr int SMALL_E = 4 * SMALL_F;
 
 struct Params {
     const int32_t *row_ptr;
@@ -100,11 +116,13 @@ struct Params {
     int32_t col_vec;          // col_idx is 16-byte aligned: 16-byte loads allowed
     int32_t pol_dir;          // BFS_DIR_*
     int32_t pol_adv;          // BFS_ADV_*
+    int32_t small_mode;       // allow the small-frontier mode
+    uint32_t barrier_ticks;   // small-mode barrier wait limit (100 MHz ticks)
 };
 
 // host-side launch helpers (bfs_device.hip)
 hipError_t launch_init(const Params &P, int grid, hipStream_t s);
-hipError_t launch_level(const Params &P, int32_t level, int grid, hipStream_t s);
+hipError_t launch_level(const Params &P, int32_t launch_index, int grid, hipStream_t s);
 int level_kernel_blocks_per_cu();
 
 // graph validation / classification (bfs_device.hip)

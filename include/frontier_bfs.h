@@ -89,19 +89,29 @@ const char *bfs_last_error(void);
 #define BFS_DIR_AUTO 0
 #define BFS_DIR_PUSH 1
 #define BFS_DIR_PULL 2
-/* Top-down advance: automatic, degree-binned (lane / wavefront / workgroup,
- * hubs split across workgroups), edge-balanced (frontier-degree scan plus
- * tile partition by search over the scan). */
+/* Top-down advance: automatic (currently edge-balanced for every top-down
+ * level that starts from a queue), degree-binned (lane / wavefront /
+ * workgroup, hubs split across workgroups), edge-balanced (frontier-degree
+ * scan plus tile partition by search over the scan). */
 #define BFS_ADV_AUTO   0
 #define BFS_ADV_BINNED 1
 #define BFS_ADV_EDGE   2
 
-/* Level loop: device-resident (level launches are enqueued ahead in growing
- * batches and read the frontier size from device memory; the host waits once
- * per batch), or host-driven (the host waits for every level's count before
- * the next launch, as bfs.cu's runBfs in the Day 38 program does). */
+/* Level loop.
+ *   DEVICE (default): launches are enqueued ahead in growing batches, read the
+ *     level to run and the frontier from device memory, and the host waits once
+ *     per batch; a small top-down level (up to 16,384 vertices and 65,536
+ *     edges) runs on 32 workgroups that carry on level after level with a
+ *     barrier among themselves, so a long thin search is a handful of launches.
+ *   HOST: one level per launch and the host waits for every level before the
+ *     next launch, as bfs.cu's runBfs in the Day 38 program does.
+ *   CHAIN: as DEVICE but one level per launch (no small-frontier mode).
+ * The small-frontier barrier's wait is bounded (2 s; the environment variable
+ * FBFS_BARRIER_TIMEOUT_US, read at bfs_graph_create, overrides it for tests):
+ * past it bfs_run returns BFS_EDEVICE instead of waiting forever. */
 #define BFS_LOOP_DEVICE 0
 #define BFS_LOOP_HOST   1
+#define BFS_LOOP_CHAIN  2
 
 /*
  * Forces a policy for later bfs_run calls on this handle.  dist, L and the

@@ -13,6 +13,7 @@ POLICIES = {
     "pull": (2, 0, 0),
     "auto_edge": (0, 2, 0),
     "auto_binned_hostloop": (0, 1, 1),
+    "auto_chain": (0, 0, 2),
 }
 
 
