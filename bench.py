@@ -6,10 +6,11 @@ Prints ONE JSON line:
 
   value       GTEPS = sum over timed steps of the undirected edges in the
               source's component / wall time of the timed steps
-  roofline    for the dominant kernel (the per-level kernel): algorithmic bytes
-              of all its launches (byte model in
-              frontier_bfs_csr_amd/csrc/bytemodel.c) / its summed launch time
-              from HIP events on the search stream, against 8 TB/s of HBM3E
+  roofline    for the dominant level kernel (bfs_td_kernel or bfs_bu_kernel,
+              whichever takes more time): algorithmic bytes of the levels it
+              ran (byte model in frontier_bfs_csr_amd/csrc/bytemodel.c) / its
+              summed launch time, each launch timed by HIP events on the search
+              stream in a second pass over the same sources, against 8 TB/s
   cpu_baseline  the CPU oracle (serial FIFO BFS, one core) on a bounded sample
               of the same sources, same GTEPS definition
 
@@ -38,7 +39,8 @@ WORKLOAD_DESC = {
     "c4": "grid4096_del5: 4096x4096 4-neighbour grid, 5% edges deleted, largest component, corner source",
     "c5": "rmat24_ef16: R-MAT scale 24, edge factor 16, (0.57,0.19,0.19,0.05), symmetrised, deduplicated",
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_kernel_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_kernels_traffic.json")
+KERNEL_NAMES = {"td": "bfs_td_kernel", "bu": "bfs_bu_kernel"}
 
 
 def kernel_source_hash():
@@ -49,15 +51,15 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per level-kernel launch from the committed PMC summary, if it
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed PMC summary, if it
     was taken on the current kernel source for this workload; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get(workload)
+    e = t.get(workload, {}).get(kernel)
     if not e or e.get("kernel_source_hash") != kernel_source_hash():
         return None
     return e.get("bytes_per_launch")
@@ -89,6 +91,8 @@ def main():
     ap.add_argument("--direction", type=int, default=0, help="0 auto, 1 push, 2 pull")
     ap.add_argument("--advance", type=int, default=0, help="0 auto, 1 binned, 2 edge-balanced")
     ap.add_argument("--loop", type=int, default=0, help="0 device-resident, 1 host-driven")
+    ap.add_argument("--alpha", type=int, default=14, help="direction switch: pull when alpha*deg(F) > deg(U)")
+    ap.add_argument("--beta", type=int, default=24, help="direction switch: push when beta*|F| < n, shrinking")
     ap.add_argument("--no-parent", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the CPU-oracle baseline sample")
@@ -122,7 +126,7 @@ def main():
     stream = torch.cuda.current_stream()
     bg = fb.BfsGraph(rp, ci)
     bg.set_policy(args.direction, args.advance, args.loop)
-    bg.set_timing(True)
+    bg.set_switch(args.alpha, args.beta)
     dist = torch.empty(g.n, dtype=torch.int32, device=dev)
     parent = None if args.no_parent else torch.empty(g.n, dtype=torch.int32, device=dev)
     sizes = torch.empty(g.n, dtype=torch.int32, device=dev)
@@ -131,6 +135,8 @@ def main():
     def step(i):
         return bg.run(sources[i % len(sources)], dist, parent, sizes, stream)
 
+    # timed pass: the timing hook off, so only the searches are in the wall time
+    bg.set_timing(False)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -139,10 +145,24 @@ def main():
     for i in range(args.steps):
         ts = time.perf_counter()
         L = step(i)
-        per_step.append((sources[i % len(sources)], L, time.perf_counter() - ts, *bg.timing()))
+        per_step.append((sources[i % len(sources)], L, time.perf_counter() - ts))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     print(f"[bench] timed {args.steps} searches in {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
+
+    # kernel pass: the same searches again, every level launch timed by HIP
+    # events on the search stream
+    bg.set_timing(True)
+    init_ms, level_ms, launches = 0.0, 0.0, 0
+    kt = {"td": [0.0, 0], "bu": [0.0, 0]}
+    for i in range(args.steps):
+        step(i)
+        a, b, c = bg.timing()
+        init_ms, level_ms, launches = init_ms + a, level_ms + b, launches + c
+        for kind, (ms, nl) in bg.kernel_timing().items():
+            kt[kind][0] += ms
+            kt[kind][1] += nl
+    bg.set_timing(False)
 
     # per distinct source: result, directions, byte model, component edges
     model = {}
@@ -153,19 +173,24 @@ def main():
         d = dist.cpu().numpy()
         init_b, lvl_b = bytemodel.alg_bytes(g.row_ptr, g.col_idx, d, dirs, with_parent=parent is not None)
         model[s] = {"L": L, "init": init_b, "levels": int(lvl_b.sum()), "medges": component_edges(deg, d),
+                    "td": int(lvl_b[dirs == 0].sum()), "bu": int(lvl_b[dirs == 1].sum()),
                     "dirs": "".join("TB"[x] for x in dirs)}
         gpu_dist[s] = d if len(gpu_dist) < 8 else None
 
     edges = sum(model[s]["medges"] for s, *_ in per_step)
     value = edges / wall / 1e9
-    level_ms = sum(p[4] for p in per_step)
-    init_ms = sum(p[3] for p in per_step)
-    launches = sum(p[5] for p in per_step)
     bytes_levels = sum(model[s]["levels"] for s, *_ in per_step)
     bytes_init = sum(model[s]["init"] for s, *_ in per_step)
-    achieved = bytes_levels / (level_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload)
-    step_gteps = [model[s]["medges"] / t / 1e9 for s, L, t, *_ in per_step]
+    kinds = {}
+    for kind in ("td", "bu"):
+        ms, nl = kt[kind]
+        b = sum(model[s][kind] for s, *_ in per_step)
+        kinds[kind] = {"kernel": KERNEL_NAMES[kind], "ms": ms, "launches": nl, "bytes": b,
+                       "achieved": b / (ms * 1e-3) / 1e9 if ms > 0 else 0.0}
+    dom = max(kinds, key=lambda k: kinds[k]["ms"])
+    kd = kinds[dom]
+    traffic = measured_traffic(args.workload, kd["kernel"])
+    step_gteps = [model[s]["medges"] / t / 1e9 for s, L, t in per_step]
 
     cpu = None
     parity_sample = None
@@ -205,20 +230,26 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_DESC[args.workload], "n": g.n, "m_csr_entries": g.m,
                    "sources": len(sources), "parent_out": parent is not None,
-                   "policy": {"direction": args.direction, "advance": args.advance, "loop": args.loop}},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                   "policy": {"direction": args.direction, "advance": args.advance, "loop": args.loop,
+                              "alpha": args.alpha, "beta": args.beta}},
+        "roofline": {"bound": "hbm", "achieved": round(kd["achieved"], 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(kd["achieved"] / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "bfs_level_kernel",
-                     "bytes_per_launch": round(bytes_levels / launches),
-                     "avg_launch_us": round(level_ms / launches * 1e3, 3),
-                     "launches": launches},
+                     "kernel": kd["kernel"],
+                     "bytes_per_launch": round(kd["bytes"] / max(kd["launches"], 1)),
+                     "avg_launch_us": round(kd["ms"] / max(kd["launches"], 1) * 1e3, 3),
+                     "launches": kd["launches"]},
         "cpu_baseline": cpu,
         "detail": {
             "ms_per_bfs_median": round(float(np.median([p[2] for p in per_step])) * 1e3, 4),
             "gteps_hmean": round(len(step_gteps) / sum(1.0 / x for x in step_gteps), 4),
             "init_kernel_us_avg": round(init_ms / args.steps * 1e3, 2),
             "level_kernels_ms_avg": round(level_ms / args.steps, 4),
+            "level_launches_avg": round(launches / args.steps, 2),
+            "kernels": {v["kernel"]: {"ms_avg": round(v["ms"] / args.steps, 4),
+                                      "launches": v["launches"],
+                                      "alg_GB_per_s": round(v["achieved"], 1)}
+                        for v in kinds.values()},
             "alg_GB_per_bfs": round((bytes_levels + bytes_init) / args.steps / 1e9, 4),
             "whole_bfs_alg_GBps": round((bytes_levels + bytes_init) / wall / 1e9, 1),
             "levels_first_source": model[s0]["L"],

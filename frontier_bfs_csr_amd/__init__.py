@@ -14,7 +14,9 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libfrontier_bfs.so")
+# FBFS_LIBRARY names another build of the same library (e.g. a variant built
+# with different compile-time constants); default: the in-tree build.
+LIB_PATH = os.environ.get("FBFS_LIBRARY") or os.path.join(_PKG, "libfrontier_bfs.so")
 
 BFS_EINVAL, BFS_EHIP, BFS_ENOMEM, BFS_EDEVICE = -1, -2, -3, -4
 DIR_AUTO, DIR_PUSH, DIR_PULL = 0, 1, 2
@@ -23,7 +25,7 @@ LOOP_DEVICE, LOOP_HOST, LOOP_CHAIN = 0, 1, 2
 
 EXPORTS = ("bfs_graph_create", "bfs_run", "bfs_graph_destroy", "bfs_last_error",
            "bfs_set_policy", "bfs_last_run_stats", "bfs_set_timing", "bfs_last_run_timing",
-           "bfs_graph_info")
+           "bfs_graph_info", "bfs_set_switch", "bfs_last_run_kernel_timing")
 
 _lib = None
 
@@ -53,6 +55,8 @@ def load():
         lib.bfs_last_error.restype = ctypes.c_char_p
         lib.bfs_set_policy.argtypes = [P, i32, i32, i32]
         lib.bfs_set_policy.restype = i32
+        lib.bfs_set_switch.argtypes = [P, i32, i32]
+        lib.bfs_set_switch.restype = i32
         lib.bfs_last_run_stats.argtypes = [P, i32, P, P]
         lib.bfs_last_run_stats.restype = i32
         lib.bfs_graph_info.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i32),
@@ -63,6 +67,9 @@ def load():
         lib.bfs_last_run_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float),
                                             ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
         lib.bfs_last_run_timing.restype = i32
+        lib.bfs_last_run_kernel_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32),
+                                                   ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+        lib.bfs_last_run_kernel_timing.restype = i32
         _lib = lib
     return _lib
 
@@ -124,6 +131,12 @@ def bfs_set_policy(g, direction=DIR_AUTO, advance=ADV_AUTO, loop=LOOP_DEVICE):
         raise BfsError(rc, bfs_last_error())
 
 
+def bfs_set_switch(g, alpha=14, beta=24):
+    rc = load().bfs_set_switch(g, int(alpha), int(beta))
+    if rc < 0:
+        raise BfsError(rc, bfs_last_error())
+
+
 def bfs_last_run_stats(g, cap=1 << 22):
     """(L, dir[int8, per level: 0 top-down, 1 bottom-up], frontier_edges[int64])."""
     L0 = load().bfs_last_run_stats(g, 0, None, None)
@@ -154,6 +167,17 @@ def bfs_last_run_timing(g):
     return a.value, b.value, c.value
 
 
+def bfs_last_run_kernel_timing(g):
+    """{"td": (ms, launches), "bu": (ms, launches)} of the last timed run."""
+    a, b = ctypes.c_float(), ctypes.c_float()
+    c, d = ctypes.c_int32(), ctypes.c_int32()
+    rc = load().bfs_last_run_kernel_timing(g, ctypes.byref(a), ctypes.byref(c), ctypes.byref(b),
+                                           ctypes.byref(d))
+    if rc < 0:
+        raise BfsError(rc, bfs_last_error())
+    return {"td": (a.value, c.value), "bu": (b.value, d.value)}
+
+
 def bfs_graph_info(g):
     m, srt, sym, mx = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     rc = load().bfs_graph_info(g, ctypes.byref(m), ctypes.byref(srt), ctypes.byref(sym),
@@ -179,6 +203,9 @@ class BfsGraph:
     def set_policy(self, direction=DIR_AUTO, advance=ADV_AUTO, loop=LOOP_DEVICE):
         bfs_set_policy(self.handle, direction, advance, loop)
 
+    def set_switch(self, alpha=14, beta=24):
+        bfs_set_switch(self.handle, alpha, beta)
+
     def stats(self):
         return bfs_last_run_stats(self.handle)
 
@@ -190,6 +217,9 @@ class BfsGraph:
 
     def timing(self):
         return bfs_last_run_timing(self.handle)
+
+    def kernel_timing(self):
+        return bfs_last_run_kernel_timing(self.handle)
 
     def close(self):
         if self.handle:

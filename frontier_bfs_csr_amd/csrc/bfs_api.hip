@@ -43,6 +43,8 @@ struct bfs_graph {
     int32_t sorted = 0, symmetric = 0, max_degree = 0;
     int grid = 0;
     uint32_t *visited = nullptr, *vis_init = nullptr, *fbm0 = nullptr, *fbm1 = nullptr;
+    uint32_t *cf = nullptr;        // 3 coarse frontier maps
+    int32_t cf_sh = 0, cf_words = 0;
     Seg *q0 = nullptr, *q1 = nullptr, *t0 = nullptr, *t1 = nullptr;
     int32_t *ts0 = nullptr, *ts1 = nullptr;
     int64_t qcap = 0, tcap = 0, tscap = 0;
@@ -54,6 +56,7 @@ struct bfs_graph {
     HostCtl *host_ctl = nullptr;   // pinned
     GraphFacts *facts = nullptr;   // device, create only
     int32_t pol_dir = BFS_DIR_AUTO, pol_adv = BFS_ADV_AUTO, pol_loop = BFS_LOOP_DEVICE;
+    int32_t alpha = ALPHA, beta = BETA;
     uint32_t barrier_ticks = 200000000u;   // 2 s at 100 MHz
     int32_t last_L = 0;
     // timing hook
@@ -61,7 +64,10 @@ struct bfs_graph {
     int32_t last_timed = 0;
     float last_init_ms = 0.f, last_level_ms = 0.f;
     int32_t last_launches = 0;
-    std::vector<hipEvent_t> events;   // [0,1] init, then pairs per batch
+    float last_kind_ms[2] = {0.f, 0.f};       // top-down, bottom-up launches
+    int32_t last_kind_launches[2] = {0, 0};
+    std::vector<hipEvent_t> events;   // [0,1] init, then one before and one after each
+                                      // launch of a batch
 };
 
 namespace {
@@ -82,7 +88,7 @@ hipError_t dalloc(T **p, size_t count) {
 }
 
 void free_all(bfs_graph *g) {
-    void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->q0, g->q1, g->t0, g->t1,
+    void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->cf, g->q0, g->q1, g->t0, g->t1,
                     g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
@@ -108,6 +114,10 @@ int alloc_workspace(bfs_graph *g) {
     g->tcap = m / TILE + m / T_WG + 1;
     g->tscap = m / EB_TE + 2;
     g->st_cap = (int32_t)((n + 1) < (1 << 22) ? (n + 1) : (1 << 22));
+    // coarse frontier map: the finest power-of-two grain that fits CF_WORDS words
+    g->cf_sh = 0;
+    while (((n + (1LL << g->cf_sh) - 1) >> g->cf_sh) > (int64_t)CF_WORDS * 32) ++g->cf_sh;
+    g->cf_words = (int32_t)((((n + (1LL << g->cf_sh) - 1) >> g->cf_sh) + 31) / 32);
     struct {
         hipError_t e;
         const char *what;
@@ -116,6 +126,7 @@ int alloc_workspace(bfs_graph *g) {
         {dalloc(&g->vis_init, 2 * nwp), "visited template"},
         {dalloc(&g->fbm0, 2 * nwp), "frontier bitmap"},
         {dalloc(&g->fbm1, 2 * nwp), "frontier bitmap"},
+        {dalloc(&g->cf, 3 * (int64_t)CF_WORDS), "coarse frontier maps"},
         {dalloc(&g->q0, (size_t)STRIPES * g->qcap), "frontier queue"},
         {dalloc(&g->q1, (size_t)STRIPES * g->qcap), "frontier queue"},
         {dalloc(&g->t0, (size_t)STRIPES * g->tcap), "tile queue"},
@@ -280,6 +291,21 @@ int32_t bfs_set_policy(bfs_graph *g, int32_t direction, int32_t advance, int32_t
     return 0;
 }
 
+int32_t bfs_set_switch(bfs_graph *g, int32_t alpha, int32_t beta) {
+    if (!g) {
+        set_error("NULL graph handle");
+        return BFS_EINVAL;
+    }
+    if (alpha < 1 || alpha > 1000000 || beta < 1 || beta > 1000000) {
+        set_error("switch parameters out of range (alpha %d, beta %d; each must be in [1, 1e6])",
+                  alpha, beta);
+        return BFS_EINVAL;
+    }
+    g->alpha = alpha;
+    g->beta = beta;
+    return 0;
+}
+
 int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent_out,
                 int32_t *level_sizes_out, hipStream_t stream) {
     g_err.clear();
@@ -311,6 +337,9 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.vis_init = g->vis_init;
     P.fbm0 = g->fbm0;
     P.fbm1 = g->fbm1;
+    P.cf = g->cf;
+    P.cf_sh = g->cf_sh;
+    P.cf_words = g->cf_words;
     P.q0 = g->q0;
     P.q1 = g->q1;
     P.t0 = g->t0;
@@ -330,6 +359,9 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.pol_dir = g->pol_dir;
     P.pol_adv = g->pol_adv;
     P.small_mode = g->pol_loop == BFS_LOOP_DEVICE;
+    P.alpha = g->alpha;
+    P.max_deg = g->max_degree;
+    P.beta = g->beta;
     P.barrier_ticks = g->barrier_ticks;
 
     const bool timing = g->timing != 0;
@@ -342,30 +374,36 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     if (timing) HIP_TRY(hipEventRecord(g->events[1], stream), BFS_EHIP);
     const bool host_loop = g->pol_loop == BFS_LOOP_HOST;
     int64_t k = 0;
-    int64_t batch = host_loop ? 1 : 8;
-    size_t nbatch = 0;
-    float level_ms = 0.f;
-    // every launch runs at least one level or finds the empty frontier, and
-    // L <= n, so launch n has found it
-    const int64_t kmax = (int64_t)g->n + 1;
+    // a first batch of 12 launches covers most searches of under ten levels
+    int64_t batch = host_loop ? 1 : 12;
+    float level_ms = 0.f, kind_ms[2] = {0.f, 0.f};
+    int32_t kind_launches[2] = {0, 0};
+    // launches alternate top-down (even index) and bottom-up (odd index); each
+    // pair runs at least one level or finds the empty frontier, and L <= n,
+    // so launch 2n + 1 has found it
+    const int64_t kmax = 2 * (int64_t)g->n + 2;
     for (;;) {
+        const int64_t k0 = k;
         if (timing) {
-            HIP_TRY(ensure_events(g, 2 + 2 * (nbatch + 1)), BFS_EHIP);
-            HIP_TRY(hipEventRecord(g->events[2 + 2 * nbatch], stream), BFS_EHIP);
+            HIP_TRY(ensure_events(g, 2 + (size_t)batch + 1), BFS_EHIP);
+            HIP_TRY(hipEventRecord(g->events[2], stream), BFS_EHIP);
         }
-        for (int64_t i = 0; i < batch && k <= kmax; ++i, ++k)
+        for (int64_t i = 0; i < batch && k <= kmax; ++i, ++k) {
             HIP_TRY(launch_level(P, (int32_t)k, g->grid, stream), BFS_EHIP);   // k = launch index
-        if (timing) HIP_TRY(hipEventRecord(g->events[3 + 2 * nbatch], stream), BFS_EHIP);
+            if (timing) HIP_TRY(hipEventRecord(g->events[3 + i], stream), BFS_EHIP);
+        }
         HIP_TRY(hipMemcpyAsync(g->host_ctl, g->ctl, sizeof(HostCtl), hipMemcpyDeviceToHost, stream),
                 BFS_EHIP);
         HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
         if (timing) {
-            float ms = 0.f;
-            HIP_TRY(hipEventElapsedTime(&ms, g->events[2 + 2 * nbatch], g->events[3 + 2 * nbatch]),
-                    BFS_EHIP);
-            level_ms += ms;
+            for (int64_t i = 0; i < k - k0; ++i) {
+                float ms = 0.f;
+                HIP_TRY(hipEventElapsedTime(&ms, g->events[2 + i], g->events[3 + i]), BFS_EHIP);
+                level_ms += ms;
+                kind_ms[(k0 + i) & 1] += ms;
+                kind_launches[(k0 + i) & 1] += 1;
+            }
         }
-        ++nbatch;
         const HostCtl h = *g->host_ctl;
         if (h.err) {
             if (h.err == ERR_BARRIER_TIMEOUT)
@@ -382,12 +420,16 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
                 g->last_init_ms = ms;
                 g->last_level_ms = level_ms;
                 g->last_launches = (int32_t)k;
+                for (int t = 0; t < 2; ++t) {
+                    g->last_kind_ms[t] = kind_ms[t];
+                    g->last_kind_launches[t] = kind_launches[t];
+                }
                 g->last_timed = 1;
             }
             return h.L;
         }
         if (k > kmax) {
-            set_error("search did not terminate after %lld levels", (long long)k);
+            set_error("search did not terminate after %lld level launches", (long long)k);
             return BFS_EDEVICE;
         }
         if (!host_loop && batch < 1024) batch *= 2;
@@ -416,6 +458,19 @@ int32_t bfs_set_timing(bfs_graph *g, int32_t on) {
         return BFS_EINVAL;
     }
     g->timing = on ? 1 : 0;
+    return 0;
+}
+
+int32_t bfs_last_run_kernel_timing(const bfs_graph *g, float *td_ms, int32_t *td_launches,
+                                   float *bu_ms, int32_t *bu_launches) {
+    if (!g || !g->last_timed) {
+        set_error(g ? "the last run was not timed (bfs_set_timing)" : "NULL graph handle");
+        return BFS_EINVAL;
+    }
+    if (td_ms) *td_ms = g->last_kind_ms[0];
+    if (td_launches) *td_launches = g->last_kind_launches[0];
+    if (bu_ms) *bu_ms = g->last_kind_ms[1];
+    if (bu_launches) *bu_launches = g->last_kind_launches[1];
     return 0;
 }
 

@@ -1,11 +1,15 @@
 // gfx950 kernels for level-synchronous, frontier-based BFS over an int32 CSR
-// graph.  One launch initialises a search; then one launch of
-// bfs_level_kernel runs one level.  Every level launch reads the frontier
-// counters left in device memory by the previous launch, decides the
-// direction itself and exits at once after the search has ended, so the host
-// can enqueue launches ahead without learning anything per level (the per-level
-// launch plus device-to-host count copy of bfs.cu's runBfs, in "Day 38 - Graph
-// traversal on a GPU", is what this removes).
+// graph.  One launch initialises a search; then launches of two level kernels
+// alternate: bfs_td_kernel (even launch indexes) runs top-down levels and
+// bfs_bu_kernel (odd indexes) runs bottom-up levels.  Every launch reads the
+// level it stands at and the frontier counters left in device memory by the
+// previous launch, decides the direction itself, runs the level if the
+// direction is its own (else passes it on) and exits at once after the
+// search has ended, so the host can enqueue launches ahead without learning
+// anything per level (the per-level launch plus device-to-host count copy of
+// bfs.cu's runBfs, in "Day 38 - Graph traversal on a GPU", is what this
+// removes).  The two directions live in separate kernels so that each gets
+// its own register allocation.
 //
 // Per level, every workgroup computes the same decision from the counters:
 //   * top-down (push): expand every frontier vertex's adjacency list; a
@@ -18,8 +22,8 @@
 // The PMPP ch.15 notes (section 15.7) switch to pull when |F| * (m/n) > |U|.
 // Counting vertices misjudges power-law frontiers, whose few hubs carry most
 // of the edges, so the switch here counts edges, which the frontier counters
-// give exactly: pull when sum deg(F) > (edges of unvisited vertices) / ALPHA,
-// back to push when |F| < n / BETA and shrinking (Beamer, Asanovic and
+// give exactly: pull when sum deg(F) > (edges of unvisited vertices) / alpha,
+// back to push when |F| < n / beta and shrinking (Beamer, Asanovic and
 // Patterson, "Direction-Optimizing Breadth-First Search", SC 2012).
 //
 // Top-down advance (PMPP ch.15 notes, section 15.7 and Gunrock reading guide,
@@ -98,9 +102,15 @@ struct LevelShared {
             int32_t tstart[CAP], toff[CAP];   // flush: piece start / edge offset of each staged slot
         };
         struct {                          // bottom-up pass, per wavefront
-            int32_t bu_lst[WAVES][BU_GP * 64];     // unvisited vertices of the group
-            unsigned long long bu_fm[WAVES][BU_GP];  // found masks per word pair
-            unsigned long long bu_vis[WAVES][BU_GP]; // visited words per word pair
+            int32_t bu_lst[WAVES][BU_GSZ];   // listed unvisited vertices
+            int32_t bu_deg[WAVES][BU_GSZ];   // their degrees
+            int32_t bu_hit[WAVES][BU_GSZ];   // entry of the first hit, BU_NOHIT if none
+            int32_t bu_pi[WAVES][BU_GSZ];    // pending vertices: index into bu_lst,
+            int32_t bu_pn[WAVES][BU_GSZ];    //   next entry to probe,
+            int32_t bu_pe[WAVES][BU_GSZ];    //   end of the list,
+            int32_t bu_ps[WAVES][BU_GSZ];    //   exclusive scan of this round's probes
+            unsigned long long bu_fm[WAVES][WAVE];  // found masks of the 64 words in hand
+            uint32_t bu_cf[CF_WORDS];        // coarse frontier map (when use_cf)
         };
     };
     int32_t ntiles;
@@ -108,10 +118,10 @@ struct LevelShared {
     unsigned long long list_base[NLISTS];
     int32_t cnt;                      // staged count (may exceed CAP: overflow spilled)
     int32_t nbig;
-    int32_t fcnt;                     // from-bitmap list count
+    int32_t fl_cnt[WAVES], fl_more[WAVES];   // from-bitmap lists: count, words left
     // decision, identical in every workgroup
     int32_t mode;                     // 0 exit, 1 finish, 2 run
-    int32_t dir, input_bm, wbits, clear_bm, adv_eb, small;
+    int32_t dir, input_bm, wbits, wcf, clear_bm, adv_eb, small, use_cf, cf_clear;
     int32_t fsize;
     int64_t fdeg, reached_before, edges_before;
     int32_t lcount[NLISTS * STRIPES];  // segments per (list, stripe)
@@ -129,6 +139,8 @@ struct Ctx {
     int32_t nslot;          // slot of level k+1
     int32_t wbits;
     uint32_t *nbm;          // bitmap of level k+1 (top-down with wbits)
+    uint32_t *ncf;          // coarse map of level k+1 (top-down with wcf)
+    int32_t wcf;
     Seg *nq, *nt;           // queues of level k+1
     int32_t *nts;
     // per-thread tallies of new frontier vertices
@@ -251,6 +263,10 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
             P.dist[v[q]] = c.level + 1;
             if (P.parent) P.parent[v[q]] = u[q];
             if (c.wbits) atomicOr(c.nbm + (v[q] >> 5), 1u << (v[q] & 31));
+            if (c.wcf) {
+                const uint32_t cb = (uint32_t)v[q] >> P.cf_sh;
+                atomicOr(c.ncf + (cb >> 5), 1u << (cb & 31));
+            }
         }
     }
 #pragma unroll
@@ -516,170 +532,370 @@ __device__ __forceinline__ void td_edge_balanced(Ctx &c, const Seg *cq, const Se
 }
 
 // Top-down from a bitmap frontier (the level after a bottom-up level): each
-// workgroup scans its range of bitmap words, lists the frontier vertices in
-// LDS and expands them as segments.  Both frontier bitmaps are zeroed on the
-// way (this level writes no bitmap).
+// wavefront reads 64 of the workgroup's bitmap words at a time (one per lane),
+// lists the frontier vertices of its words in its own LDS region (up to
+// FL_WAVE; the words that do not fit wait for the next round), and the
+// workgroup expands the listed vertices as segments.  Both frontier bitmaps
+// are zeroed on the way (this level writes no bitmap).
+constexpr int FL_WAVE = FLIST_CAP / WAVES;
+
 __device__ __forceinline__ void td_from_bitmap(Ctx &c, uint32_t *cbm, uint32_t *obm) {
     const Params &P = *c.P;
     LevelShared &sh = *c.sh;
-    int32_t *flist = sh.work;
+    const int lane = lane_id();
+    const int wv = wave_id();
+    int32_t *flist = sh.work + wv * FL_WAVE;
+    uint64_t *cb64 = reinterpret_cast<uint64_t *>(cbm);
+    uint64_t *ob64 = reinterpret_cast<uint64_t *>(obm);
     const int per = (P.nwp + c.G - 1) / c.G;
-    const int start = c.wg * per;
+    const int start = min(P.nwp, c.wg * per);
     const int end = min(P.nwp, start + per);
-    constexpr int R = FLIST_CAP / BLOCK;   // word pairs per wave per round
-    for (int base = start; base < end; base += WAVES * R) {
-        for (int j = 0; j < R; ++j) {
-            const int wp = base + wave_id() * R + j;
-            if (wp < end) {
-                uint64_t *cw = reinterpret_cast<uint64_t *>(cbm) + wp;
-                const uint64_t word = *cw;
-                const bool in = (word >> lane_id()) & 1ull;
+    for (int base = start; base < end; base += WAVES * WAVE) {
+        const int w0 = base + wv * WAVE;
+        const int wp = w0 + lane;
+        uint64_t word = 0;
+        if (wp < end) {
+            word = cb64[wp];
+            cb64[wp] = 0ull;
+            ob64[wp] = 0ull;
+        }
+        uint64_t todo = __ballot(word != 0);
+        for (;;) {
+            // list the vertices of this wavefront's words, word by word, while they fit
+            int cnt = 0;
+            while (todo) {
+                const int j = __ffsll((unsigned long long)todo) - 1;
+                const uint32_t lo = (uint32_t)readlane_i((int)(uint32_t)word, j);
+                const uint32_t hi = (uint32_t)readlane_i((int)(uint32_t)(word >> 32), j);
+                const uint64_t wj = ((uint64_t)hi << 32) | lo;
+                const int bits = __popcll(wj);
+                if (cnt + bits > FL_WAVE) break;
+                const bool in = (wj >> lane) & 1ull;
                 const uint64_t m = __ballot(in);
-                if (m) {
-                    const int leader = __ffsll((unsigned long long)m) - 1;
-                    int b0 = 0;
-                    if (lane_id() == leader) b0 = atomicAdd(&sh.fcnt, __popcll(m));
-                    b0 = readlane_i(b0, leader);
-                    if (in) flist[b0 + mbcnt64(m)] = wp * 64 + lane_id();
-                }
-                if (lane_id() == 0) {
-                    *cw = 0ull;
-                    reinterpret_cast<uint64_t *>(obm)[wp] = 0ull;
-                }
+                if (in) flist[cnt + mbcnt64(m)] = (w0 + j) * 64 + lane;
+                cnt += bits;
+                todo &= todo - 1;
             }
-        }
-        __syncthreads();
-        const int nf = sh.fcnt;
-        for (int c0 = 0; c0 < nf; c0 += BLOCK) {
-            const int i = c0 + (int)threadIdx.x;
-            const bool has = i < nf && flist[i] < P.n;
-            int v = 0, beg = 0, len = 0;
-            if (has) {
-                v = flist[i];
-                beg = P.row_ptr[v];
-                len = P.row_ptr[v + 1] - beg;
+            if (lane == 0) { sh.fl_cnt[wv] = cnt; sh.fl_more[wv] = todo != 0; }
+            __syncthreads();
+            int maxc = 0, more = 0;
+            for (int w = 0; w < WAVES; ++w) { maxc = max(maxc, sh.fl_cnt[w]); more |= sh.fl_more[w]; }
+            // expand: pass p takes entry p*64 + lane of every wavefront's region
+            for (int p0 = 0; p0 < maxc; p0 += WAVE) {
+                const int i = p0 + lane;
+                const bool has = i < sh.fl_cnt[wv] && flist[i] < P.n;
+                int v = 0, beg = 0, len = 0;
+                if (has) {
+                    v = flist[i];
+                    beg = P.row_ptr[v];
+                    len = P.row_ptr[v + 1] - beg;
+                }
+                expand_segments(c, has && len > 0, v, beg, len);
+                maybe_flush(c);
             }
-            expand_segments(c, has && len > 0, v, beg, len);
-            maybe_flush(c);
+            __syncthreads();
+            if (!more) break;
         }
-        if (threadIdx.x == 0) sh.fcnt = 0;
-        __syncthreads();
     }
 }
 
 // -------------------------------------------------------- bottom-up --------
 
-// Every unvisited vertex looks for a parent in the frontier bitmap, in CSR
-// order; a wavefront owns 64 consecutive vertices, so __ballot(found) is the
-// next bitmap's 64-bit word and the visited word update needs no atomics.
+// Every unvisited vertex looks for a parent: its first neighbour, in CSR
+// order, that is in the frontier bitmap.  Each wavefront owns a contiguous
+// range of 64-vertex words and walks it 64 words at a time: it reads their
+// visited words (one per lane), skips the fully visited ones and lists the
+// unvisited vertices in LDS, BU_GSZ at a time.  Round 0 loads the aligned
+// 8-entry block that holds every listed vertex's first entry and probes the
+// first entry, then the rest of the block for the vertices still searching.  Each later
+// round gives every vertex still without a parent its next min(W, rest)
+// entries (W = 8, 32, 128, ... per round) and
+// lays those probes out densely, 64 per instruction whatever the mix of list
+// lengths: an exclusive scan of the counts and a binary search over it give
+// each lane its (vertex, entry).  The first hit in CSR order is kept by an LDS
+// atomicMin on the entry index.  When the frontier is a small share of the
+// vertices, a coarse copy of it (one bit per 2^cf_sh vertices, set by the
+// previous level's claims) sits in LDS and answers most probes without a
+// memory access.  A wavefront owns whole 64-vertex words, so the next
+// frontier's bitmap words and the visited words are plain stores: no global
+// atomics and no duplicates.
 __device__ __forceinline__ void wave_lds_sync() {
     // order this wavefront's LDS traffic between lanes (no workgroup barrier)
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
 }
 
+__device__ __forceinline__ int wave_incl_scan_i32(int x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) {
+        const int y = __shfl_up(x, (unsigned)d, WAVE);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+constexpr int BU_NOHIT = 0x7fffffff;
+
+// Can u be in the frontier?  (false only when its coarse bit is clear)
+__device__ __forceinline__ bool cf_maybe(const LevelShared &sh, int use_cf, int cf_sh, int u) {
+    if (!use_cf) return true;
+    const uint32_t b = (uint32_t)u >> cf_sh;
+    return (sh.bu_cf[b >> 5] >> (b & 31)) & 1u;
+}
+
+// Entries of the aligned 8-entry block of col_idx that holds entry e, as x[q]
+// = col_idx[blk + q]; entries outside [lo, hi) (or all, when !go) read as -1.
+__device__ __forceinline__ void load_block8(const Params &P, bool go, int e, int lo, int hi,
+                                            int (&x)[8]) {
+    const int blk = e & ~7;
+    if (go && P.col_vec && blk + 8 <= P.m) {
+        const int4 a = *reinterpret_cast<const int4 *>(P.col_idx + blk);
+        const int4 b = *reinterpret_cast<const int4 *>(P.col_idx + blk + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            x[q] = (go && blk + q >= lo && blk + q < hi) ? P.col_idx[blk + q] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        if (!(go && blk + q >= lo && blk + q < hi)) x[q] = -1;
+}
+
+// The first entry of x (in order) that is in the frontier, else -1.  All
+// probes are issued before any result is used.
+__device__ __forceinline__ int probe_first(const LevelShared &sh, const uint32_t *cbm, int use_cf,
+                                           int cf_sh, const int (&x)[8]) {
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        w[q] = (x[q] >= 0 && cf_maybe(sh, use_cf, cf_sh, x[q])) ? cbm[x[q] >> 5] : 0u;
+    int hit = -1;
+#pragma unroll
+    for (int q = 7; q >= 0; --q)
+        if (x[q] >= 0 && ((w[q] >> (x[q] & 31)) & 1u)) hit = x[q];
+    return hit;
+}
+
+// Records that listed vertex v found parent u.
+__device__ __forceinline__ void bu_found(Ctx &c, int wbase, int v, int u, int d) {
+    const Params &P = *c.P;
+    P.dist[v] = c.level + 1;
+    if (P.parent) P.parent[v] = u;
+    atomicOr(&c.sh->bu_fm[wave_id()][(v >> 6) - wbase], 1ull << (v & 63));
+    c.fcnt += 1;
+    c.fdeg += d;
+}
+
+// Searches parents for the listed vertices lst[0, cnt) of this wavefront
+// (all inside words [wbase, wbase + 64)).
+__device__ __forceinline__ void bu_list(Ctx &c, const uint32_t *cbm, int cnt, int wbase) {
+    const Params &P = *c.P;
+    LevelShared &sh = *c.sh;
+    const int lane = lane_id();
+    const int wv = wave_id();
+    const int use_cf = sh.use_cf, cf_sh = P.cf_sh;
+    int32_t *lst = sh.bu_lst[wv], *deg = sh.bu_deg[wv], *hit = sh.bu_hit[wv];
+    int32_t *pi = sh.bu_pi[wv], *pn = sh.bu_pn[wv], *pe = sh.bu_pe[wv], *ps = sh.bu_ps[wv];
+    constexpr int R0 = BU_GSZ / WAVE;   // listed vertices per lane in round 0
+    // round 0: the aligned 8-entry block holding the first entry of every
+    // listed vertex (two 16-byte loads); R0 vertices per lane with their loads
+    // overlapped; a hit is recorded at once
+    int npend = 0;
+    {
+        int v[R0], beg[R0], en[R0];
+        int x[R0][8];
+#pragma unroll
+        for (int j = 0; j < R0; ++j) {
+            const int i = j * WAVE + lane;
+            v[j] = (i < cnt) ? lst[i] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < R0; ++j) {
+            beg[j] = (v[j] >= 0) ? P.row_ptr[v[j]] : 0;
+            en[j] = (v[j] >= 0) ? P.row_ptr[v[j] + 1] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < R0; ++j) load_block8(P, beg[j] < en[j], beg[j], beg[j], en[j], x[j]);
+        // the first entry alone (most vertices of a wide level stop there) ...
+        int par[R0];
+        {
+            int f[R0];
+            uint32_t w[R0];
+#pragma unroll
+            for (int j = 0; j < R0; ++j) {
+                f[j] = -1;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if ((beg[j] & 7) == q) f[j] = x[j][q];
+                w[j] = (f[j] >= 0 && cf_maybe(sh, use_cf, cf_sh, f[j])) ? cbm[f[j] >> 5] : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < R0; ++j) par[j] = (f[j] >= 0 && ((w[j] >> (f[j] & 31)) & 1u)) ? f[j] : -1;
+        }
+        // ... then the rest of the block for the vertices still searching
+        bool more = false;
+#pragma unroll
+        for (int j = 0; j < R0; ++j) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (par[j] >= 0 || q <= (beg[j] & 7)) x[j][q] = -1;
+            more |= par[j] < 0 && beg[j] + 1 < min((beg[j] | 7) + 1, en[j]);
+        }
+        if (__ballot(more)) {
+#pragma unroll
+            for (int j = 0; j < R0; ++j)
+                if (par[j] < 0) par[j] = probe_first(sh, cbm, use_cf, cf_sh, x[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < R0; ++j) {
+            const int i = j * WAVE + lane;
+            const bool found = par[j] >= 0;
+            if (found) bu_found(c, wbase, v[j], par[j], en[j] - beg[j]);
+            if (v[j] >= 0) {
+                hit[i] = BU_NOHIT;
+                deg[i] = en[j] - beg[j];
+            }
+            const int nx = (beg[j] | 7) + 1;   // first entry after the block
+            const bool keep = v[j] >= 0 && !found && nx < en[j];
+            const uint64_t m = __ballot(keep);
+            if (keep) {
+                const int p = npend + mbcnt64(m);
+                pi[p] = i; pn[p] = nx; pe[p] = en[j];
+            }
+            npend += __popcll(m);
+        }
+    }
+    if (npend == 0) return;
+    // later rounds, dense
+    for (int W = BU_W1; npend > 0; W = min(4 * W, BU_WMAX)) {
+        wave_lds_sync();
+        int T = 0;
+        for (int b = 0; b < npend; b += WAVE) {
+            const int i = b + lane;
+            const int cc = (i < npend) ? min(pe[i] - pn[i], W) : 0;
+            const int incl = wave_incl_scan_i32(cc);
+            if (i < npend) ps[i] = T + incl - cc;
+            T += readlane_i(incl, WAVE - 1);
+        }
+        wave_lds_sync();
+        for (int t0 = 0; t0 < T; t0 += BU_U * WAVE) {
+            int e[BU_U], own[BU_U], u[BU_U];
+            uint32_t w[BU_U];
+#pragma unroll
+            for (int q = 0; q < BU_U; ++q) {
+                const int slot = t0 + q * WAVE + lane;
+                e[q] = -1;
+                own[q] = 0;
+                if (slot < T) {
+                    // the pending vertex owning this slot: last p with ps[p] <= slot
+                    // (every pending vertex has at least one entry left, so ps rises)
+                    int lo = 0, hi = npend;
+                    while (hi - lo > 1) {
+                        const int mid = (lo + hi) >> 1;
+                        if (ps[mid] <= slot) lo = mid; else hi = mid;
+                    }
+                    e[q] = pn[lo] + (slot - ps[lo]);
+                    own[q] = pi[lo];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < BU_U; ++q) u[q] = (e[q] >= 0) ? P.col_idx[e[q]] : -1;
+#pragma unroll
+            for (int q = 0; q < BU_U; ++q)
+                w[q] = (u[q] >= 0 && cf_maybe(sh, use_cf, cf_sh, u[q])) ? cbm[u[q] >> 5] : 0u;
+#pragma unroll
+            for (int q = 0; q < BU_U; ++q)
+                if (u[q] >= 0 && ((w[q] >> (u[q] & 31)) & 1u)) atomicMin(&hit[own[q]], e[q]);
+        }
+        wave_lds_sync();
+        // keep the vertices without a hit whose lists go on (in place: a
+        // chunk reads its entries before writing at or below them)
+        int nn = 0;
+        for (int b = 0; b < npend; b += WAVE) {
+            const int i = b + lane;
+            bool keep = false;
+            int a = 0, nx = 0, ee = 0;
+            if (i < npend) {
+                a = pi[i];
+                ee = pe[i];
+                nx = pn[i] + min(ee - pn[i], W);
+                keep = hit[a] == BU_NOHIT && nx < ee;
+            }
+            const uint64_t m = __ballot(keep);
+            if (keep) {
+                const int p = nn + mbcnt64(m);
+                pi[p] = a; pn[p] = nx; pe[p] = ee;
+            }
+            nn += __popcll(m);
+        }
+        npend = nn;
+    }
+    wave_lds_sync();
+    // the vertices found in the later rounds: the neighbour at the first hit
+#pragma unroll
+    for (int j = 0; j < R0; ++j) {
+        const int i = j * WAVE + lane;
+        const int h = (i < cnt) ? hit[i] : BU_NOHIT;
+        if (h != BU_NOHIT) bu_found(c, wbase, lst[i], P.col_idx[h], deg[i]);
+    }
+}
+
 __device__ __forceinline__ void bottom_up(Ctx &c, const uint32_t *cbm, uint32_t *nbm) {
     const Params &P = *c.P;
     LevelShared &sh = *c.sh;
-    const int per = (P.nwp + c.G - 1) / c.G;
-    const int start = c.wg * per;
-    const int end = min(P.nwp, start + per);
     const int lane = lane_id();
     const int wv = wave_id();
+    if (sh.use_cf) {
+        // the coarse frontier map, into LDS
+        const uint32_t *cf = P.cf + (size_t)(c.level % 3) * CF_WORDS;
+        for (int i = threadIdx.x; i < P.cf_words; i += BLOCK) sh.bu_cf[i] = cf[i];
+        __syncthreads();
+    }
+    // this workgroup's words, then this wavefront's share of them
+    const int per = (P.nwp + c.G - 1) / c.G;
+    const int start = min(P.nwp, c.wg * per);
+    const int end = min(P.nwp, start + per);
+    const int wper = (end - start + WAVES - 1) / WAVES;
+    const int ws = min(end, start + wv * wper);
+    const int we = min(end, ws + wper);
     uint64_t *vis64 = reinterpret_cast<uint64_t *>(P.visited);
     uint64_t *nbm64 = reinterpret_cast<uint64_t *>(nbm);
     int32_t *lst = sh.bu_lst[wv];
-    // a wavefront takes BU_GP word pairs (BU_GP*64 vertices) at a time,
-    // gathers their unvisited vertices into a dense LDS list, and scans them
-    // 64 at a time: every lane has a vertex whatever share is visited
-    for (int g0 = start + wv * BU_GP; g0 < end; g0 += WAVES * BU_GP) {
-        const int ng = min(BU_GP, end - g0);
+    for (int cw = ws; cw < we; cw += WAVE) {
+        const int nw = min(WAVE, we - cw);
+        const uint64_t myvis = (lane < nw) ? vis64[cw + lane] : ~0ull;
+        sh.bu_fm[wv][lane] = 0ull;
+        const uint64_t todo = __ballot(myvis != ~0ull);   // words with unvisited vertices
         int cnt = 0;
-        for (int j = 0; j < ng; ++j) {
-            const uint64_t vis = vis64[g0 + j];
-            const bool act = !((vis >> lane) & 1ull);   // padding bits are set
+        for (uint64_t tm = todo; tm; tm &= tm - 1) {
+            const int j = __ffsll((unsigned long long)tm) - 1;
+            const uint32_t lo = (uint32_t)readlane_i((int)(uint32_t)myvis, j);
+            const uint32_t hi = (uint32_t)readlane_i((int)(uint32_t)(myvis >> 32), j);
+            const uint64_t vis = ((uint64_t)hi << 32) | lo;
+            const bool act = !((vis >> lane) & 1ull);      // padding bits are set
             const uint64_t m = __ballot(act);
-            if (act) lst[cnt + mbcnt64(m)] = (g0 + j) * 64 + lane;
-            if (lane == 0) { sh.bu_vis[wv][j] = vis; sh.bu_fm[wv][j] = 0ull; }
+            if (cnt + __popcll(m) > BU_GSZ) {
+                wave_lds_sync();
+                bu_list(c, cbm, cnt, cw);
+                wave_lds_sync();
+                cnt = 0;
+            }
+            if (act) lst[cnt + mbcnt64(m)] = (cw + j) * 64 + lane;
             cnt += __popcll(m);
         }
-        wave_lds_sync();
-        for (int b0 = 0; b0 < cnt; b0 += WAVE) {
-            const bool act = b0 + lane < cnt;
-            const int v = act ? lst[b0 + lane] : 0;
-            const int beg = act ? P.row_ptr[v] : 0;
-            const int eend = act ? P.row_ptr[v + 1] : 0;
-            const int lim = min(eend, beg + BU_LANE_SCAN);
-            int e = beg, par = -1;
-            bool fnd = false;
-            // lane scan: each step covers the aligned 8-entry block holding
-            // the scan position, fetched as two 16-byte loads, then probes the
-            // block's entries inside [e, lim); the first hit in CSR order wins
-            for (int step = 0; step <= BU_LANE_SCAN / 8; ++step) {
-                const bool go = act && e < lim;
-                if (!__ballot(go)) break;
-                const int blk = e & ~7;
-                int x[8];
-                if (go && P.col_vec && blk + 8 <= P.m) {
-                    const int4 a = *reinterpret_cast<const int4 *>(P.col_idx + blk);
-                    const int4 b = *reinterpret_cast<const int4 *>(P.col_idx + blk + 4);
-                    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-                    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        x[q] = (go && blk + q >= e && blk + q < lim) ? P.col_idx[blk + q] : -1;
-                }
-                uint32_t w[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    if (!(go && blk + q >= e && blk + q < lim)) x[q] = -1;
-                    w[q] = (x[q] >= 0) ? cbm[x[q] >> 5] : 0u;
-                }
-#pragma unroll
-                for (int q = 7; q >= 0; --q)
-                    if (x[q] >= 0 && ((w[q] >> (x[q] & 31)) & 1u)) { fnd = true; par = x[q]; }
-                if (go) e = fnd ? lim : min(blk + 8, lim);
-            }
-            if (!fnd) e = lim;
-            // long lists: the whole wavefront scans 64 entries at a time; the
-            // first hit in CSR order is the lowest set lane of the first chunk
-            uint64_t pm = __ballot(act && !fnd && e < eend);
-            while (pm) {
-                const int src = __ffsll((unsigned long long)pm) - 1;
-                pm &= pm - 1;
-                const int sb = readlane_i(e, src), se = readlane_i(eend, src);
-                for (int c0 = sb; c0 < se; c0 += WAVE) {
-                    const int ee = c0 + lane;
-                    int u = 0;
-                    bool hit = false;
-                    if (ee < se) {
-                        u = P.col_idx[ee];
-                        hit = (cbm[u >> 5] >> (u & 31)) & 1u;
-                    }
-                    const uint64_t hm = __ballot(hit);
-                    if (hm) {
-                        const int first = __ffsll((unsigned long long)hm) - 1;
-                        const int pu = readlane_i(u, first);
-                        if (lane == src) { fnd = true; par = pu; }
-                        break;
-                    }
-                }
-            }
-            if (fnd) {
-                P.dist[v] = c.level + 1;
-                if (P.parent) P.parent[v] = par;
-                atomicOr(&sh.bu_fm[wv][(v >> 6) - g0], 1ull << (v & 63));
-                c.fcnt += 1;
-                c.fdeg += eend - beg;
-            }
+        if (cnt > 0) {
+            wave_lds_sync();
+            bu_list(c, cbm, cnt, cw);
         }
         wave_lds_sync();
-        // the group's next-bitmap words (every word written) and visited words
-        if (lane < ng) {
+        // the next-bitmap words (every word written) and visited words
+        if (lane < nw) {
             const uint64_t fm = sh.bu_fm[wv][lane];
-            nbm64[g0 + lane] = fm;
-            if (fm) vis64[g0 + lane] = sh.bu_vis[wv][lane] | fm;
+            nbm64[cw + lane] = fm;
+            if (fm) vis64[cw + lane] = myvis | fm;
         }
         wave_lds_sync();
     }
@@ -699,6 +915,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
     const uint64_t *init64 = reinterpret_cast<const uint64_t *>(P.vis_init);
     uint64_t *b0 = reinterpret_cast<uint64_t *>(P.fbm0);
     uint64_t *b1 = reinterpret_cast<uint64_t *>(P.fbm1);
+    for (int i = tid; i < 3 * CF_WORDS; i += nth) P.cf[i] = 0u;
     for (int wp = tid; wp < P.nwp; wp += nth) {
         const uint64_t sbit = (wp == (s >> 6)) ? (1ull << (s & 63)) : 0ull;
         vis64[wp] = init64[wp] | sbit;
@@ -714,7 +931,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
             P.ctl->lvl[0] = 0; P.ctl->lvl[1] = 0;
             P.ctl->bar_count = 0; P.ctl->bar_gen = 0;
             for (int k = 0; k < NSLOTS; ++k) {
-                P.ctl->slot[k].dir = 0; P.ctl->slot[k].wbits = 0;
+                P.ctl->slot[k].dir = 0; P.ctl->slot[k].wbits = 0; P.ctl->slot[k].wcf = 0;
                 P.ctl->slot[k].input_bm = 0; P.ctl->slot[k].fsize = 0;
                 P.ctl->slot[k].reached_before = 0; P.ctl->slot[k].edges_before = 0;
             }
@@ -723,7 +940,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
         if (threadIdx.x == 0) {
             Ctx c;
             c.P = &P; c.sh = nullptr; c.level = -1; c.wg = 0; c.G = 1; c.stripe = 0; c.nslot = 0; c.wbits = 0;
-            c.nbm = nullptr; c.nq = P.q0; c.nt = P.t0; c.nts = P.ts0; c.fcnt = 0; c.fdeg = 0;
+            c.nbm = nullptr; c.ncf = nullptr; c.wcf = 0; c.nq = P.q0; c.nt = P.t0; c.nts = P.ts0; c.fcnt = 0; c.fdeg = 0;
             const int beg = P.row_ptr[s];
             const int len = P.row_ptr[s + 1] - beg;
             const int l = list_of(len);
@@ -755,9 +972,13 @@ __device__ __forceinline__ void decide(const Params &P, LevelShared &sh, int k) 
         sh.ledges[lane] = (int32_t)(cv & 0xffffffffull);
     }
     if (lane == 0) {
-        sh.cnt = 0; sh.nbig = 0; sh.fcnt = 0;
+        sh.cnt = 0; sh.nbig = 0;
         sh.fsize = (int32_t)fsize; sh.fdeg = fdeg;
         sh.small = 0;
+        sh.use_cf = 0;
+        // the coarse map of level k+2 was written by level k-2 if it set wcf
+        // (the slot ring still holds level k-2's record at level k)
+        sh.cf_clear = (k >= 2) ? P.ctl->slot[(k + NSLOTS - 2) % NSLOTS].wcf : 0;
         if (done || P.ctl->err) {
             sh.mode = 0;
         } else if (fsize == 0) {
@@ -777,9 +998,9 @@ __device__ __forceinline__ void decide(const Params &P, LevelShared &sh, int k) 
             } else if (k == 0 || prev.dir == DIR_TD) {
                 // edges still to be explored from unvisited vertices
                 const int64_t m_u = (int64_t)P.m - edges_before - fdeg;
-                want_pull = fdeg * ALPHA > m_u;
+                want_pull = fdeg * P.alpha > m_u;
             } else {
-                want_pull = !(fsize * BETA < (int64_t)P.n && fsize < prev.fsize);
+                want_pull = !(fsize * P.beta < (int64_t)P.n && fsize < prev.fsize);
             }
             const int dir = (want_pull && P.symmetric && has_bm) ? DIR_BU : DIR_TD;
             sh.dir = dir;
@@ -788,13 +1009,26 @@ __device__ __forceinline__ void decide(const Params &P, LevelShared &sh, int k) 
             sh.input_bm = (dir == DIR_TD) && !has_queue;
             sh.clear_bm = (dir == DIR_TD) && has_queue && has_bm;
             // a top-down level from a queue also sets its new vertices in the
-            // next bitmap whenever the next level may pull
-            sh.wbits = (dir == DIR_TD) && has_queue && P.symmetric && P.pol_dir == BFS_DIR_AUTO;
+            // next bitmap whenever the next level may pull.  The next level
+            // pulls when alpha*deg(F') > m - (edges reached so far) - deg(F'),
+            // and deg(F') <= max_deg*|F'| <= max_deg*deg(F), so levels for
+            // which even that bound cannot tip the rule skip the bit writes.
+            const int64_t m_left = (int64_t)P.m - edges_before - fdeg;
+            const bool may_pull = (double)P.max_deg * (double)fdeg * (double)(P.alpha + 1) > (double)m_left;
+            sh.wbits = (dir == DIR_TD) && has_queue && P.symmetric && P.pol_dir == BFS_DIR_AUTO && may_pull;
             // edge-balanced unless the binned advance is forced: its tiles
             // spread even a small frontier over several workgroups and
             // bound the winners between flushes
             sh.adv_eb = (dir == DIR_TD) && has_queue && P.pol_adv != BFS_ADV_BINNED;
             sh.small = P.small_mode && (dir == DIR_TD) && has_queue && fsize <= SMALL_F && fdeg <= SMALL_E;
+            // the coarse frontier map exists when the previous level set it (a
+            // top-down level with wcf); it filters well while the frontier
+            // covers under about two vertices per coarse bit
+            sh.use_cf = (dir == DIR_BU) && k > 0 && prev.dir == DIR_TD && prev.wcf &&
+                        (fsize << P.cf_sh) <= 2 * (int64_t)P.n;
+            // a top-down level sets the next coarse map only when its edges (a
+            // bound on the next frontier) are few enough for the map to filter
+            sh.wcf = sh.wbits && (fdeg << P.cf_sh) <= 2 * (int64_t)P.n;
         }
     }
 }
@@ -828,7 +1062,9 @@ __device__ __forceinline__ void small_barrier(const Params &P, int G) {
     __syncthreads();
 }
 
-// One level on the G workgroups taking part (this one is number wg).
+// One level on the G workgroups taking part (this one is number wg); BU
+// selects the direction's code (the decision in sh must agree).
+template <bool BU>
 __device__ __forceinline__ void run_level(const Params &P, LevelShared &sh, int k, int wg, int G) {
     const int lane = lane_id();
     const int slot = k % NSLOTS;
@@ -854,6 +1090,7 @@ __device__ __forceinline__ void run_level(const Params &P, LevelShared &sh, int 
             if (k < P.st_cap) { P.st_dir[k] = (int8_t)sh.dir; P.st_fdeg[k] = sh.fdeg; }
             P.ctl->slot[slot].dir = sh.dir;
             P.ctl->slot[slot].wbits = sh.wbits;
+            P.ctl->slot[slot].wcf = sh.wcf;
             P.ctl->slot[slot].input_bm = sh.input_bm;
             P.ctl->slot[slot].fsize = sh.fsize;
             P.ctl->slot[(k + 1) % NSLOTS].reached_before = sh.reached_before + sh.fsize;
@@ -872,10 +1109,19 @@ __device__ __forceinline__ void run_level(const Params &P, LevelShared &sh, int 
     c.stripe = wg % STRIPES;
     c.nslot = (k + 1) % NSLOTS;
     c.wbits = sh.wbits;
+    c.wcf = sh.wcf;
     const int cur = k & 1;
     uint32_t *cbm = cur ? P.fbm1 : P.fbm0;
     uint32_t *obm = cur ? P.fbm0 : P.fbm1;
     c.nbm = obm;
+    c.ncf = P.cf + (size_t)((k + 1) % 3) * CF_WORDS;
+    if (sh.cf_clear) {
+        // clear the coarse map of level k+2: level k-2 wrote it (when its
+        // wcf was set), level k-1 was its last reader and level k+1 is its
+        // first writer
+        uint32_t *z = P.cf + (size_t)((k + 2) % 3) * CF_WORDS;
+        for (int i = wg * BLOCK + (int)threadIdx.x; i < P.cf_words; i += G * BLOCK) z[i] = 0u;
+    }
     c.nq = cur ? P.q0 : P.q1;
     c.nt = cur ? P.t0 : P.t1;
     c.nts = cur ? P.ts0 : P.ts1;
@@ -885,16 +1131,12 @@ __device__ __forceinline__ void run_level(const Params &P, LevelShared &sh, int 
     const Seg *ct = cur ? P.t1 : P.t0;
     const int32_t *cts = cur ? P.ts1 : P.ts0;
 
-    if (sh.dir == DIR_BU) {
+    if constexpr (BU) {
         bottom_up(c, cbm, obm);
-    } else if (sh.input_bm) {
-        td_from_bitmap(c, cbm, obm);
-        if (sh.cnt > 0) flush(c);
-    } else if (sh.adv_eb) {
-        td_edge_balanced(c, cq, ct, cts, cbm);
-        if (sh.cnt > 0) flush(c);
     } else {
-        td_binned(c, cq, ct, cbm);
+        if (sh.input_bm) td_from_bitmap(c, cbm, obm);
+        else if (sh.adv_eb) td_edge_balanced(c, cq, ct, cts, cbm);
+        else td_binned(c, cq, ct, cbm);
         if (sh.cnt > 0) flush(c);
     }
 
@@ -911,37 +1153,71 @@ __device__ __forceinline__ void run_level(const Params &P, LevelShared &sh, int 
     }
 }
 
-// One launch: runs the level lvl[launch & 1] on the whole grid, or, when that
-// level is small, runs levels on the first SMALL_G workgroups until one is
-// not small; then records where the next launch starts.
-__global__ __launch_bounds__(BLOCK, 4) void bfs_level_kernel(Params P, int32_t launch) {
-    __shared__ LevelShared sh;
-    int k = P.ctl->lvl[launch & 1];
+// Common start of a level launch: the level it stands at and the decision
+// for it.  Returns that level, or -1 when the launch has nothing to do (the
+// search is over, an error was recorded, or it has just found the empty
+// frontier and recorded the end).
+__device__ __forceinline__ int level_launch_start(const Params &P, LevelShared &sh, int launch) {
+    const int k = P.ctl->lvl[launch & 1];
     if (threadIdx.x < WAVE) decide(P, sh, k);
     __syncthreads();
-    if (sh.mode == 0) return;
+    if (sh.mode == 0) return -1;
     if (sh.mode == 1) {
         if (blockIdx.x == 0 && threadIdx.x == 0) { P.ctl->L = k; P.ctl->done = 1; }
-        return;
+        return -1;
     }
-    const bool small = sh.small;
-    if (small && blockIdx.x >= SMALL_G) return;
-    const int G = small ? min((int)gridDim.x, SMALL_G) : (int)gridDim.x;
+    return k;
+}
+
+__device__ __forceinline__ void set_next_level(const Params &P, int launch, int k) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) P.ctl->lvl[(launch + 1) & 1] = k;
+}
+
+// Top-down launch: runs the level it stands at on the whole grid when that
+// level is top-down, or, when the level is small, runs levels on the first
+// SMALL_G workgroups until one is not small (or is bottom-up); a bottom-up
+// level is passed on to the next launch.  One decision point serves every
+// level of the launch.
+__global__ __launch_bounds__(BLOCK, 4) void bfs_td_kernel(Params P, int32_t launch) {
+    __shared__ LevelShared sh;
+    int k = P.ctl->lvl[launch & 1];
+    int G = 0;   // 0 until the first level is decided
     for (;;) {
-        run_level(P, sh, k, blockIdx.x, G);
-        ++k;
-        if (!small) break;
-        small_barrier(P, G);
         if (threadIdx.x < WAVE) decide(P, sh, k);
         __syncthreads();
-        if (sh.mode == 0) return;    // an error was recorded
+        if (sh.mode == 0) return;    // over, or an error was recorded
         if (sh.mode == 1) {
             if (blockIdx.x == 0 && threadIdx.x == 0) { P.ctl->L = k; P.ctl->done = 1; }
             return;
         }
-        if (!sh.small) break;
+        if (G == 0) {
+            if (sh.dir == DIR_BU) break;   // for the bottom-up launch
+            if (sh.small && blockIdx.x >= SMALL_G) return;
+            G = sh.small ? min((int)gridDim.x, SMALL_G) : (int)gridDim.x;
+        } else if (!sh.small) {
+            break;                         // not small, or bottom-up
+        }
+        const bool small = sh.small;
+        run_level<false>(P, sh, k, blockIdx.x, G);
+        ++k;
+        if (!small) break;
+        small_barrier(P, G);
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) P.ctl->lvl[(launch + 1) & 1] = k;
+    set_next_level(P, launch, k);
+}
+
+// Bottom-up launch: runs the level it stands at when that level is
+// bottom-up, else passes it on.
+__global__ __launch_bounds__(BLOCK, 4) void bfs_bu_kernel(Params P, int32_t launch) {
+    __shared__ LevelShared sh;
+    const int k = level_launch_start(P, sh, launch);
+    if (k < 0) return;
+    if (sh.dir != DIR_BU) {
+        set_next_level(P, launch, k);
+        return;
+    }
+    run_level<true>(P, sh, k, blockIdx.x, (int)gridDim.x);
+    set_next_level(P, launch, k + 1);
 }
 
 // ------------------------------------------------- graph validation --------
@@ -1028,15 +1304,21 @@ hipError_t launch_init(const Params &P, int grid, hipStream_t s) {
 }
 
 hipError_t launch_level(const Params &P, int32_t launch_index, int grid, hipStream_t s) {
-    hipLaunchKernelGGL(bfs_level_kernel, dim3(grid), dim3(BLOCK), 0, s, P, launch_index);
+    if (launch_index & 1)
+        hipLaunchKernelGGL(bfs_bu_kernel, dim3(grid), dim3(BLOCK), 0, s, P, launch_index);
+    else
+        hipLaunchKernelGGL(bfs_td_kernel, dim3(grid), dim3(BLOCK), 0, s, P, launch_index);
     return hipGetLastError();
 }
 
 int level_kernel_blocks_per_cu() {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void *)bfs_level_kernel, BLOCK, 0) !=
-        hipSuccess)
+    int a = 0, b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, (const void *)bfs_td_kernel, BLOCK, 0) !=
+            hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, (const void *)bfs_bu_kernel, BLOCK, 0) !=
+            hipSuccess)
         return 1;
+    const int nb = a < b ? a : b;
     return nb > 0 ? nb : 1;
 }
 

@@ -20,12 +20,16 @@ constexpr int CAP = 2048;                // LDS staging capacity for new frontie
 constexpr int STEP_CLAIMS = CAP / 2;     // claims between flush checks: a flush starts at
                                          // CAP / 2 staged, so a step never overfills
 constexpr int EB_TE = 1024;              // edges per tile of the edge-balanced advance
-constexpr int BU_LANE_SCAN = 32;         // bottom-up: entries a lane scans alone before
-                                         // its list is handed to the whole wavefront
-constexpr int BU_GP = 8;                 // bottom-up: word pairs a wavefront gathers at a time
+constexpr int BU_GSZ = 128;              // bottom-up: vertices a wavefront lists at a time
+constexpr int BU_W1 = 8;                 // bottom-up: entries per vertex in the round after
+                                         // the first (x4 per round after that)
+constexpr int BU_WMAX = 8192;            // bottom-up: cap of the per-round entries per vertex
+constexpr int BU_U = 4;                  // bottom-up: probes a lane keeps in flight per step
+constexpr int CF_WORDS = 8192;           // coarse frontier map: at most 8192 words (32 KB)
 // direction switching (edge-based, as in Beamer et al. SC'12): go bottom-up
-// when the frontier's edges exceed 1/ALPHA of the unexplored vertices' edges;
-// come back top-down when the frontier is under n/BETA and shrinking
+// when the frontier's edges exceed 1/alpha of the unexplored vertices' edges;
+// come back top-down when the frontier is under n/beta and shrinking.  These
+// are the defaults; bfs_set_switch changes them per handle.
 constexpr int ALPHA = 14;
 constexpr int BETA = 24;
 
@@ -59,6 +63,7 @@ struct SlotInfo {
     int32_t wbits;        // this level's new vertices were also set in the next bitmap
     int32_t input_bm;     // this level's frontier came as a bitmap only
     int32_t fsize;        // this level's frontier size
+    int32_t wcf;          // this level's new vertices were also set in the next coarse map
     int64_t reached_before;  // vertices in levels < this one
     int64_t edges_before;    // sum of degrees of the vertices in levels < this one
 };
@@ -117,6 +122,12 @@ struct Params {
     int32_t pol_dir;          // BFS_DIR_*
     int32_t pol_adv;          // BFS_ADV_*
     int32_t small_mode;       // allow the small-frontier mode
+    int32_t alpha, beta;      // direction-switch parameters
+    int32_t max_deg;          // largest degree of the graph
+    uint32_t *cf;             // 3 coarse frontier maps of CF_WORDS words: bit b of map j
+                              // says some vertex in [b << cf_sh, (b+1) << cf_sh) joined the
+                              // frontier of a level l with l % 3 == j
+    int32_t cf_sh, cf_words;  // vertices per coarse bit (log2); words in use per map
     uint32_t barrier_ticks;   // small-mode barrier wait limit (100 MHz ticks)
 };
 

@@ -97,15 +97,18 @@ const char *bfs_last_error(void);
 #define BFS_ADV_BINNED 1
 #define BFS_ADV_EDGE   2
 
-/* Level loop.
- *   DEVICE (default): launches are enqueued ahead in growing batches, read the
- *     level to run and the frontier from device memory, and the host waits once
- *     per batch; a small top-down level (up to 16,384 vertices and 65,536
- *     edges) runs on 32 workgroups that carry on level after level with a
- *     barrier among themselves, so a long thin search is a handful of launches.
- *   HOST: one level per launch and the host waits for every level before the
- *     next launch, as bfs.cu's runBfs in the Day 38 program does.
- *   CHAIN: as DEVICE but one level per launch (no small-frontier mode).
+/* Level loop.  Level launches alternate between a top-down kernel and a
+ * bottom-up kernel; each reads the level to run and the frontier from device
+ * memory, runs that level if its direction is the kernel's own and otherwise
+ * leaves it to the next launch.
+ *   DEVICE (default): launches are enqueued ahead in growing batches and the
+ *     host waits once per batch; a small top-down level (up to 16,384
+ *     vertices and 65,536 edges) runs on 32 workgroups that carry on level
+ *     after level with a barrier among themselves, so a long thin search is a
+ *     handful of launches.
+ *   HOST: the host waits for every launch before the next one, as bfs.cu's
+ *     runBfs in the Day 38 program waits for every level.
+ *   CHAIN: as DEVICE but at most one level per launch (no small-frontier mode).
  * The small-frontier barrier's wait is bounded (2 s; the environment variable
  * FBFS_BARRIER_TIMEOUT_US, read at bfs_graph_create, overrides it for tests):
  * past it bfs_run returns BFS_EDEVICE instead of waiting forever. */
@@ -120,6 +123,19 @@ const char *bfs_last_error(void);
  * symmetric).
  */
 int32_t bfs_set_policy(bfs_graph *g, int32_t direction, int32_t advance, int32_t loop);
+
+/*
+ * Direction-switch parameters of the automatic policy, for later bfs_run calls
+ * on this handle (defaults 14 and 24, the constants of Beamer, Asanovic and
+ * Patterson, SC 2012).  After a top-down level, the next level pulls when
+ * alpha * (sum of degrees of the frontier) exceeds the degree sum of the
+ * vertices not yet reached; after a bottom-up level, it pushes again when
+ * beta * |frontier| < n and the frontier shrank.  The PMPP chapter 15 notes
+ * (section 15.7) state the vertex-count form of this rule.  dist, L and the
+ * level sizes do not depend on them.  Returns 0, or BFS_EINVAL when the handle
+ * is NULL or either value is outside [1, 1e6].
+ */
+int32_t bfs_set_switch(bfs_graph *g, int32_t alpha, int32_t beta);
 
 /*
  * Per-level record of the last bfs_run on this handle, for the byte model and
@@ -140,14 +156,24 @@ int32_t bfs_set_timing(bfs_graph *g, int32_t on);
 
 /*
  * Milliseconds of the last timed bfs_run (host memory, any may be NULL):
- * init_ms = the initialisation launch; level_ms = the level launches, summed
- * over batches (host waits between batches excluded); level_launches = level
+ * init_ms = the initialisation launch; level_ms = the level launches, each
+ * timed alone (host waits between batches excluded); level_launches = level
  * launches issued (including the one that found the empty frontier and any
  * that exited at once after it).  Returns 0, or BFS_EINVAL if the last run was
  * not timed.
  */
 int32_t bfs_last_run_timing(const bfs_graph *g, float *init_ms, float *level_ms,
                             int32_t *level_launches);
+
+/*
+ * The level launches of the last timed bfs_run split by kernel (host memory,
+ * any may be NULL): milliseconds and launches of the top-down kernel and of
+ * the bottom-up kernel, each launch timed by HIP events recorded just before
+ * and just after it on the run's stream.  The two sums make up level_ms of
+ * bfs_last_run_timing.  Returns 0, or BFS_EINVAL if the last run was not timed.
+ */
+int32_t bfs_last_run_kernel_timing(const bfs_graph *g, float *td_ms, int32_t *td_launches,
+                                   float *bu_ms, int32_t *bu_launches);
 
 /*
  * Graph facts found by bfs_graph_create (host memory, any may be NULL):

@@ -86,6 +86,48 @@ def test_c5_workload_sampled():
     check_graph(g, sources=g.sources[2:3], policies=["push_binned", "pull"])
 
 
+@pytest.mark.parametrize("alpha,beta", [(1, 1), (1, 10**6), (10**6, 1), (10**6, 10**6), (4, 64)])
+def test_switch_parameters(alpha, beta):
+    """The automatic policy under extreme direction-switch parameters: results
+    never change; a huge alpha pulls from the second level on."""
+    import frontier_bfs_csr_amd as fb
+    for g in (gg.rmat(14, 16, seed=21, nsrc=3), gg.c1_chung_lu()):
+        rp, ci = to_dev(g)
+        with fb.BfsGraph(rp, ci) as bg:
+            bg.set_switch(alpha, beta)
+            for s in g.sources[:3]:
+                s = int(s)
+                print(f"[gpu] switch {alpha},{beta} {g.name} source={s}", flush=True)
+                L, dist, parent, sizes = run_hip(bg, g.n, s)
+                ref = oracle.bfs(g.row_ptr, g.col_idx, s)
+                oracle.assert_bfs_ok(g.row_ptr, g.col_idx, s, ref, dist, parent, L, sizes[:L],
+                                     symmetric=True, label=f"{g.name} s={s} switch {alpha},{beta}")
+                _, dirs, _ = bg.stats()
+                if alpha == 10**6 and L > 2:
+                    assert dirs[1] == 1, dirs
+
+
+def test_timing_hooks():
+    """Per-launch timing splits the level launches between the two kernels."""
+    import frontier_bfs_csr_amd as fb
+    g = gg.rmat(14, 16, seed=5, nsrc=2)
+    rp, ci = to_dev(g)
+    with fb.BfsGraph(rp, ci) as bg:
+        for pol in ((0, 0, 0), (0, 0, 1), (0, 0, 2)):
+            bg.set_policy(*pol)
+            bg.set_timing(True)
+            L, dist, parent, sizes = run_hip(bg, g.n, g.sources[0])
+            init_ms, level_ms, launches = bg.timing()
+            kt = bg.kernel_timing()
+            assert kt["td"][1] + kt["bu"][1] == launches, (pol, kt, launches)
+            assert kt["td"][1] - kt["bu"][1] in (0, 1), kt   # they alternate, top-down first
+            assert abs(kt["td"][0] + kt["bu"][0] - level_ms) <= 1e-3 * max(1.0, level_ms)
+            _, dirs, _ = bg.stats()
+            assert (kt["bu"][0] > 0) == bool((dirs == 1).any()) or kt["bu"][0] > 0
+            assert init_ms > 0 and level_ms > 0
+            bg.set_timing(False)
+
+
 def test_optional_outputs():
     import torch
     import frontier_bfs_csr_amd as fb
