@@ -41,7 +41,8 @@ struct bfs_graph {
     const int32_t *row_ptr = nullptr;
     const int32_t *col_idx = nullptr;
     int32_t sorted = 0, symmetric = 0, max_degree = 0;
-    int grid = 0;
+    int grid = 0;      // init and top-down launches: one full wave of workgroups
+    int grid_bu = 0;   // bottom-up launches
     uint32_t *visited = nullptr, *vis_init = nullptr, *fbm0 = nullptr, *fbm1 = nullptr;
     uint32_t *cf = nullptr;        // 3 coarse frontier maps
     int32_t cf_sh = 0, cf_words = 0;
@@ -253,7 +254,8 @@ bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *co
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, g->device) != hipSuccess ||
             cus <= 0)
             cus = 256;
-        g->grid = cus * level_kernel_blocks_per_cu();
+        g->grid = cus * level_kernel_blocks_per_cu(false);
+        g->grid_bu = cus * level_kernel_blocks_per_cu(true);
     }
     if (rc != 0) {
         free_all(g);
@@ -389,7 +391,8 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
             HIP_TRY(hipEventRecord(g->events[2], stream), BFS_EHIP);
         }
         for (int64_t i = 0; i < batch && k <= kmax; ++i, ++k) {
-            HIP_TRY(launch_level(P, (int32_t)k, g->grid, stream), BFS_EHIP);   // k = launch index
+            HIP_TRY(launch_level(P, (int32_t)k, (k & 1) ? g->grid_bu : g->grid, stream),
+                    BFS_EHIP);   // k = launch index
             if (timing) HIP_TRY(hipEventRecord(g->events[3 + i], stream), BFS_EHIP);
         }
         HIP_TRY(hipMemcpyAsync(g->host_ctl, g->ctl, sizeof(HostCtl), hipMemcpyDeviceToHost, stream),

@@ -86,40 +86,15 @@ __device__ __forceinline__ T wave_sum(T x) {
 
 // ---------------------------------------------------------- LDS layout -----
 
-// Shared state of one level launch.  The work area is used by one pass at a
-// time: the frontier list of the from-bitmap pass or the segment table of the
-// edge-balanced pass.
 constexpr int WORK_INTS = 3 * (EB_TE + 1);
 constexpr int FLIST_CAP = 4 * BLOCK;     // from-bitmap pass: 4 word pairs per wave per round
 static_assert(FLIST_CAP <= WORK_INTS, "work area too small");
 
-struct LevelShared {
-    union {
-        struct {                          // top-down passes
-            int32_t buf[CAP];             // staged new frontier vertices
-            int32_t work[WORK_INTS];
-            int32_t big_v[BLOCK], big_beg[BLOCK], big_len[BLOCK];
-            int32_t tstart[CAP], toff[CAP];   // flush: piece start / edge offset of each staged slot
-        };
-        struct {                          // bottom-up pass, per wavefront
-            int32_t bu_lst[WAVES][BU_GSZ];   // listed unvisited vertices
-            int32_t bu_deg[WAVES][BU_GSZ];   // their degrees
-            int32_t bu_hit[WAVES][BU_GSZ];   // entry of the first hit, BU_NOHIT if none
-            int32_t bu_pi[WAVES][BU_GSZ];    // pending vertices: index into bu_lst,
-            int32_t bu_pn[WAVES][BU_GSZ];    //   next entry to probe,
-            int32_t bu_pe[WAVES][BU_GSZ];    //   end of the list,
-            int32_t bu_ps[WAVES][BU_GSZ];    //   exclusive scan of this round's probes
-            unsigned long long bu_fm[WAVES][WAVE];  // found masks of the 64 words in hand
-            uint32_t bu_cf[CF_WORDS];        // coarse frontier map (when use_cf)
-        };
-    };
-    int32_t ntiles;
+// Shared state of one level launch: the decision (identical in every
+// workgroup) and the bookkeeping common to both directions ...
+struct LevelCommon {
     uint64_t scan_tmp[3][WAVES];
-    unsigned long long list_base[NLISTS];
-    int32_t cnt;                      // staged count (may exceed CAP: overflow spilled)
-    int32_t nbig;
-    int32_t fl_cnt[WAVES], fl_more[WAVES];   // from-bitmap lists: count, words left
-    // decision, identical in every workgroup
+    // decision
     int32_t mode;                     // 0 exit, 1 finish, 2 run
     int32_t dir, input_bm, wbits, wcf, clear_bm, adv_eb, small, use_cf, cf_clear;
     int32_t fsize;
@@ -129,10 +104,40 @@ struct LevelShared {
     int32_t uprefix[NLISTS * STRIPES + 1];  // unit prefix (binned or edge-balanced)
 };
 
-// Per-thread context of one level launch.
-struct Ctx {
+// ... then the top-down kernel's work areas (one pass at a time uses the work
+// area: the frontier lists of the from-bitmap pass or the segment table of
+// the edge-balanced pass) ...
+struct TdLds : LevelCommon {
+    int32_t buf[CAP];                 // staged new frontier vertices
+    int32_t work[WORK_INTS];
+    int32_t big_v[BLOCK], big_beg[BLOCK], big_len[BLOCK];
+    int32_t tstart[CAP], toff[CAP];   // flush: piece start / edge offset of each staged slot
+    int32_t ntiles;
+    unsigned long long list_base[NLISTS];
+    int32_t cnt;                      // staged count (may exceed CAP: overflow spilled)
+    int32_t nbig;
+    int32_t fl_cnt[WAVES], fl_more[WAVES];   // from-bitmap lists: count, words left
+};
+
+// ... and the bottom-up kernel's, per wavefront; kept small so that several
+// workgroups share a compute unit.
+struct BuLds : LevelCommon {
+    int32_t bu_lst[WAVES][BU_GSZ];   // listed unvisited vertices
+    int32_t bu_deg[WAVES][BU_GSZ];   // their degrees
+    int32_t bu_hit[WAVES][BU_GSZ];   // entry of the first hit, BU_NOHIT if none
+    int32_t bu_pi[WAVES][BU_GSZ];    // pending vertices: index into bu_lst,
+    int32_t bu_pn[WAVES][BU_GSZ];    //   next entry to probe,
+    int32_t bu_pe[WAVES][BU_GSZ];    //   end of the list,
+    int32_t bu_ps[WAVES][BU_GSZ];    //   exclusive scan of this round's probes
+    unsigned long long bu_fm[WAVES][WAVE];  // found masks of the 64 words in hand
+    uint32_t bu_cf[CF_WORDS];        // coarse frontier map (when use_cf)
+};
+
+// Per-thread context of one level launch (S: the kernel's LDS layout).
+template <class S>
+struct CtxT {
     const Params *P;
-    LevelShared *sh;
+    S *sh;
     int32_t level;          // k: new vertices get k+1
     int32_t wg, G;          // this workgroup's index among the G taking part
     int32_t stripe;         // counter / queue stripe of this workgroup
@@ -147,6 +152,8 @@ struct Ctx {
     int32_t fcnt;
     int64_t fdeg;
 };
+using Ctx = CtxT<TdLds>;
+using BuCtx = CtxT<BuLds>;
 
 // --------------------------------------------------------- emission --------
 
@@ -296,7 +303,7 @@ __device__ __forceinline__ void claim_run(Ctx &c, int e0, int stride, int end, i
 // few registers live; the second pass re-reads row_ptr entries the first one
 // just loaded.
 __device__ __forceinline__ void flush(Ctx &c) {
-    LevelShared &sh = *c.sh;
+    auto &sh = *c.sh;
     const Params &P = *c.P;
     __syncthreads();
     const int cnt = min(sh.cnt, CAP);
@@ -401,7 +408,7 @@ __device__ __forceinline__ void maybe_flush(Ctx &c) {
 // Expand the segments held by the threads of the workgroup (at most one per
 // thread): lane, wavefront or workgroup mapping by length.  Ends with a barrier.
 __device__ __forceinline__ void expand_segments(Ctx &c, bool has, int v, int beg, int len) {
-    LevelShared &sh = *c.sh;
+    auto &sh = *c.sh;
     // lane bin: CB consecutive entries per step
     if (has && len < T_LANE) {
         for (int e = beg; e < beg + len; e += CB) claim_run(c, e, 1, beg + len, v);
@@ -441,7 +448,7 @@ __device__ __forceinline__ void expand_segments(Ctx &c, bool has, int v, int beg
 // per lane, BLOCK per unit); units are dealt round-robin to workgroups.
 __device__ __forceinline__ void td_binned(Ctx &c, const Seg *cq, const Seg *ct, uint32_t *cbm) {
     const Params &P = *c.P;
-    LevelShared &sh = *c.sh;
+    auto &sh = *c.sh;
     const int total = sh.uprefix[NLISTS * STRIPES];
     for (int u = c.wg; u < total; u += c.G) {
         // find (list, stripe) region of unit u
@@ -477,7 +484,7 @@ __device__ __forceinline__ void td_binned(Ctx &c, const Seg *cq, const Seg *ct, 
 __device__ __forceinline__ void td_edge_balanced(Ctx &c, const Seg *cq, const Seg *ct, const int32_t *cts,
                                  uint32_t *cbm) {
     const Params &P = *c.P;
-    LevelShared &sh = *c.sh;
+    auto &sh = *c.sh;
     int32_t *s_off = sh.work;
     int32_t *s_v = sh.work + (EB_TE + 1);
     int32_t *s_beg = sh.work + 2 * (EB_TE + 1);
@@ -541,7 +548,7 @@ constexpr int FL_WAVE = FLIST_CAP / WAVES;
 
 __device__ __forceinline__ void td_from_bitmap(Ctx &c, uint32_t *cbm, uint32_t *obm) {
     const Params &P = *c.P;
-    LevelShared &sh = *c.sh;
+    auto &sh = *c.sh;
     const int lane = lane_id();
     const int wv = wave_id();
     int32_t *flist = sh.work + wv * FL_WAVE;
@@ -638,7 +645,7 @@ __device__ __forceinline__ int wave_incl_scan_i32(int x) {
 constexpr int BU_NOHIT = 0x7fffffff;
 
 // Can u be in the frontier?  (false only when its coarse bit is clear)
-__device__ __forceinline__ bool cf_maybe(const LevelShared &sh, int use_cf, int cf_sh, int u) {
+__device__ __forceinline__ bool cf_maybe(const BuLds &sh, int use_cf, int cf_sh, int u) {
     if (!use_cf) return true;
     const uint32_t b = (uint32_t)u >> cf_sh;
     return (sh.bu_cf[b >> 5] >> (b & 31)) & 1u;
@@ -666,7 +673,7 @@ __device__ __forceinline__ void load_block8(const Params &P, bool go, int e, int
 
 // The first entry of x (in order) that is in the frontier, else -1.  All
 // probes are issued before any result is used.
-__device__ __forceinline__ int probe_first(const LevelShared &sh, const uint32_t *cbm, int use_cf,
+__device__ __forceinline__ int probe_first(const BuLds &sh, const uint32_t *cbm, int use_cf,
                                            int cf_sh, const int (&x)[8]) {
     uint32_t w[8];
 #pragma unroll
@@ -680,7 +687,7 @@ __device__ __forceinline__ int probe_first(const LevelShared &sh, const uint32_t
 }
 
 // Records that listed vertex v found parent u.
-__device__ __forceinline__ void bu_found(Ctx &c, int wbase, int v, int u, int d) {
+__device__ __forceinline__ void bu_found(BuCtx &c, int wbase, int v, int u, int d) {
     const Params &P = *c.P;
     P.dist[v] = c.level + 1;
     if (P.parent) P.parent[v] = u;
@@ -691,9 +698,9 @@ __device__ __forceinline__ void bu_found(Ctx &c, int wbase, int v, int u, int d)
 
 // Searches parents for the listed vertices lst[0, cnt) of this wavefront
 // (all inside words [wbase, wbase + 64)).
-__device__ __forceinline__ void bu_list(Ctx &c, const uint32_t *cbm, int cnt, int wbase) {
+__device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, int wbase) {
     const Params &P = *c.P;
-    LevelShared &sh = *c.sh;
+    auto &sh = *c.sh;
     const int lane = lane_id();
     const int wv = wave_id();
     const int use_cf = sh.use_cf, cf_sh = P.cf_sh;
@@ -843,9 +850,9 @@ __device__ __forceinline__ void bu_list(Ctx &c, const uint32_t *cbm, int cnt, in
     }
 }
 
-__device__ __forceinline__ void bottom_up(Ctx &c, const uint32_t *cbm, uint32_t *nbm) {
+__device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_t *nbm) {
     const Params &P = *c.P;
-    LevelShared &sh = *c.sh;
+    auto &sh = *c.sh;
     const int lane = lane_id();
     const int wv = wave_id();
     if (sh.use_cf) {
@@ -958,7 +965,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
 // Decision for level k, taken by wavefront 0 of every workgroup from the
 // counters the previous level left (identical in every workgroup); the
 // caller synchronises before reading it.
-__device__ __forceinline__ void decide(const Params &P, LevelShared &sh, int k) {
+__device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) {
     const int lane = lane_id();
     const int slot = k % NSLOTS;
     const int done = P.ctl->done;
@@ -972,7 +979,6 @@ __device__ __forceinline__ void decide(const Params &P, LevelShared &sh, int k) 
         sh.ledges[lane] = (int32_t)(cv & 0xffffffffull);
     }
     if (lane == 0) {
-        sh.cnt = 0; sh.nbig = 0;
         sh.fsize = (int32_t)fsize; sh.fdeg = fdeg;
         sh.small = 0;
         sh.use_cf = 0;
@@ -1064,10 +1070,13 @@ __device__ __forceinline__ void small_barrier(const Params &P, int G) {
 
 // One level on the G workgroups taking part (this one is number wg); BU
 // selects the direction's code (the decision in sh must agree).
-template <bool BU>
-__device__ __forceinline__ void run_level(const Params &P, LevelShared &sh, int k, int wg, int G) {
+template <bool BU, class S>
+__device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg, int G) {
     const int lane = lane_id();
     const int slot = k % NSLOTS;
+    if constexpr (!BU) {
+        if (threadIdx.x == 0) { sh.cnt = 0; sh.nbig = 0; }
+    }
     // unit prefix tables
     if (threadIdx.x == 0) {
         int acc = 0;
@@ -1100,7 +1109,7 @@ __device__ __forceinline__ void run_level(const Params &P, LevelShared &sh, int 
     }
     __syncthreads();
 
-    Ctx c;
+    CtxT<S> c;
     c.P = &P;
     c.sh = &sh;
     c.level = k;
@@ -1157,7 +1166,7 @@ __device__ __forceinline__ void run_level(const Params &P, LevelShared &sh, int 
 // for it.  Returns that level, or -1 when the launch has nothing to do (the
 // search is over, an error was recorded, or it has just found the empty
 // frontier and recorded the end).
-__device__ __forceinline__ int level_launch_start(const Params &P, LevelShared &sh, int launch) {
+__device__ __forceinline__ int level_launch_start(const Params &P, LevelCommon &sh, int launch) {
     const int k = P.ctl->lvl[launch & 1];
     if (threadIdx.x < WAVE) decide(P, sh, k);
     __syncthreads();
@@ -1179,7 +1188,7 @@ __device__ __forceinline__ void set_next_level(const Params &P, int launch, int 
 // level is passed on to the next launch.  One decision point serves every
 // level of the launch.
 __global__ __launch_bounds__(BLOCK, 4) void bfs_td_kernel(Params P, int32_t launch) {
-    __shared__ LevelShared sh;
+    __shared__ TdLds sh;
     int k = P.ctl->lvl[launch & 1];
     int G = 0;   // 0 until the first level is decided
     for (;;) {
@@ -1208,8 +1217,8 @@ __global__ __launch_bounds__(BLOCK, 4) void bfs_td_kernel(Params P, int32_t laun
 
 // Bottom-up launch: runs the level it stands at when that level is
 // bottom-up, else passes it on.
-__global__ __launch_bounds__(BLOCK, 4) void bfs_bu_kernel(Params P, int32_t launch) {
-    __shared__ LevelShared sh;
+__global__ __launch_bounds__(BLOCK, 8) void bfs_bu_kernel(Params P, int32_t launch) {
+    __shared__ BuLds sh;
     const int k = level_launch_start(P, sh, launch);
     if (k < 0) return;
     if (sh.dir != DIR_BU) {
@@ -1311,14 +1320,10 @@ hipError_t launch_level(const Params &P, int32_t launch_index, int grid, hipStre
     return hipGetLastError();
 }
 
-int level_kernel_blocks_per_cu() {
-    int a = 0, b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, (const void *)bfs_td_kernel, BLOCK, 0) !=
-            hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, (const void *)bfs_bu_kernel, BLOCK, 0) !=
-            hipSuccess)
-        return 1;
-    const int nb = a < b ? a : b;
+int level_kernel_blocks_per_cu(bool bottom_up) {
+    int nb = 0;
+    const void *fn = bottom_up ? (const void *)bfs_bu_kernel : (const void *)bfs_td_kernel;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, BLOCK, 0) != hipSuccess) return 1;
     return nb > 0 ? nb : 1;
 }
 

@@ -25,7 +25,7 @@ constexpr int BU_W1 = 8;                 // bottom-up: entries per vertex in the
                                          // the first (x4 per round after that)
 constexpr int BU_WMAX = 8192;            // bottom-up: cap of the per-round entries per vertex
 constexpr int BU_U = 4;                  // bottom-up: probes a lane keeps in flight per step
-constexpr int CF_WORDS = 8192;           // coarse frontier map: at most 8192 words (32 KB)
+constexpr int CF_WORDS = 4096;           // coarse frontier map: at most 4096 words (16 KB)
 // direction switching (edge-based, as in Beamer et al. SC'12): go bottom-up
 // when the frontier's edges exceed 1/alpha of the unexplored vertices' edges;
 // come back top-down when the frontier is under n/beta and shrinking.  These
@@ -133,8 +133,11 @@ struct Params {
 
 // host-side launch helpers (bfs_device.hip)
 hipError_t launch_init(const Params &P, int grid, hipStream_t s);
+// launch `launch_index` of the level chain: even indexes run the top-down
+// kernel, odd ones the bottom-up kernel
 hipError_t launch_level(const Params &P, int32_t launch_index, int grid, hipStream_t s);
-int level_kernel_blocks_per_cu();
+// resident workgroups per compute unit of the top-down or bottom-up kernel
+int level_kernel_blocks_per_cu(bool bottom_up);
 
 // graph validation / classification (bfs_device.hip)
 struct GraphFacts {
