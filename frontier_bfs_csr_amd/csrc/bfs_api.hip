@@ -45,6 +45,7 @@ struct bfs_graph {
     int grid_bu = 0;   // bottom-up launches
     uint32_t *visited = nullptr, *vis_init = nullptr, *fbm0 = nullptr, *fbm1 = nullptr;
     uint32_t *cf = nullptr;        // 3 coarse frontier maps
+    int32_t *fnb = nullptr;        // first neighbour of each vertex
     int32_t cf_sh = 0, cf_words = 0;
     Seg *q0 = nullptr, *q1 = nullptr, *t0 = nullptr, *t1 = nullptr;
     int32_t *ts0 = nullptr, *ts1 = nullptr;
@@ -89,7 +90,7 @@ hipError_t dalloc(T **p, size_t count) {
 }
 
 void free_all(bfs_graph *g) {
-    void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->cf, g->q0, g->q1, g->t0, g->t1,
+    void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->cf, g->fnb, g->q0, g->q1, g->t0, g->t1,
                     g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
@@ -128,6 +129,7 @@ int alloc_workspace(bfs_graph *g) {
         {dalloc(&g->fbm0, 2 * nwp), "frontier bitmap"},
         {dalloc(&g->fbm1, 2 * nwp), "frontier bitmap"},
         {dalloc(&g->cf, 3 * (int64_t)CF_WORDS), "coarse frontier maps"},
+        {dalloc(&g->fnb, n), "first-neighbour index"},
         {dalloc(&g->q0, (size_t)STRIPES * g->qcap), "frontier queue"},
         {dalloc(&g->q1, (size_t)STRIPES * g->qcap), "frontier queue"},
         {dalloc(&g->t0, (size_t)STRIPES * g->tcap), "tile queue"},
@@ -239,9 +241,11 @@ bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *co
     if (rc == 0) rc = alloc_workspace(g);
     if (rc == 0) {
         hipError_t e = launch_build_vis_init(row_ptr, n, g->symmetric, g->vis_init, 0);
+        if (e == hipSuccess) e = launch_build_first_nb(row_ptr, col_idx, n, g->fnb, 0);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) {
-            set_error("building the visited template failed: %s", hipGetErrorString(e));
+            set_error("building the visited template and first-neighbour index failed: %s",
+                      hipGetErrorString(e));
             rc = BFS_EHIP;
         }
     }
@@ -337,6 +341,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.level_sizes = level_sizes_out;
     P.visited = g->visited;
     P.vis_init = g->vis_init;
+    P.fnb = g->fnb;
     P.fbm0 = g->fbm0;
     P.fbm1 = g->fbm1;
     P.cf = g->cf;

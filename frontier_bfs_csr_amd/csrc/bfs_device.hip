@@ -707,51 +707,43 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
     int32_t *lst = sh.bu_lst[wv], *deg = sh.bu_deg[wv], *hit = sh.bu_hit[wv];
     int32_t *pi = sh.bu_pi[wv], *pn = sh.bu_pn[wv], *pe = sh.bu_pe[wv], *ps = sh.bu_ps[wv];
     constexpr int R0 = BU_GSZ / WAVE;   // listed vertices per lane in round 0
-    // round 0: the aligned 8-entry block holding the first entry of every
-    // listed vertex (two 16-byte loads); R0 vertices per lane with their loads
-    // overlapped; a hit is recorded at once
+    // round 0: every listed vertex's first neighbour, from the first-neighbour
+    // index (read in vertex order beside row_ptr, so no scattered adjacency
+    // line is fetched for the vertices that stop there); R0 vertices per lane
+    // with their loads overlapped; a hit is recorded at once
     int npend = 0;
     {
-        int v[R0], beg[R0], en[R0];
+        int v[R0], beg[R0], en[R0], par[R0];
         int x[R0][8];
 #pragma unroll
         for (int j = 0; j < R0; ++j) {
             const int i = j * WAVE + lane;
             v[j] = (i < cnt) ? lst[i] : -1;
         }
-#pragma unroll
-        for (int j = 0; j < R0; ++j) {
-            beg[j] = (v[j] >= 0) ? P.row_ptr[v[j]] : 0;
-            en[j] = (v[j] >= 0) ? P.row_ptr[v[j] + 1] : 0;
-        }
-#pragma unroll
-        for (int j = 0; j < R0; ++j) load_block8(P, beg[j] < en[j], beg[j], beg[j], en[j], x[j]);
-        // the first entry alone (most vertices of a wide level stop there) ...
-        int par[R0];
         {
             int f[R0];
             uint32_t w[R0];
 #pragma unroll
             for (int j = 0; j < R0; ++j) {
-                f[j] = -1;
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    if ((beg[j] & 7) == q) f[j] = x[j][q];
-                w[j] = (f[j] >= 0 && cf_maybe(sh, use_cf, cf_sh, f[j])) ? cbm[f[j] >> 5] : 0u;
+                beg[j] = (v[j] >= 0) ? P.row_ptr[v[j]] : 0;
+                en[j] = (v[j] >= 0) ? P.row_ptr[v[j] + 1] : 0;
+                f[j] = (v[j] >= 0) ? P.fnb[v[j]] : -1;
             }
+#pragma unroll
+            for (int j = 0; j < R0; ++j)
+                w[j] = (f[j] >= 0 && cf_maybe(sh, use_cf, cf_sh, f[j])) ? cbm[f[j] >> 5] : 0u;
 #pragma unroll
             for (int j = 0; j < R0; ++j) par[j] = (f[j] >= 0 && ((w[j] >> (f[j] & 31)) & 1u)) ? f[j] : -1;
         }
-        // ... then the rest of the block for the vertices still searching
+        // ... then the aligned 8-entry block holding the first entry (two
+        // 16-byte loads), for the vertices still searching with more entries
         bool more = false;
 #pragma unroll
-        for (int j = 0; j < R0; ++j) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                if (par[j] >= 0 || q <= (beg[j] & 7)) x[j][q] = -1;
-            more |= par[j] < 0 && beg[j] + 1 < min((beg[j] | 7) + 1, en[j]);
-        }
+        for (int j = 0; j < R0; ++j) more |= par[j] < 0 && beg[j] + 1 < min((beg[j] | 7) + 1, en[j]);
         if (__ballot(more)) {
+#pragma unroll
+            for (int j = 0; j < R0; ++j)
+                load_block8(P, par[j] < 0 && beg[j] + 1 < en[j], beg[j], beg[j] + 1, en[j], x[j]);
 #pragma unroll
             for (int j = 0; j < R0; ++j)
                 if (par[j] < 0) par[j] = probe_first(sh, cbm, use_cf, cf_sh, x[j]);
@@ -1217,7 +1209,7 @@ __global__ __launch_bounds__(BLOCK, 4) void bfs_td_kernel(Params P, int32_t laun
 
 // Bottom-up launch: runs the level it stands at when that level is
 // bottom-up, else passes it on.
-__global__ __launch_bounds__(BLOCK, 8) void bfs_bu_kernel(Params P, int32_t launch) {
+__global__ __launch_bounds__(BLOCK, 6) void bfs_bu_kernel(Params P, int32_t launch) {
     __shared__ BuLds sh;
     const int k = level_launch_start(P, sh, launch);
     if (k < 0) return;
@@ -1350,6 +1342,23 @@ hipError_t launch_check_symmetry(const int32_t *row_ptr, const int32_t *col_idx,
                                  GraphFacts *f, hipStream_t s) {
     hipLaunchKernelGGL(check_symmetry_kernel, dim3(grid_for((int64_t)n * WAVE, 256 * 8)), dim3(256), 0,
                        s, row_ptr, col_idx, n, f);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void first_nb_kernel(const int32_t *row_ptr,
+                                                       const int32_t *col_idx, int32_t n,
+                                                       int32_t *fnb) {
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n; v += nth) {
+        const int32_t b = row_ptr[v];
+        fnb[v] = (b < row_ptr[v + 1]) ? col_idx[b] : -1;
+    }
+}
+
+hipError_t launch_build_first_nb(const int32_t *row_ptr, const int32_t *col_idx, int32_t n,
+                                 int32_t *fnb, hipStream_t s) {
+    hipLaunchKernelGGL(first_nb_kernel, dim3(grid_for(n, 256 * 4)), dim3(256), 0, s, row_ptr,
+                       col_idx, n, fnb);
     return hipGetLastError();
 }
 

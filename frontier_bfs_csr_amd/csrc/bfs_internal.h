@@ -106,6 +106,7 @@ struct Params {
     int32_t *level_sizes;     // may be null
     uint32_t *visited;        // 2*nwp words
     const uint32_t *vis_init; // 2*nwp words: isolated vertices (symmetric graphs) + padding
+    const int32_t *fnb;       // n entries: first CSR neighbour of each vertex, -1 if none
     uint32_t *fbm0, *fbm1;    // frontier bitmaps, 2*nwp words each
     Seg *q0, *q1;             // STRIPES regions of qcap segments (small from the front,
                               // mid from the back)
@@ -155,5 +156,7 @@ hipError_t launch_check_symmetry(const int32_t *row_ptr, const int32_t *col_idx,
                                  GraphFacts *f, hipStream_t s);
 hipError_t launch_build_vis_init(const int32_t *row_ptr, int32_t n, int32_t mark_isolated,
                                  uint32_t *vis_init, hipStream_t s);
+hipError_t launch_build_first_nb(const int32_t *row_ptr, const int32_t *col_idx, int32_t n,
+                                 int32_t *fnb, hipStream_t s);
 
 }  // namespace fbfs
