@@ -91,7 +91,7 @@ def main():
     ap.add_argument("--direction", type=int, default=0, help="0 auto, 1 push, 2 pull")
     ap.add_argument("--advance", type=int, default=0, help="0 auto, 1 binned, 2 edge-balanced")
     ap.add_argument("--loop", type=int, default=0, help="0 device-resident, 1 host-driven")
-    ap.add_argument("--alpha", type=int, default=14, help="direction switch: pull when alpha*deg(F) > deg(U)")
+    ap.add_argument("--alpha", type=int, default=28, help="direction switch: pull when alpha*deg(F) > deg(U)")
     ap.add_argument("--beta", type=int, default=24, help="direction switch: push when beta*|F| < n, shrinking")
     ap.add_argument("--no-parent", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,

@@ -131,7 +131,7 @@ def bfs_set_policy(g, direction=DIR_AUTO, advance=ADV_AUTO, loop=LOOP_DEVICE):
         raise BfsError(rc, bfs_last_error())
 
 
-def bfs_set_switch(g, alpha=14, beta=24):
+def bfs_set_switch(g, alpha=28, beta=24):
     rc = load().bfs_set_switch(g, int(alpha), int(beta))
     if rc < 0:
         raise BfsError(rc, bfs_last_error())
@@ -203,7 +203,7 @@ class BfsGraph:
     def set_policy(self, direction=DIR_AUTO, advance=ADV_AUTO, loop=LOOP_DEVICE):
         bfs_set_policy(self.handle, direction, advance, loop)
 
-    def set_switch(self, alpha=14, beta=24):
+    def set_switch(self, alpha=28, beta=24):
         bfs_set_switch(self.handle, alpha, beta)
 
     def stats(self):

@@ -109,6 +109,7 @@ struct LevelCommon {
 // the edge-balanced pass) ...
 struct TdLds : LevelCommon {
     int32_t buf[CAP];                 // staged new frontier vertices
+    int32_t sbeg[CAP], slen[CAP];     // their adjacency start and degree
     int32_t work[WORK_INTS];
     int32_t big_v[BLOCK], big_beg[BLOCK], big_len[BLOCK];
     int32_t tstart[CAP], toff[CAP];   // flush: piece start / edge offset of each staged slot
@@ -117,6 +118,7 @@ struct TdLds : LevelCommon {
     int32_t cnt;                      // staged count (may exceed CAP: overflow spilled)
     int32_t nbig;
     int32_t fl_cnt[WAVES], fl_more[WAVES];   // from-bitmap lists: count, words left
+    int32_t vfilter;                  // claims first load the visited words
 };
 
 // ... and the bottom-up kernel's, per wavefront; kept small so that several
@@ -206,12 +208,10 @@ __device__ __forceinline__ int list_of(int len) {
     return len <= 0 ? -1 : (len < T_LANE ? L_SMALL : (len < T_WG ? L_MID : L_TILE));
 }
 
-// One vertex, one lane: used when the LDS staging buffer is full (the
-// expansion loops flush often enough that this is rare).
-__device__ __forceinline__ void emit_single(Ctx &c, int v) {
+// One vertex (adjacency [beg, beg+len)), one lane: used when the LDS staging
+// buffer is full (the expansion loops flush often enough that this is rare).
+__device__ __forceinline__ void emit_single(Ctx &c, int v, int beg, int len) {
     const Params &P = *c.P;
-    const int beg = P.row_ptr[v];
-    const int len = P.row_ptr[v + 1] - beg;
     c.fcnt += 1;
     c.fdeg += len;
     const int l = list_of(len);
@@ -222,8 +222,9 @@ __device__ __forceinline__ void emit_single(Ctx &c, int v) {
     write_vertex_segments(c, l, v, beg, len, (int64_t)(base >> 32), (int64_t)(base & 0xffffffffull));
 }
 
-// Stage a winner in LDS (wave-aggregated LDS atomic, rank by mbcnt).
-__device__ __forceinline__ void stage(Ctx &c, bool win, int v) {
+// Stage a winner (adjacency [beg, beg+len)) in LDS (wave-aggregated LDS
+// atomic, rank by mbcnt).
+__device__ __forceinline__ void stage(Ctx &c, bool win, int v, int beg, int len) {
     const uint64_t m = __ballot(win);
     if (m == 0) return;
     const int leader = __ffsll((unsigned long long)m) - 1;
@@ -233,18 +234,26 @@ __device__ __forceinline__ void stage(Ctx &c, bool win, int v) {
     bool spill = false;
     if (win) {
         const int slot = base + mbcnt64(m);
-        if (slot < CAP) c.sh->buf[slot] = v;
-        else spill = true;
+        if (slot < CAP) {
+            c.sh->buf[slot] = v;
+            c.sh->sbeg[slot] = beg;
+            c.sh->slen[slot] = len;
+        } else {
+            spill = true;
+        }
     }
     // the lanes that found the buffer full append their vertex directly
-    if (spill) emit_single(c, v);
+    if (spill) emit_single(c, v, beg, len);
 }
 
 // Claim up to N targets (v[q] valid where ok[q], reached from u[q]) for
-// level k+1: filter on plain loads of the visited words, then one atomicOr per
-// remaining target decides its single winner.  The N loads and the N atomics
-// are each issued before any result is used, so a lane keeps N claims in
-// flight instead of one.
+// level k+1: one atomicOr per target on the visited bitmap decides its single
+// winner.  On wide levels (vfilter) a plain load of the visited words first
+// drops the targets already visited, sparing their atomics; on narrow levels
+// that load would only lengthen the chain.  The loads and atomics of the N
+// targets are each issued before any result is used, so a lane keeps N
+// claims in flight; a winner's adjacency bounds are fetched at once for the
+// flush.
 constexpr int CB = 4;
 
 template <int N>
@@ -252,20 +261,31 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
                                             const int (&u)[N]) {
     constexpr int CB = N;
     const Params &P = *c.P;
-    uint32_t w[CB];
-#pragma unroll
-    for (int q = 0; q < CB; ++q) w[q] = ok[q] ? P.visited[v[q] >> 5] : ~0u;
     bool tryq[CB];
+    if (c.sh->vfilter) {
+        uint32_t w[CB];
 #pragma unroll
-    for (int q = 0; q < CB; ++q) tryq[q] = ok[q] && !((w[q] >> (v[q] & 31)) & 1u);
+        for (int q = 0; q < CB; ++q) w[q] = ok[q] ? P.visited[v[q] >> 5] : ~0u;
+#pragma unroll
+        for (int q = 0; q < CB; ++q) tryq[q] = ok[q] && !((w[q] >> (v[q] & 31)) & 1u);
+    } else {
+#pragma unroll
+        for (int q = 0; q < CB; ++q) tryq[q] = ok[q];
+    }
     uint32_t old[CB];
 #pragma unroll
     for (int q = 0; q < CB; ++q)
         old[q] = tryq[q] ? atomicOr(P.visited + (v[q] >> 5), 1u << (v[q] & 31)) : ~0u;
     bool win[CB];
+    int beg[CB], len[CB];
 #pragma unroll
     for (int q = 0; q < CB; ++q) {
         win[q] = tryq[q] && !((old[q] >> (v[q] & 31)) & 1u);
+        beg[q] = win[q] ? P.row_ptr[v[q]] : 0;
+        len[q] = win[q] ? P.row_ptr[v[q] + 1] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < CB; ++q) {
         if (win[q]) {
             P.dist[v[q]] = c.level + 1;
             if (P.parent) P.parent[v[q]] = u[q];
@@ -277,7 +297,7 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
         }
     }
 #pragma unroll
-    for (int q = 0; q < CB; ++q) stage(c, win[q], v[q]);
+    for (int q = 0; q < CB; ++q) stage(c, win[q], v[q], beg[q], len[q] - beg[q]);
 }
 
 // Claims for entries e0, e0+stride, ... (N of them) of col_idx below `end`.
@@ -300,8 +320,7 @@ __device__ __forceinline__ void claim_run(Ctx &c, int e0, int stride, int end, i
 // Workgroup flush of the staged vertices: one global atomic per list per
 // flush (exclusive scans of (segments, edges) give every vertex its place).
 // Two passes over the thread's staged slots -- tally, then write -- keep
-// few registers live; the second pass re-reads row_ptr entries the first one
-// just loaded.
+// few registers live; both read the staged adjacency bounds from LDS.
 __device__ __forceinline__ void flush(Ctx &c) {
     auto &sh = *c.sh;
     const Params &P = *c.P;
@@ -311,9 +330,7 @@ __device__ __forceinline__ void flush(Ctx &c) {
     const int i0 = threadIdx.x * EPT;
     uint64_t tot0 = 0, tot1 = 0, tot2 = 0;
     for (int i = i0; i < min(i0 + EPT, cnt); ++i) {
-        const int v = sh.buf[i];
-        const int beg = P.row_ptr[v];
-        const int len = P.row_ptr[v + 1] - beg;
+        const int len = sh.slen[i];
         c.fcnt += 1;
         c.fdeg += len;
         const int l = list_of(len);
@@ -352,8 +369,8 @@ __device__ __forceinline__ void flush(Ctx &c) {
     const uint64_t b0 = sh.list_base[L_SMALL], b1 = sh.list_base[L_MID];
     for (int i = i0; i < min(i0 + EPT, cnt); ++i) {
         const int v = sh.buf[i];
-        const int beg = P.row_ptr[v];
-        const int len = P.row_ptr[v + 1] - beg;
+        const int beg = sh.sbeg[i];
+        const int len = sh.slen[i];
         const int l = list_of(len);
         sh.tstart[i] = (int32_t)(ex2 >> 32);
         sh.toff[i] = (int32_t)(ex2 & 0xffffffffull);
@@ -383,8 +400,8 @@ __device__ __forceinline__ void flush(Ctx &c) {
                 if (sh.tstart[mid] <= gt) lo = mid; else hi = mid;
             }
             const int v = sh.buf[lo];
-            const int beg = P.row_ptr[v];
-            const int len = P.row_ptr[v + 1] - beg;
+            const int beg = sh.sbeg[lo];
+            const int len = sh.slen[lo];
             const int pcs = gt - sh.tstart[lo];
             write_piece(c, L_TILE, tbase + gt, v, beg + pcs * TILE, min(TILE, len - pcs * TILE),
                         ebase + sh.toff[lo] + (int64_t)pcs * TILE);
@@ -1067,7 +1084,13 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
     const int lane = lane_id();
     const int slot = k % NSLOTS;
     if constexpr (!BU) {
-        if (threadIdx.x == 0) { sh.cnt = 0; sh.nbig = 0; }
+        if (threadIdx.x == 0) {
+            sh.cnt = 0;
+            sh.nbig = 0;
+            // a visited-word load before each claim pays on levels with many
+            // edges (it spares the atomics of targets already reached)
+            sh.vfilter = sh.fdeg >= VFILTER_EDGES;
+        }
     }
     // unit prefix tables
     if (threadIdx.x == 0) {

@@ -20,6 +20,8 @@ constexpr int CAP = 2048;                // LDS staging capacity for new frontie
 constexpr int STEP_CLAIMS = CAP / 2;     // claims between flush checks: a flush starts at
                                          // CAP / 2 staged, so a step never overfills
 constexpr int EB_TE = 1024;              // edges per tile of the edge-balanced advance
+constexpr int64_t VFILTER_EDGES = 1 << 20;  // top-down levels with at least this many
+                                         // edges load the visited word before a claim
 constexpr int BU_GSZ = 128;              // bottom-up: vertices a wavefront lists at a time
 constexpr int BU_W1 = 8;                 // bottom-up: entries per vertex in the round after
                                          // the first (x4 per round after that)
@@ -30,7 +32,7 @@ constexpr int CF_WORDS = 4096;           // coarse frontier map: at most 4096 wo
 // when the frontier's edges exceed 1/alpha of the unexplored vertices' edges;
 // come back top-down when the frontier is under n/beta and shrinking.  These
 // are the defaults; bfs_set_switch changes them per handle.
-constexpr int ALPHA = 14;
+constexpr int ALPHA = 28;
 constexpr int BETA = 24;
 
 // lists of a frontier queue
