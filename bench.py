@@ -4,8 +4,10 @@ One step = one complete search (initialisation plus every level) from the next
 source of the workload's source list, with the graph already resident in HBM.
 Prints ONE JSON line:
 
-  value       GTEPS = sum over timed steps of the undirected edges in the
-              source's component / wall time of the timed steps
+  value       GTEPS = sum over timed steps of the edges in the part of the
+              graph the search reached (undirected edges; out-edges of the
+              reached vertices on the directed workloads) / wall time of the
+              timed steps
   roofline    for the dominant level kernel (bfs_td_kernel or bfs_bu_kernel,
               whichever takes more time): algorithmic bytes of the levels it
               ran (byte model in frontier_bfs_csr_amd/csrc/bytemodel.c) / its
@@ -38,7 +40,10 @@ WORKLOAD_DESC = {
     "c3": "er_4M_deg16: Erdos-Renyi 4,194,304 vertices, 8n uniform pairs symmetrised",
     "c4": "grid4096_del5: 4096x4096 4-neighbour grid, 5% edges deleted, largest component, corner source",
     "c5": "rmat24_ef16: R-MAT scale 24, edge factor 16, (0.57,0.19,0.19,0.05), symmetrised, deduplicated",
+    "c2d": "rmat20_ef16_directed: R-MAT scale 20, edge factor 16, (0.57,0.19,0.19,0.05), directed, deduplicated",
+    "c5d": "rmat24_ef16_directed: R-MAT scale 24, edge factor 16, (0.57,0.19,0.19,0.05), directed, deduplicated",
 }
+DIRECTED = {"c2d": (20, 6), "c5d": (24, 7)}   # scale, seed
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "level_kernels_traffic.json")
 KERNEL_NAMES = {"td": "bfs_td_kernel", "bu": "bfs_bu_kernel"}
 
@@ -65,9 +70,12 @@ def measured_traffic(workload, kernel):
     return e.get("bytes_per_launch")
 
 
-def component_edges(deg, dist):
-    """Undirected edges of the source's component: half the reached degrees."""
-    return int(deg[dist >= 0].sum()) // 2
+def component_edges(deg, dist, symmetric=True):
+    """Edges of the part of the graph the search reached: half the reached
+    degrees of an undirected graph; the reached vertices' out-edges of a
+    directed one."""
+    total = int(deg[dist >= 0].sum())
+    return total // 2 if symmetric else total
 
 
 def copy_calibration(nbytes):
@@ -116,7 +124,12 @@ def main():
     from frontier_bfs_csr_amd import bytemodel
 
     t0 = time.time()
-    g = gg.WORKLOADS[args.workload]()
+    if args.workload in DIRECTED:
+        scale, seed = DIRECTED[args.workload]
+        g = gg.rmat_directed(scale, 16, seed=seed, nsrc=64)
+    else:
+        g = gg.WORKLOADS[args.workload]()
+    in_csr = None if g.symmetric else bytemodel.transpose(g.row_ptr, g.col_idx)
     print(f"[bench] {args.workload}: n={g.n} m={g.m} sources={len(g.sources)} "
           f"generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     deg = g.degrees()
@@ -171,8 +184,9 @@ def main():
         L = bg.run(s, dist, parent, sizes, stream)
         Ls, dirs, _ = bg.stats()
         d = dist.cpu().numpy()
-        init_b, lvl_b = bytemodel.alg_bytes(g.row_ptr, g.col_idx, d, dirs, with_parent=parent is not None)
-        model[s] = {"L": L, "init": init_b, "levels": int(lvl_b.sum()), "medges": component_edges(deg, d),
+        init_b, lvl_b = bytemodel.alg_bytes(g.row_ptr, g.col_idx, d, dirs, with_parent=parent is not None,
+                                            in_csr=in_csr)
+        model[s] = {"L": L, "init": init_b, "levels": int(lvl_b.sum()), "medges": component_edges(deg, d, g.symmetric),
                     "td": int(lvl_b[dirs == 0].sum()), "bu": int(lvl_b[dirs == 1].sum()),
                     "dirs": "".join("TB"[x] for x in dirs)}
         gpu_dist[s] = d if len(gpu_dist) < 8 else None
@@ -201,7 +215,7 @@ def main():
             ts = time.perf_counter()
             ref = oracle.bfs(g.row_ptr, g.col_idx, s)
             spent += time.perf_counter() - ts
-            cedges += component_edges(deg, ref[0])
+            cedges += component_edges(deg, ref[0], g.symmetric)
             cnt += 1
             if s in gpu_dist and gpu_dist[s] is not None:
                 ok = ok and bool((gpu_dist[s] == ref[0]).all())

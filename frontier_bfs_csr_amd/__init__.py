@@ -60,7 +60,7 @@ def load():
         lib.bfs_last_run_stats.argtypes = [P, i32, P, P]
         lib.bfs_last_run_stats.restype = i32
         lib.bfs_graph_info.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i32),
-                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
+                                       ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
         lib.bfs_graph_info.restype = i32
         lib.bfs_set_timing.argtypes = [P, i32]
         lib.bfs_set_timing.restype = i32
@@ -179,13 +179,14 @@ def bfs_last_run_kernel_timing(g):
 
 
 def bfs_graph_info(g):
-    m, srt, sym, mx = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    m, srt, sym, mx, pr = (ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(),
+                           ctypes.c_int32())
     rc = load().bfs_graph_info(g, ctypes.byref(m), ctypes.byref(srt), ctypes.byref(sym),
-                               ctypes.byref(mx))
+                               ctypes.byref(mx), ctypes.byref(pr))
     if rc < 0:
         raise BfsError(rc, bfs_last_error())
     return {"m": m.value, "sorted_rows": bool(srt.value), "symmetric": bool(sym.value),
-            "max_degree": mx.value}
+            "max_degree": mx.value, "pull_ready": bool(pr.value)}
 
 
 class BfsGraph:

@@ -45,7 +45,9 @@ struct bfs_graph {
     int grid_bu = 0;   // bottom-up launches
     uint32_t *visited = nullptr, *vis_init = nullptr, *fbm0 = nullptr, *fbm1 = nullptr;
     uint32_t *cf = nullptr;        // 3 coarse frontier maps
-    int32_t *fnb = nullptr;        // first neighbour of each vertex
+    int32_t *fnb = nullptr;        // first in-neighbour of each vertex
+    int32_t *in_row_ptr = nullptr, *in_col = nullptr;   // transpose (directed graphs)
+    int32_t can_pull = 0;          // in-edges available
     int32_t cf_sh = 0, cf_words = 0;
     Seg *q0 = nullptr, *q1 = nullptr, *t0 = nullptr, *t1 = nullptr;
     int32_t *ts0 = nullptr, *ts1 = nullptr;
@@ -90,7 +92,7 @@ hipError_t dalloc(T **p, size_t count) {
 }
 
 void free_all(bfs_graph *g) {
-    void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->cf, g->fnb, g->q0, g->q1, g->t0, g->t1,
+    void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->cf, g->fnb, g->in_row_ptr, g->in_col, g->q0, g->q1, g->t0, g->t1,
                     g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
@@ -210,6 +212,42 @@ int validate_and_classify(bfs_graph *g) {
 
 }  // namespace
 
+// In-edges for the bottom-up pass: the CSR itself when symmetric; else its
+// transpose, built on the device.  If the transpose does not fit in device
+// memory the graph stays push-only (can_pull = 0) instead of failing.
+hipError_t build_in_edges(bfs_graph *g) {
+    if (g->symmetric) {
+        g->can_pull = 1;
+        return hipSuccess;
+    }
+    const int64_t n = g->n, m = g->m;
+    int32_t *tmp = nullptr, *cnt = nullptr;
+    const int64_t tmp_n = scan_tmp_ints(n);
+    if (dalloc(&g->in_row_ptr, n + 1) != hipSuccess || dalloc(&g->in_col, m > 0 ? m : 1) != hipSuccess ||
+        dalloc(&cnt, n) != hipSuccess || dalloc(&tmp, tmp_n) != hipSuccess) {
+        (void)hipGetLastError();
+        if (g->in_row_ptr) (void)hipFree(g->in_row_ptr);
+        if (g->in_col) (void)hipFree(g->in_col);
+        if (cnt) (void)hipFree(cnt);
+        if (tmp) (void)hipFree(tmp);
+        g->in_row_ptr = g->in_col = nullptr;
+        g->can_pull = 0;
+        return hipSuccess;
+    }
+    hipError_t e = hipMemset(cnt, 0, sizeof(int32_t) * n);
+    if (e == hipSuccess && m > 0) e = launch_in_degree(g->col_idx, g->m, cnt, 0);
+    if (e == hipSuccess) e = exclusive_scan(cnt, g->in_row_ptr, n, tmp, 0);
+    // the counts become the append cursors: cnt = in_row_ptr[0, n)
+    if (e == hipSuccess)
+        e = hipMemcpy(cnt, g->in_row_ptr, sizeof(int32_t) * n, hipMemcpyDeviceToDevice);
+    if (e == hipSuccess && m > 0) e = launch_transpose_fill(g->row_ptr, g->col_idx, g->n, cnt, g->in_col, 0);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    (void)hipFree(cnt);
+    (void)hipFree(tmp);
+    if (e == hipSuccess) g->can_pull = 1;
+    return e;
+}
+
 extern "C" {
 
 const char *bfs_last_error(void) { return g_err.c_str(); }
@@ -240,11 +278,16 @@ bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *co
     int rc = validate_and_classify(g);
     if (rc == 0) rc = alloc_workspace(g);
     if (rc == 0) {
-        hipError_t e = launch_build_vis_init(row_ptr, n, g->symmetric, g->vis_init, 0);
-        if (e == hipSuccess) e = launch_build_first_nb(row_ptr, col_idx, n, g->fnb, 0);
+        hipError_t e = build_in_edges(g);
+        const int32_t *irp = g->symmetric ? row_ptr : g->in_row_ptr;
+        const int32_t *icol = g->symmetric ? col_idx : g->in_col;
+        // with in-edges at hand, vertices without any are unreachable (but for
+        // the source) and start out visited
+        if (e == hipSuccess) e = launch_build_vis_init(g->can_pull ? irp : row_ptr, n, g->can_pull, g->vis_init, 0);
+        if (e == hipSuccess && g->can_pull) e = launch_build_first_nb(irp, icol, n, g->fnb, 0);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) {
-            set_error("building the visited template and first-neighbour index failed: %s",
+            set_error("building the visited template, in-edges and first-neighbour index failed: %s",
                       hipGetErrorString(e));
             rc = BFS_EHIP;
         }
@@ -287,8 +330,8 @@ int32_t bfs_set_policy(bfs_graph *g, int32_t direction, int32_t advance, int32_t
         set_error("unknown policy (direction %d, advance %d, loop %d)", direction, advance, loop);
         return BFS_EINVAL;
     }
-    if (direction == BFS_DIR_PULL && !g->symmetric) {
-        set_error("pull-only needs a symmetric graph with sorted rows (this graph is not)");
+    if (direction == BFS_DIR_PULL && !g->can_pull) {
+        set_error("pull-only needs in-edges: a symmetric graph, or room for its transpose");
         return BFS_EINVAL;
     }
     g->pol_dir = direction;
@@ -342,6 +385,9 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.visited = g->visited;
     P.vis_init = g->vis_init;
     P.fnb = g->fnb;
+    P.in_row_ptr = g->symmetric ? g->row_ptr : g->in_row_ptr;
+    P.in_col_idx = g->symmetric ? g->col_idx : g->in_col;
+    P.can_pull = g->can_pull;
     P.fbm0 = g->fbm0;
     P.fbm1 = g->fbm1;
     P.cf = g->cf;
@@ -363,6 +409,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.st_cap = g->st_cap;
     P.symmetric = g->symmetric;
     P.col_vec = (reinterpret_cast<uintptr_t>(g->col_idx) % 16) == 0;
+    P.in_col_vec = (reinterpret_cast<uintptr_t>(P.in_col_idx) % 16) == 0;
     P.pol_dir = g->pol_dir;
     P.pol_adv = g->pol_adv;
     P.small_mode = g->pol_loop == BFS_LOOP_DEVICE;
@@ -495,7 +542,7 @@ int32_t bfs_last_run_timing(const bfs_graph *g, float *init_ms, float *level_ms,
 }
 
 int32_t bfs_graph_info(const bfs_graph *g, int64_t *m, int32_t *sorted_rows, int32_t *symmetric,
-                       int32_t *max_degree) {
+                       int32_t *max_degree, int32_t *pull_ready) {
     if (!g) {
         set_error("NULL graph handle");
         return BFS_EINVAL;
@@ -504,6 +551,7 @@ int32_t bfs_graph_info(const bfs_graph *g, int64_t *m, int32_t *sorted_rows, int
     if (sorted_rows) *sorted_rows = g->sorted;
     if (symmetric) *symmetric = g->symmetric;
     if (max_degree) *max_degree = g->max_degree;
+    if (pull_ready) *pull_ready = g->can_pull;
     return 0;
 }
 

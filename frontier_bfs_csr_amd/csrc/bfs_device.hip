@@ -625,8 +625,9 @@ __device__ __forceinline__ void td_from_bitmap(Ctx &c, uint32_t *cbm, uint32_t *
 
 // -------------------------------------------------------- bottom-up --------
 
-// Every unvisited vertex looks for a parent: its first neighbour, in CSR
-// order, that is in the frontier bitmap.  Each wavefront owns a contiguous
+// Every unvisited vertex looks for a parent: its first in-neighbour, in CSR
+// order of the in-edge lists (the graph itself when symmetric, else its
+// transpose), that is in the frontier bitmap.  Each wavefront owns a contiguous
 // range of 64-vertex words and walks it 64 words at a time: it reads their
 // visited words (one per lane), skips the fully visited ones and lists the
 // unvisited vertices in LDS, BU_GSZ at a time.  Round 0 loads the aligned
@@ -673,15 +674,15 @@ __device__ __forceinline__ bool cf_maybe(const BuLds &sh, int use_cf, int cf_sh,
 __device__ __forceinline__ void load_block8(const Params &P, bool go, int e, int lo, int hi,
                                             int (&x)[8]) {
     const int blk = e & ~7;
-    if (go && P.col_vec && blk + 8 <= P.m) {
-        const int4 a = *reinterpret_cast<const int4 *>(P.col_idx + blk);
-        const int4 b = *reinterpret_cast<const int4 *>(P.col_idx + blk + 4);
+    if (go && P.in_col_vec && blk + 8 <= P.m) {
+        const int4 a = *reinterpret_cast<const int4 *>(P.in_col_idx + blk);
+        const int4 b = *reinterpret_cast<const int4 *>(P.in_col_idx + blk + 4);
         x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
         x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
     } else {
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            x[q] = (go && blk + q >= lo && blk + q < hi) ? P.col_idx[blk + q] : -1;
+            x[q] = (go && blk + q >= lo && blk + q < hi) ? P.in_col_idx[blk + q] : -1;
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -703,9 +704,11 @@ __device__ __forceinline__ int probe_first(const BuLds &sh, const uint32_t *cbm,
     return hit;
 }
 
-// Records that listed vertex v found parent u.
+// Records that listed vertex v found parent u (d = its in-degree; the
+// frontier tally counts out-degrees, which differ on a directed graph).
 __device__ __forceinline__ void bu_found(BuCtx &c, int wbase, int v, int u, int d) {
     const Params &P = *c.P;
+    if (!P.symmetric) d = P.row_ptr[v + 1] - P.row_ptr[v];
     P.dist[v] = c.level + 1;
     if (P.parent) P.parent[v] = u;
     atomicOr(&c.sh->bu_fm[wave_id()][(v >> 6) - wbase], 1ull << (v & 63));
@@ -742,8 +745,8 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
             uint32_t w[R0];
 #pragma unroll
             for (int j = 0; j < R0; ++j) {
-                beg[j] = (v[j] >= 0) ? P.row_ptr[v[j]] : 0;
-                en[j] = (v[j] >= 0) ? P.row_ptr[v[j] + 1] : 0;
+                beg[j] = (v[j] >= 0) ? P.in_row_ptr[v[j]] : 0;
+                en[j] = (v[j] >= 0) ? P.in_row_ptr[v[j] + 1] : 0;
                 f[j] = (v[j] >= 0) ? P.fnb[v[j]] : -1;
             }
 #pragma unroll
@@ -818,7 +821,7 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
                 }
             }
 #pragma unroll
-            for (int q = 0; q < BU_U; ++q) u[q] = (e[q] >= 0) ? P.col_idx[e[q]] : -1;
+            for (int q = 0; q < BU_U; ++q) u[q] = (e[q] >= 0) ? P.in_col_idx[e[q]] : -1;
 #pragma unroll
             for (int q = 0; q < BU_U; ++q)
                 w[q] = (u[q] >= 0 && cf_maybe(sh, use_cf, cf_sh, u[q])) ? cbm[u[q] >> 5] : 0u;
@@ -855,7 +858,7 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
     for (int j = 0; j < R0; ++j) {
         const int i = j * WAVE + lane;
         const int h = (i < cnt) ? hit[i] : BU_NOHIT;
-        if (h != BU_NOHIT) bu_found(c, wbase, lst[i], P.col_idx[h], deg[i]);
+        if (h != BU_NOHIT) bu_found(c, wbase, lst[i], P.in_col_idx[h], deg[i]);
     }
 }
 
@@ -1017,7 +1020,7 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
             } else {
                 want_pull = !(fsize * P.beta < (int64_t)P.n && fsize < prev.fsize);
             }
-            const int dir = (want_pull && P.symmetric && has_bm) ? DIR_BU : DIR_TD;
+            const int dir = (want_pull && P.can_pull && has_bm) ? DIR_BU : DIR_TD;
             sh.dir = dir;
             sh.reached_before = reached_before;
             sh.edges_before = edges_before;
@@ -1030,7 +1033,7 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
             // which even that bound cannot tip the rule skip the bit writes.
             const int64_t m_left = (int64_t)P.m - edges_before - fdeg;
             const bool may_pull = (double)P.max_deg * (double)fdeg * (double)(P.alpha + 1) > (double)m_left;
-            sh.wbits = (dir == DIR_TD) && has_queue && P.symmetric && P.pol_dir == BFS_DIR_AUTO && may_pull;
+            sh.wbits = (dir == DIR_TD) && has_queue && P.can_pull && P.pol_dir == BFS_DIR_AUTO && may_pull;
             // edge-balanced unless the binned advance is forced: its tiles
             // spread even a small frontier over several workgroups and
             // bound the winners between flushes
@@ -1368,6 +1371,71 @@ hipError_t launch_check_symmetry(const int32_t *row_ptr, const int32_t *col_idx,
     return hipGetLastError();
 }
 
+// ---------------------------------------------------- in-edge transpose -----
+// A counting sort of the CSR entries by target: in-degree counts, an
+// exclusive scan into in_row_ptr, then every entry u -> v is appended to v's
+// in-list at a cursor taken with an atomic.  In-lists come out in no fixed
+// order (any in-neighbour in the frontier is a valid parent).
+
+__global__ __launch_bounds__(256) void in_degree_kernel(const int32_t *col_idx, int32_t m,
+                                                        int32_t *cnt) {
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < m; e += nth)
+        atomicAdd(&cnt[col_idx[e]], 1);
+}
+
+constexpr int SCAN_BLOCK = 256;
+constexpr int SCAN_ITEMS = 4;
+constexpr int SCAN_TILE = SCAN_BLOCK * SCAN_ITEMS;
+
+// Exclusive scan of one tile of cnt into out; the tile's total goes to sums.
+__global__ __launch_bounds__(SCAN_BLOCK) void scan_tile_kernel(const int32_t *cnt, int32_t *out,
+                                                              int64_t n, int32_t *sums) {
+    __shared__ int32_t wsum[SCAN_BLOCK / WAVE];
+    const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
+    int32_t x[SCAN_ITEMS], t = 0;
+#pragma unroll
+    for (int i = 0; i < SCAN_ITEMS; ++i) {
+        x[i] = (base + i < n) ? cnt[base + i] : 0;
+        t += x[i];
+    }
+    // exclusive prefix of the per-thread totals over the block
+    int32_t incl = t;
+    for (int d = 1; d < WAVE; d <<= 1) {
+        const int32_t y = __shfl_up(incl, (unsigned)d, WAVE);
+        if (lane_id() >= d) incl += y;
+    }
+    if (lane_id() == WAVE - 1) wsum[threadIdx.x / WAVE] = incl;
+    __syncthreads();
+    int32_t before = 0;
+    for (int w = 0; w < (int)(threadIdx.x / WAVE); ++w) before += wsum[w];
+    int32_t run = before + incl - t;
+#pragma unroll
+    for (int i = 0; i < SCAN_ITEMS; ++i) {
+        if (base + i < n) out[base + i] = run;
+        run += x[i];
+    }
+    if (threadIdx.x == SCAN_BLOCK - 1) sums[blockIdx.x] = run;
+}
+
+__global__ __launch_bounds__(SCAN_BLOCK) void scan_add_kernel(int32_t *out, int64_t n,
+                                                             const int32_t *offs) {
+    const int64_t base = (int64_t)blockIdx.x * SCAN_TILE;
+    for (int i = threadIdx.x; i < SCAN_TILE; i += SCAN_BLOCK)
+        if (base + i < n) out[base + i] += offs[blockIdx.x];
+}
+
+// Every entry u -> v appended to v's in-list.
+__global__ __launch_bounds__(256) void transpose_fill_kernel(const int32_t *row_ptr,
+                                                             const int32_t *col_idx, int32_t n,
+                                                             int32_t *cursor, int32_t *in_col) {
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n; u += nth) {
+        const int32_t b = row_ptr[u], e = row_ptr[u + 1];
+        for (int32_t j = b; j < e; ++j) in_col[atomicAdd(&cursor[col_idx[j]], 1)] = (int32_t)u;
+    }
+}
+
 __global__ __launch_bounds__(256) void first_nb_kernel(const int32_t *row_ptr,
                                                        const int32_t *col_idx, int32_t n,
                                                        int32_t *fnb) {
@@ -1382,6 +1450,50 @@ hipError_t launch_build_first_nb(const int32_t *row_ptr, const int32_t *col_idx,
                                  int32_t *fnb, hipStream_t s) {
     hipLaunchKernelGGL(first_nb_kernel, dim3(grid_for(n, 256 * 4)), dim3(256), 0, s, row_ptr,
                        col_idx, n, fnb);
+    return hipGetLastError();
+}
+
+hipError_t launch_in_degree(const int32_t *col_idx, int32_t m, int32_t *cnt, hipStream_t s) {
+    hipLaunchKernelGGL(in_degree_kernel, dim3(grid_for(m, 256 * 4)), dim3(256), 0, s, col_idx, m, cnt);
+    return hipGetLastError();
+}
+
+int64_t scan_tmp_ints(int64_t n) {
+    int64_t total = 0;
+    for (int64_t len = n; len > 1;) {
+        const int64_t tiles = (len + SCAN_TILE - 1) / SCAN_TILE;
+        total += 2 * tiles + 1;   // tile sums and their scan (plus the grand total)
+        len = tiles;
+    }
+    return total + 1;
+}
+
+hipError_t exclusive_scan(const int32_t *cnt, int32_t *out, int64_t n, int32_t *tmp, hipStream_t s) {
+    // out[0, n) = exclusive prefix; out[n] = total.  Tiles of SCAN_TILE are
+    // scanned alone, their totals are scanned the same way (recursively), and
+    // the scanned totals are added back.
+    if (n <= 0) {
+        return hipMemsetAsync(out, 0, sizeof(int32_t), s);
+    }
+    const int64_t tiles = (n + SCAN_TILE - 1) / SCAN_TILE;
+    if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+    int32_t *sums = tmp, *offs = tmp + tiles;
+    hipLaunchKernelGGL(scan_tile_kernel, dim3((unsigned)tiles), dim3(SCAN_BLOCK), 0, s, cnt, out, n, sums);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (tiles == 1) return hipMemcpyAsync(out + n, sums, sizeof(int32_t), hipMemcpyDeviceToDevice, s);
+    e = exclusive_scan(sums, offs, tiles, tmp + 2 * tiles + 1, s);   // offs[tiles] = total
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)tiles), dim3(SCAN_BLOCK), 0, s, out, n, offs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return hipMemcpyAsync(out + n, offs + tiles, sizeof(int32_t), hipMemcpyDeviceToDevice, s);
+}
+
+hipError_t launch_transpose_fill(const int32_t *row_ptr, const int32_t *col_idx, int32_t n,
+                                 int32_t *cursor, int32_t *in_col, hipStream_t s) {
+    hipLaunchKernelGGL(transpose_fill_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, row_ptr,
+                       col_idx, n, cursor, in_col);
     return hipGetLastError();
 }
 

@@ -108,7 +108,11 @@ struct Params {
     int32_t *level_sizes;     // may be null
     uint32_t *visited;        // 2*nwp words
     const uint32_t *vis_init; // 2*nwp words: isolated vertices (symmetric graphs) + padding
-    const int32_t *fnb;       // n entries: first CSR neighbour of each vertex, -1 if none
+    // in-edges, read by the bottom-up pass: the CSR itself when it is
+    // symmetric, else its transpose built at graph creation
+    const int32_t *in_row_ptr;
+    const int32_t *in_col_idx;
+    const int32_t *fnb;       // n entries: first in-neighbour of each vertex, -1 if none
     uint32_t *fbm0, *fbm1;    // frontier bitmaps, 2*nwp words each
     Seg *q0, *q1;             // STRIPES regions of qcap segments (small from the front,
                               // mid from the back)
@@ -122,6 +126,8 @@ struct Params {
     int32_t st_cap;
     int32_t symmetric;
     int32_t col_vec;          // col_idx is 16-byte aligned: 16-byte loads allowed
+    int32_t in_col_vec;       // the same for in_col_idx
+    int32_t can_pull;         // in-edges are available (symmetric, or transpose built)
     int32_t pol_dir;          // BFS_DIR_*
     int32_t pol_adv;          // BFS_ADV_*
     int32_t small_mode;       // allow the small-frontier mode
@@ -160,5 +166,12 @@ hipError_t launch_build_vis_init(const int32_t *row_ptr, int32_t n, int32_t mark
                                  uint32_t *vis_init, hipStream_t s);
 hipError_t launch_build_first_nb(const int32_t *row_ptr, const int32_t *col_idx, int32_t n,
                                  int32_t *fnb, hipStream_t s);
+// transpose (in-edge CSR) of a CSR: in-degree counts, exclusive scan, scatter
+hipError_t launch_in_degree(const int32_t *col_idx, int32_t m, int32_t *cnt, hipStream_t s);
+// exclusive scan of cnt[0, n) into out[0, n]; tmp holds scan_tmp_ints(n) ints
+int64_t scan_tmp_ints(int64_t n);
+hipError_t exclusive_scan(const int32_t *cnt, int32_t *out, int64_t n, int32_t *tmp, hipStream_t s);
+hipError_t launch_transpose_fill(const int32_t *row_ptr, const int32_t *col_idx, int32_t n,
+                                 int32_t *cursor, int32_t *in_col, hipStream_t s);
 
 }  // namespace fbfs

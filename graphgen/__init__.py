@@ -296,6 +296,29 @@ def rmat(scale, edge_factor=16, seed=5, perm_seed=None, nsrc=64, src_seed=None):
                  {"scale": scale, "edge_factor": edge_factor, "seed": seed})
 
 
+def rmat_directed(scale, edge_factor=16, seed=6, nsrc=64, src_seed=None):
+    """Directed R-MAT graph at `scale`: the same edge generator and relabelling
+    as ``rmat`` without the symmetric closure; self-loops and duplicate edges
+    removed, rows sorted.  Sources have out-degree >= 1."""
+    lib = _load()
+    n = 1 << scale
+    E = edge_factor * n
+    perm = np.empty(n, dtype=np.int32)
+    lib.gen_permutation(n, ctypes.c_uint64(seed + 1000), _p(perm))
+    src = np.empty(E, dtype=np.int32)
+    dst = np.empty(E, dtype=np.int32)
+    a, b, c, _ = RMAT_ABCD
+    lib.gen_rmat_edges(scale, E, a, b, c, ctypes.c_uint64(seed), _p(perm), _p(src), _p(dst))
+    del perm
+    keep = src != dst
+    key = np.unique(src[keep].astype(np.int64) * n + dst[keep])
+    del src, dst, keep
+    row_ptr, col = csr_from_directed_edges(n, key // n, key % n)
+    srcs = pick_sources(row_ptr, nsrc, src_seed if src_seed is not None else seed + 100)
+    return Graph(f"rmat{scale}_ef{edge_factor}_directed", row_ptr, col, False, srcs,
+                 {"scale": scale, "edge_factor": edge_factor, "seed": seed})
+
+
 def erdos_renyi(n=4_194_304, pairs_per_vertex=8, seed=3, nsrc=64):
     """Undirected uniform random graph: n*pairs_per_vertex uniform pairs,
     symmetrised and deduplicated (mean degree ~ 2*pairs_per_vertex)."""

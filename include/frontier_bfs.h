@@ -51,8 +51,10 @@ typedef struct bfs_graph bfs_graph;   /* opaque handle */
  *   col_idx  device, m entries, each in [0, n) (may be NULL when m = 0)
  * The arrays are validated on the device (the first bad index is named in
  * bfs_last_error), and the graph is classified: rows sorted or not, and
- * symmetric or not.  The bottom-up (pull) pass is enabled only on symmetric
- * graphs, because pulling needs in-edges (Gunrock reading guide, question 3).
+ * symmetric or not.  The bottom-up (pull) pass needs in-edges (Gunrock reading
+ * guide, question 3): a symmetric graph serves as its own; for any other
+ * graph the transpose is built here on the device (a counting sort by target,
+ * m + n + 1 more ints), and if it does not fit the graph stays push-only.
  * Returns NULL on invalid input or allocation failure.  Uses the current
  * device and the null stream; synchronises before returning.
  */
@@ -85,7 +87,7 @@ const char *bfs_last_error(void);
 /* ---- measurement and test hooks (results never depend on them) --------- */
 
 /* Direction policy: automatic switching, push (top-down) only, pull
- * (bottom-up) only.  Pull needs a symmetric graph. */
+ * (bottom-up) only.  Pull needs in-edges (see bfs_graph_create). */
 #define BFS_DIR_AUTO 0
 #define BFS_DIR_PUSH 1
 #define BFS_DIR_PULL 2
@@ -119,8 +121,8 @@ const char *bfs_last_error(void);
 /*
  * Forces a policy for later bfs_run calls on this handle.  dist, L and the
  * level sizes are the same under every policy; only speed differs.
- * Returns 0, or BFS_EINVAL (unknown value, or pull on a graph that is not
- * symmetric).
+ * Returns 0, or BFS_EINVAL (unknown value, or pull on a graph without
+ * in-edges: see bfs_graph_create).
  */
 int32_t bfs_set_policy(bfs_graph *g, int32_t direction, int32_t advance, int32_t loop);
 
@@ -178,11 +180,13 @@ int32_t bfs_last_run_kernel_timing(const bfs_graph *g, float *td_ms, int32_t *td
 
 /*
  * Graph facts found by bfs_graph_create (host memory, any may be NULL):
- * CSR entry count, rows-sorted flag, symmetric flag, maximum degree.
- * Returns 0 or BFS_EINVAL.
+ * CSR entry count, rows-sorted flag, symmetric flag, maximum degree, and
+ * whether the bottom-up (pull) pass is available: always on a symmetric
+ * graph, and on any other graph once its transpose (the in-edges) was built,
+ * which fails only when device memory runs short.  Returns 0 or BFS_EINVAL.
  */
 int32_t bfs_graph_info(const bfs_graph *g, int64_t *m, int32_t *sorted_rows,
-                       int32_t *symmetric, int32_t *max_degree);
+                       int32_t *symmetric, int32_t *max_degree, int32_t *pull_ready);
 
 #ifdef __cplusplus
 }

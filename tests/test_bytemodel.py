@@ -33,3 +33,19 @@ def test_isolated_vertices_not_counted_in_bottom_up():
     dist = np.array([0, 1, 1, 2, -1], np.int32)
     _, lv = bytemodel.alg_bytes(g.row_ptr, g.col_idx, dist, np.ones(3, np.int8))
     assert lv.tolist() == [2 + 24 + 12 + 16, 2 + 8 + 4 + 8, 2]
+
+
+def test_bottomup_directed_uses_in_edges():
+    """P5's directed graph pulled over its in-edges: in-lists 1:[0] 2:[0,1]
+    3:[1,2] 4:[2,3] 5:[3,4], counted by hand."""
+    g = gg.chapter22_graph()
+    dist = np.array([0, 1, 1, 2, 2, 3], np.int32)
+    in_csr = bytemodel.transpose(g.row_ptr, g.col_idx)
+    assert in_csr[0].tolist() == [0, 0, 1, 3, 5, 7, 9]
+    assert in_csr[1].tolist() == [0, 0, 1, 1, 2, 2, 3, 3, 4]
+    _, lv = bytemodel.alg_bytes(g.row_ptr, g.col_idx, dist, np.ones(4, np.int8), in_csr=in_csr)
+    # level 0: U={1..5} 40, scans 1+1+2+2+2 = 8 entries 32, 2 found 16, bitmaps 2
+    # level 1: U={3,4,5} 24, scans 1+1+2 16, 2 found 16, bitmaps 2
+    # level 2: U={5} 8, scan 1 entry 4, 1 found 8, bitmaps 2
+    assert lv.tolist() == [90, 58, 22, 2]
+

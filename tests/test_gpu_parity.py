@@ -43,6 +43,14 @@ def test_directed_random():
         check_graph(gg.random_directed(n, deg, seed))
 
 
+@pytest.mark.parametrize("scale", [12, 16])
+def test_directed_rmat(scale):
+    """Directed R-MAT (no symmetrisation): pull and direction switching run on
+    in-edges from the transpose built at graph creation."""
+    g = gg.rmat_directed(scale, 16, seed=40 + scale, nsrc=3)
+    check_graph(g)
+
+
 @pytest.mark.parametrize("scale", [10, 14, 17])
 def test_rmat_scaled(scale):
     g = gg.rmat(scale, 16, seed=100 + scale, nsrc=3)
@@ -193,8 +201,12 @@ def test_run_argument_errors():
             assert ei.value.code == fb.BFS_EINVAL
         assert (d.cpu().numpy() == 9).all()   # untouched on EINVAL
         with pytest.raises(fb.BfsError):
-            bg.set_policy(fb.DIR_PULL)         # directed graph: no pull
-        assert not bg.info()["symmetric"]
+            bg.set_policy(7)                   # unknown direction
+        with pytest.raises(fb.BfsError):
+            bg.set_switch(0, 24)               # alpha outside [1, 1e6]
+        info = bg.info()
+        assert not info["symmetric"] and info["pull_ready"]   # directed: pull via the transpose
+        bg.set_policy(fb.DIR_PULL)
 
 
 def test_unaligned_col_idx():

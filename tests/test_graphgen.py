@@ -86,3 +86,21 @@ def test_tiny_random_variety():
         kinds.add(("directed" if g.meta["directed"] else "sym",
                    bool((rows == g.col_idx).any())))
     assert len(kinds) == 4
+
+
+def test_rmat_directed_clean():
+    """Directed R-MAT: deterministic, no self-loops, no duplicate entries,
+    sorted rows, not symmetric; sources have out-degree >= 1."""
+    g1 = gg.rmat_directed(10, 16, seed=9, nsrc=4)
+    g2 = gg.rmat_directed(10, 16, seed=9, nsrc=4)
+    assert (g1.row_ptr == g2.row_ptr).all() and (g1.col_idx == g2.col_idx).all()
+    assert not g1.symmetric
+    rows = np.repeat(np.arange(g1.n), np.diff(g1.row_ptr))
+    assert (rows != g1.col_idx).all()
+    for u in range(g1.n):
+        r = g1.col_idx[g1.row_ptr[u]:g1.row_ptr[u + 1]]
+        assert (np.diff(r) > 0).all()
+    fwd = set(zip(rows.tolist(), g1.col_idx.tolist()))
+    assert any((v, u) not in fwd for u, v in fwd)
+    assert (np.diff(g1.row_ptr)[g1.sources] >= 1).all()
+
