@@ -10,7 +10,9 @@ a serial FIFO-queue BFS as in the sequential baseline of "Chapter 22: The
 Frontier Model for Parallel Breadth-First Search" (section 22.1) and
 ``bfsCpu`` of the Day 38 program (bfs.cu), plus a checker that applies the
 gates of that program's ``main`` (exact dist, level count, frontier sizes
-summing to the reached count) and the BFS-parent and edge invariants.
+summing to the reached count) and the BFS-parent and edge invariants, and
+the neighbour-walk checksum that the Day 38 page's isolated level walk checks
+its kernels against.
 """
 from __future__ import annotations
 
@@ -89,6 +91,8 @@ def _load():
         lib.oracle_check.argtypes = [i32, P, P, i32, P, i32, P, P, P, i32, P, i32,
                                      ctypes.POINTER(i64)]
         lib.oracle_check.restype = i32
+        lib.oracle_walk_checksum.argtypes = [i32, P, P, i32, P, i32, P]
+        lib.oracle_walk_checksum.restype = i32
         _lib = lib
     return _lib
 
@@ -138,6 +142,22 @@ def bfs_many(row_ptr, col_idx, sources):
     if rc != 0:
         raise ValueError(f"oracle_bfs_many failed with {rc}")
     return levels, reached
+
+
+def walk_checksum(row_ptr, col_idx, vertices, repeats=64):
+    """Per-vertex neighbour-walk checksums (uint32) of the listed vertices:
+    the wrapping sum over repeats r and CSR entries of (neighbour XOR r), as
+    the Day 38 page's isolated level walk defines it."""
+    lib = _load()
+    row_ptr, col_idx = _i32(row_ptr), _i32(col_idx)
+    n = row_ptr.shape[0] - 1
+    v = _i32(vertices)
+    out = np.empty(v.shape[0], np.uint32)
+    rc = lib.oracle_walk_checksum(n, _ptr(row_ptr), _ptr(col_idx), v.shape[0], _ptr(v), int(repeats),
+                                  _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_walk_checksum failed with {rc}")
+    return out
 
 
 def check(row_ptr, col_idx, source, ref, dist, parent=None, L=None, sizes=None,

@@ -42,6 +42,8 @@
  *   3 parent[v] = v                       4 L one short
  *   5 neighbours scanned in reverse       6 checker skips the adjacency test
  *   7 checker skips the last vertex's dist
+ *   8 walk adds (c + r) instead of (c ^ r)  9 walk starts at r = 1
+ *  10 walk sums entry indices, not neighbour ids
  */
 #ifndef ORACLE_MUTANT
 #define ORACLE_MUTANT 0
@@ -273,3 +275,39 @@ int32_t oracle_check(int32_t n, const int32_t *row_ptr, const int32_t *col_idx,
     }
     return CHK_OK;
 }
+
+/*
+ * Neighbour-walk checksum of one level ("Day 38 - Graph traversal on a GPU",
+ * "Measuring the mapping without measuring the launch"): for every listed
+ * vertex u, the wrapping unsigned 32-bit sum over repeats r = 0 .. repeats-1
+ * and over u's CSR entries of (neighbour id XOR r).  Unsigned arithmetic wraps
+ * by definition, so every correct walk returns the same value whatever order
+ * it adds in.  Returns 0, or -1 on bad arguments.
+ */
+int32_t oracle_walk_checksum(int32_t n, const int32_t *row_ptr, const int32_t *col_idx,
+                             int32_t count, const int32_t *vertices, int32_t repeats,
+                             uint32_t *out)
+{
+    if (n < 0 || count < 0 || repeats < 0 || (count > 0 && (!vertices || !out))) return -1;
+    for (int32_t i = 0; i < count; ++i) {
+        const int32_t u = vertices[i];
+        if (u < 0 || u >= n) return -1;
+        uint32_t acc = 0u;
+#if ORACLE_MUTANT == 9
+        for (int32_t r = 1; r < repeats; ++r)
+#else
+        for (int32_t r = 0; r < repeats; ++r)
+#endif
+            for (int32_t e = row_ptr[u]; e < row_ptr[u + 1]; ++e)
+#if ORACLE_MUTANT == 8
+                acc += (uint32_t)col_idx[e] + (uint32_t)r;
+#elif ORACLE_MUTANT == 10
+                acc += (uint32_t)e ^ (uint32_t)r;
+#else
+                acc += (uint32_t)col_idx[e] ^ (uint32_t)r;
+#endif
+        out[i] = acc;
+    }
+    return 0;
+}
+

@@ -222,8 +222,41 @@ def pin_checker_rejects():
     return None
 
 
+def pin_walk_checksum():
+    """The neighbour-walk checksum against closed forms of the XOR sum:
+    sum_{r<R} (c ^ r) = R*c + R(R-1)/2 when c has no bit below R set, and
+    R*c - R(R-1)/2 when c has every bit below R set (R a power of two), all
+    mod 2**32; a vertex's checksum is the sum over its entries; degree 0
+    gives 0; the listed order is kept."""
+    R = 64
+    n = 1 << 20
+    c_hi = 1024                 # bits above R only
+    c_lo = (1 << 20) - 1        # every bit below R set (and more)
+    adj = {0: [0], 1: [c_hi], 2: [c_lo], 3: [c_hi, c_lo, 0], 4: []}
+    row_ptr = np.zeros(n + 1, np.int32)
+    col = []
+    for u in range(n):
+        col += adj.get(u, [])
+        row_ptr[u + 1] = len(col)
+    col = np.array(col, np.int32)
+    tri = R * (R - 1) // 2
+    f = {0: tri, c_hi: R * c_hi + tri, c_lo: R * c_lo - tri}
+    want = {u: sum(f[c] for c in cs) % 2**32 for u, cs in adj.items()}
+    order = [3, 0, 4, 2, 1]
+    got = oracle.walk_checksum(row_ptr, col, order, R)
+    if got.tolist() != [want[u] for u in order]:
+        return f"walk checksum {got.tolist()} != {[want[u] for u in order]}"
+    # wrap-around: 2**13 repeats of c_lo exceed 2**32 before the reduction
+    R2 = 1 << 13
+    got2 = int(oracle.walk_checksum(row_ptr, col, [2], R2)[0])
+    want2 = (R2 * c_lo - R2 * (R2 - 1) // 2) % 2**32
+    if got2 != want2:
+        return f"walk checksum with wrap {got2} != {want2}"
+    return None
+
+
 ALL_PINS = [pin_chapter22_bfs, pin_chapter22_partial_states, pin_pmpp_graph,
-            pin_tiny_random, pin_closed_forms, pin_checker_rejects]
+            pin_tiny_random, pin_closed_forms, pin_checker_rejects, pin_walk_checksum]
 
 
 def failing_pins(tiny_count=300):
