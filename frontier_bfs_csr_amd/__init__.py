@@ -22,10 +22,11 @@ BFS_EINVAL, BFS_EHIP, BFS_ENOMEM, BFS_EDEVICE = -1, -2, -3, -4
 DIR_AUTO, DIR_PUSH, DIR_PULL = 0, 1, 2
 ADV_AUTO, ADV_BINNED, ADV_EDGE = 0, 1, 2
 LOOP_DEVICE, LOOP_HOST, LOOP_CHAIN = 0, 1, 2
+WALK_LANE, WALK_WAVE, WALK_BINNED, WALK_MERGE = 0, 1, 2, 3
 
 EXPORTS = ("bfs_graph_create", "bfs_run", "bfs_graph_destroy", "bfs_last_error",
            "bfs_set_policy", "bfs_last_run_stats", "bfs_set_timing", "bfs_last_run_timing",
-           "bfs_graph_info", "bfs_set_switch", "bfs_last_run_kernel_timing")
+           "bfs_graph_info", "bfs_set_switch", "bfs_last_run_kernel_timing", "bfs_walk_level")
 
 _lib = None
 
@@ -70,6 +71,8 @@ def load():
         lib.bfs_last_run_kernel_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32),
                                                    ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
         lib.bfs_last_run_kernel_timing.restype = i32
+        lib.bfs_walk_level.argtypes = [P, P, i32, i32, i32, P, P]
+        lib.bfs_walk_level.restype = i32
         _lib = lib
     return _lib
 
@@ -133,6 +136,17 @@ def bfs_set_policy(g, direction=DIR_AUTO, advance=ADV_AUTO, loop=LOOP_DEVICE):
 
 def bfs_set_switch(g, alpha=28, beta=24):
     rc = load().bfs_set_switch(g, int(alpha), int(beta))
+    if rc < 0:
+        raise BfsError(rc, bfs_last_error())
+
+
+def bfs_walk_level(g, vertices, out, mapping=WALK_WAVE, repeats=64, stream=None):
+    """Isolated neighbour walk of the listed vertices (int32 CUDA tensor) into
+    out (int32 CUDA tensor of the same length; its bits are the uint32 sums)."""
+    count = vertices.numel() if vertices is not None else 0
+    v = _dev_i32(vertices, "vertices")
+    o = _dev_i32(out, "out", count)
+    rc = load().bfs_walk_level(g, v, count, int(mapping), int(repeats), o, _stream_handle(stream))
     if rc < 0:
         raise BfsError(rc, bfs_last_error())
 
@@ -203,6 +217,9 @@ class BfsGraph:
 
     def set_policy(self, direction=DIR_AUTO, advance=ADV_AUTO, loop=LOOP_DEVICE):
         bfs_set_policy(self.handle, direction, advance, loop)
+
+    def walk(self, vertices, out, mapping=WALK_WAVE, repeats=64, stream=None):
+        bfs_walk_level(self.handle, vertices, out, mapping, repeats, stream)
 
     def set_switch(self, alpha=28, beta=24):
         bfs_set_switch(self.handle, alpha, beta)

@@ -491,6 +491,70 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     }
 }
 
+int32_t bfs_walk_level(bfs_graph *g, const int32_t *vertices, int32_t count, int32_t mapping,
+                       int32_t repeats, uint32_t *out, hipStream_t stream) {
+    g_err.clear();
+    if (!g) {
+        set_error("NULL graph handle");
+        return BFS_EINVAL;
+    }
+    if (count < 0 || repeats < 0) {
+        set_error("count (%d) and repeats (%d) must not be negative", count, repeats);
+        return BFS_EINVAL;
+    }
+    if (mapping < BFS_WALK_LANE || mapping > BFS_WALK_MERGE) {
+        set_error("unknown walk mapping %d", mapping);
+        return BFS_EINVAL;
+    }
+    if (count > 0 && (!vertices || !out)) {
+        set_error("vertices and out must be device pointers");
+        return BFS_EINVAL;
+    }
+    // the merge mapping's scratch lives in the first frontier queue
+    // (STRIPES * qcap segments of 16 bytes)
+    const int64_t scratch_ints = (int64_t)STRIPES * g->qcap * (int64_t)(sizeof(Seg) / sizeof(int32_t));
+    if ((int64_t)count > 8 * (int64_t)g->n || walk_scratch_ints(count) > scratch_ints) {
+        set_error("count %d is above the walk's limit of 8n = %lld", count, 8LL * g->n);
+        return BFS_EINVAL;
+    }
+    HIP_TRY(hipSetDevice(g->device), BFS_EHIP);
+    Params P;
+    std::memset(&P, 0, sizeof(P));
+    P.row_ptr = g->row_ptr;
+    P.col_idx = g->col_idx;
+    P.n = g->n;
+    P.m = g->m;
+    int32_t *bad = &g->ctl->err;
+    const bool timing = g->timing != 0;
+    g->last_timed = 0;
+    HIP_TRY(hipMemsetAsync(bad, 0, sizeof(int32_t), stream), BFS_EHIP);
+    if (timing) {
+        HIP_TRY(ensure_events(g, 2), BFS_EHIP);
+        HIP_TRY(hipEventRecord(g->events[0], stream), BFS_EHIP);
+    }
+    HIP_TRY(launch_walk(P, vertices, count, mapping, repeats, out, reinterpret_cast<int32_t *>(g->q0), bad,
+                        g->grid, stream),
+            BFS_EHIP);
+    if (timing) HIP_TRY(hipEventRecord(g->events[1], stream), BFS_EHIP);
+    HIP_TRY(hipMemcpyAsync(g->host_ctl, g->ctl, sizeof(HostCtl), hipMemcpyDeviceToHost, stream), BFS_EHIP);
+    HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+    if (g->host_ctl->err) {
+        set_error("a listed vertex is outside [0, %d)", g->n);
+        return BFS_EINVAL;
+    }
+    if (timing) {
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, g->events[0], g->events[1]), BFS_EHIP);
+        g->last_init_ms = 0.f;
+        g->last_level_ms = ms;
+        g->last_launches = 1;
+        g->last_kind_ms[0] = g->last_kind_ms[1] = 0.f;
+        g->last_kind_launches[0] = g->last_kind_launches[1] = 0;
+        g->last_timed = 1;
+    }
+    return 0;
+}
+
 int32_t bfs_last_run_stats(const bfs_graph *g, int32_t cap, int8_t *dir, int64_t *frontier_edges) {
     if (!g || cap < 0) {
         set_error("NULL graph handle or negative capacity");

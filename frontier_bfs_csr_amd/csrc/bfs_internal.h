@@ -174,4 +174,14 @@ hipError_t exclusive_scan(const int32_t *cnt, int32_t *out, int64_t n, int32_t *
 hipError_t launch_transpose_fill(const int32_t *row_ptr, const int32_t *col_idx, int32_t n,
                                  int32_t *cursor, int32_t *in_col, hipStream_t s);
 
+// isolated neighbour walk of listed vertices (bfs_walk.hip); scratch holds
+// walk_scratch_ints(count) ints, bad is raised for ids outside [0, n)
+int64_t walk_scratch_ints(int64_t count);
+#ifndef WALK_MERGE_K
+#define WALK_MERGE_K 4   // longest run of entries per lane in the merge walk
+#endif
+hipError_t launch_walk(const Params &P, const int32_t *vs, int32_t count, int32_t mapping,
+                       int32_t repeats, uint32_t *out, int32_t *scratch, int32_t *bad,
+                       int lanes_grid, hipStream_t s);
+
 }  // namespace fbfs

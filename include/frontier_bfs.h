@@ -179,6 +179,34 @@ int32_t bfs_last_run_kernel_timing(const bfs_graph *g, float *td_ms, int32_t *td
                                    float *bu_ms, int32_t *bu_launches);
 
 /*
+ * Isolated neighbour walk of one level: the measurement the "Day 38 - Graph
+ * traversal on a GPU" page uses to compare thread-to-work mappings without
+ * the atomics, frontier build and distance writes of a real level (section
+ * "Measuring the mapping without measuring the launch").  For listed vertex i
+ * (vertices[i], device, count entries, each in [0, n)) out[i] (device, count
+ * entries) becomes the wrapping unsigned 32-bit sum over r = 0 .. repeats-1
+ * and over the vertex's CSR entries of (neighbour id XOR r).  mapping is one
+ * of BFS_WALK_*: one lane per list; one 64-lane wavefront per list; degree
+ * bins over the whole level (a lane per list under 32 entries, a wavefront
+ * per list under 512, a workgroup per longer list); or the edge-balanced
+ * split, where an exclusive scan of the listed degrees gives every lane an
+ * equal short run of entries and the owner of its first entry by binary
+ * search (Gunrock reading guide, steps 4 and 5).  Uses the handle's
+ * workspace, so it must not overlap a bfs_run on the same handle; runs on
+ * stream and returns after the work finished.  With the timing hook on,
+ * bfs_last_run_timing reports the walk's kernels as level_ms.  Returns 0;
+ * BFS_EINVAL for a NULL handle or buffer, negative count or repeats, an
+ * unknown mapping, count above 8n, or a listed id outside [0, n) (then out is
+ * unspecified); BFS_EHIP if a HIP call fails.
+ */
+#define BFS_WALK_LANE   0
+#define BFS_WALK_WAVE   1
+#define BFS_WALK_BINNED 2
+#define BFS_WALK_MERGE  3
+int32_t bfs_walk_level(bfs_graph *g, const int32_t *vertices, int32_t count, int32_t mapping,
+                       int32_t repeats, uint32_t *out, hipStream_t stream);
+
+/*
  * Graph facts found by bfs_graph_create (host memory, any may be NULL):
  * CSR entry count, rows-sorted flag, symmetric flag, maximum degree, and
  * whether the bottom-up (pull) pass is available: always on a symmetric
