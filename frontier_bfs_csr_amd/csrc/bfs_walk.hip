@@ -41,12 +41,16 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
     return x;
 }
 
-// The walk of one list piece [b, e) for every repeat, from one lane.
+// The walk of one list piece [b, e) for every repeat, from one lane.  The
+// entry loop is unrolled by four so that a lane keeps four loads in flight
+// (rolled, it waits out each load's latency before issuing the next).
 __device__ __forceinline__ uint32_t walk_run(const int32_t *col_idx, int b, int e, int stride,
                                              int repeats) {
     uint32_t acc = 0u;
-    for (int r = 0; r < repeats; ++r)
+    for (int r = 0; r < repeats; ++r) {
+#pragma unroll 4
         for (int j = b; j < e; j += stride) acc += (uint32_t)col_idx[j] ^ (uint32_t)r;
+    }
     return acc;
 }
 
