@@ -727,10 +727,11 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
     int32_t *lst = sh.bu_lst[wv], *deg = sh.bu_deg[wv], *hit = sh.bu_hit[wv];
     int32_t *pi = sh.bu_pi[wv], *pn = sh.bu_pn[wv], *pe = sh.bu_pe[wv], *ps = sh.bu_ps[wv];
     constexpr int R0 = BU_GSZ / WAVE;   // listed vertices per lane in round 0
-    // round 0: every listed vertex's first neighbour, from the first-neighbour
-    // index (read in vertex order beside row_ptr, so no scattered adjacency
-    // line is fetched for the vertices that stop there); R0 vertices per lane
-    // with their loads overlapped; a hit is recorded at once
+    // round 0: every listed vertex's probe neighbour (its in-neighbour of
+    // highest out-degree), from the probe-neighbour index read in vertex
+    // order beside row_ptr, so no scattered adjacency line is fetched for the
+    // vertices that stop there; R0 vertices per lane with their loads
+    // overlapped; a hit is recorded at once
     int npend = 0;
     {
         int v[R0], beg[R0], en[R0], par[R0];
@@ -747,7 +748,7 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
             for (int j = 0; j < R0; ++j) {
                 beg[j] = (v[j] >= 0) ? P.in_row_ptr[v[j]] : 0;
                 en[j] = (v[j] >= 0) ? P.in_row_ptr[v[j] + 1] : 0;
-                f[j] = (v[j] >= 0) ? P.fnb[v[j]] : -1;
+                f[j] = (v[j] >= 0) ? P.pnb[v[j]] : -1;
             }
 #pragma unroll
             for (int j = 0; j < R0; ++j)
@@ -756,14 +757,15 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
             for (int j = 0; j < R0; ++j) par[j] = (f[j] >= 0 && ((w[j] >> (f[j] & 31)) & 1u)) ? f[j] : -1;
         }
         // ... then the aligned 8-entry block holding the first entry (two
-        // 16-byte loads), for the vertices still searching with more entries
+        // 16-byte loads), for the vertices still searching with more than
+        // one entry (the probe neighbour may sit in the block: probed twice)
         bool more = false;
 #pragma unroll
-        for (int j = 0; j < R0; ++j) more |= par[j] < 0 && beg[j] + 1 < min((beg[j] | 7) + 1, en[j]);
+        for (int j = 0; j < R0; ++j) more |= par[j] < 0 && beg[j] + 1 < en[j];
         if (__ballot(more)) {
 #pragma unroll
             for (int j = 0; j < R0; ++j)
-                load_block8(P, par[j] < 0 && beg[j] + 1 < en[j], beg[j], beg[j] + 1, en[j], x[j]);
+                load_block8(P, par[j] < 0 && beg[j] + 1 < en[j], beg[j], beg[j], en[j], x[j]);
 #pragma unroll
             for (int j = 0; j < R0; ++j)
                 if (par[j] < 0) par[j] = probe_first(sh, cbm, use_cf, cf_sh, x[j]);
@@ -1436,20 +1438,42 @@ __global__ __launch_bounds__(256) void transpose_fill_kernel(const int32_t *row_
     }
 }
 
-__global__ __launch_bounds__(256) void first_nb_kernel(const int32_t *row_ptr,
-                                                       const int32_t *col_idx, int32_t n,
-                                                       int32_t *fnb) {
-    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n; v += nth) {
-        const int32_t b = row_ptr[v];
-        fnb[v] = (b < row_ptr[v + 1]) ? col_idx[b] : -1;
+// Probe-neighbour index: for every vertex v the in-neighbour of highest
+// out-degree (the first in CSR order among equals), -1 without in-neighbours.
+// Hubs are reached in the first levels, so this is the in-neighbour most
+// likely to be in a bottom-up level's frontier.  One wavefront per vertex.
+__global__ __launch_bounds__(256) void probe_nb_kernel(const int32_t *row_ptr, const int32_t *in_row_ptr,
+                                                       const int32_t *in_col, int32_t n, int32_t *pnb) {
+    const int lane = lane_id();
+    const int64_t nw = (int64_t)gridDim.x * (blockDim.x / WAVE);
+    for (int64_t v = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE; v < n; v += nw) {
+        const int b = in_row_ptr[v], e = in_row_ptr[v + 1];
+        int best_d = -1, best_j = 0x7fffffff;
+        for (int j = b + lane; j < e; j += WAVE) {
+            const int u = in_col[j];
+            const int d = row_ptr[u + 1] - row_ptr[u];
+            if (d > best_d) {   // a lane's entries rise, so the first among equals stays
+                best_d = d;
+                best_j = j;
+            }
+        }
+#pragma unroll
+        for (int off = WAVE / 2; off > 0; off >>= 1) {
+            const int od = __shfl_xor(best_d, off, WAVE);
+            const int oj = __shfl_xor(best_j, off, WAVE);
+            if (od > best_d || (od == best_d && oj < best_j)) {
+                best_d = od;
+                best_j = oj;
+            }
+        }
+        if (lane == 0) pnb[v] = best_d >= 0 ? in_col[best_j] : -1;
     }
 }
 
-hipError_t launch_build_first_nb(const int32_t *row_ptr, const int32_t *col_idx, int32_t n,
-                                 int32_t *fnb, hipStream_t s) {
-    hipLaunchKernelGGL(first_nb_kernel, dim3(grid_for(n, 256 * 4)), dim3(256), 0, s, row_ptr,
-                       col_idx, n, fnb);
+hipError_t launch_build_probe_nb(const int32_t *row_ptr, const int32_t *in_row_ptr, const int32_t *in_col,
+                                 int32_t n, int32_t *pnb, hipStream_t s) {
+    hipLaunchKernelGGL(probe_nb_kernel, dim3(grid_for(n, 4 * 16)), dim3(256), 0, s, row_ptr, in_row_ptr,
+                       in_col, n, pnb);
     return hipGetLastError();
 }
 
