@@ -730,16 +730,22 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
     // round 0: every listed vertex's probe neighbour (its in-neighbour of
     // highest out-degree), from the probe-neighbour index read in vertex
     // order beside row_ptr, so no scattered adjacency line is fetched for the
-    // vertices that stop there; R0 vertices per lane with their loads
+    // vertices that stop there (entries with bit 31 set were probed there
+    // already, in the word walk); then, for the vertices still searching with
+    // more than one entry, the aligned 8-entry block of the list holding its
+    // first entry (two 16-byte loads).  R0 vertices per lane with their loads
     // overlapped; a hit is recorded at once
     int npend = 0;
     {
         int v[R0], beg[R0], en[R0], par[R0];
         int x[R0][8];
+        bool probed[R0];
 #pragma unroll
         for (int j = 0; j < R0; ++j) {
             const int i = j * WAVE + lane;
-            v[j] = (i < cnt) ? lst[i] : -1;
+            const int raw = (i < cnt) ? lst[i] : 0;
+            probed[j] = i < cnt && raw < 0;
+            v[j] = (i < cnt) ? (raw & 0x7fffffff) : -1;
         }
         {
             int f[R0];
@@ -748,7 +754,7 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
             for (int j = 0; j < R0; ++j) {
                 beg[j] = (v[j] >= 0) ? P.in_row_ptr[v[j]] : 0;
                 en[j] = (v[j] >= 0) ? P.in_row_ptr[v[j] + 1] : 0;
-                f[j] = (v[j] >= 0) ? P.pnb[v[j]] : -1;
+                f[j] = (v[j] >= 0 && !probed[j]) ? P.pnb[v[j]] : -1;
             }
 #pragma unroll
             for (int j = 0; j < R0; ++j)
@@ -756,9 +762,6 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
 #pragma unroll
             for (int j = 0; j < R0; ++j) par[j] = (f[j] >= 0 && ((w[j] >> (f[j] & 31)) & 1u)) ? f[j] : -1;
         }
-        // ... then the aligned 8-entry block holding the first entry (two
-        // 16-byte loads), for the vertices still searching with more than
-        // one entry (the probe neighbour may sit in the block: probed twice)
         bool more = false;
 #pragma unroll
         for (int j = 0; j < R0; ++j) more |= par[j] < 0 && beg[j] + 1 < en[j];
@@ -856,11 +859,12 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
     }
     wave_lds_sync();
     // the vertices found in the later rounds: the neighbour at the first hit
+    // (bit 31 of a list entry is the word walk's mark, not part of the id)
 #pragma unroll
     for (int j = 0; j < R0; ++j) {
         const int i = j * WAVE + lane;
         const int h = (i < cnt) ? hit[i] : BU_NOHIT;
-        if (h != BU_NOHIT) bu_found(c, wbase, lst[i], P.in_col_idx[h], deg[i]);
+        if (h != BU_NOHIT) bu_found(c, wbase, lst[i] & 0x7fffffff, P.in_col_idx[h], deg[i]);
     }
 }
 
@@ -885,18 +889,71 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
     uint64_t *vis64 = reinterpret_cast<uint64_t *>(P.visited);
     uint64_t *nbm64 = reinterpret_cast<uint64_t *>(nbm);
     int32_t *lst = sh.bu_lst[wv];
+    const int use_cf = sh.use_cf, cf_sh = P.cf_sh;
+    constexpr int FW = 4;   // words probed together
     for (int cw = ws; cw < we; cw += WAVE) {
         const int nw = min(WAVE, we - cw);
         const uint64_t myvis = (lane < nw) ? vis64[cw + lane] : ~0ull;
         sh.bu_fm[wv][lane] = 0ull;
-        const uint64_t todo = __ballot(myvis != ~0ull);   // words with unvisited vertices
+        // pass 1, over the words with at least BU_DENSE unvisited vertices,
+        // FW words at a time with lane l on vertex l of each: the probe
+        // neighbour and the in-list bounds (consecutive ids, coalesced), then
+        // the frontier probe; a hit is recorded here, a miss with one
+        // in-neighbour is settled.  Lane j keeps in myrest the vertices of
+        // word j still to be listed: those left by pass 1 in a dense word,
+        // every unvisited one in a sparse word
+        const bool dense = lane < nw && __popcll(~myvis) >= BU_DENSE;
+        uint64_t myrest = dense ? 0ull : ~myvis;
+        for (uint64_t todo = __ballot(dense); todo;) {
+            int jw[FW], v[FW], f[FW], b[FW], e[FW];
+            uint32_t w[FW];
+#pragma unroll
+            for (int q = 0; q < FW; ++q) {
+                jw[q] = todo ? __ffsll((unsigned long long)todo) - 1 : -1;
+                todo &= todo - 1;
+                bool act = false;
+                if (jw[q] >= 0) {
+                    const uint32_t lo = (uint32_t)readlane_i((int)(uint32_t)myvis, jw[q]);
+                    const uint32_t hi = (uint32_t)readlane_i((int)(uint32_t)(myvis >> 32), jw[q]);
+                    act = !(((((uint64_t)hi << 32) | lo) >> lane) & 1ull);   // padding bits are set
+                }
+                v[q] = act ? (cw + jw[q]) * 64 + lane : -1;
+            }
+#pragma unroll
+            for (int q = 0; q < FW; ++q) {
+                f[q] = (v[q] >= 0) ? P.pnb[v[q]] : -1;
+                b[q] = (v[q] >= 0) ? P.in_row_ptr[v[q]] : 0;
+                e[q] = (v[q] >= 0) ? P.in_row_ptr[v[q] + 1] : 0;
+            }
+#pragma unroll
+            for (int q = 0; q < FW; ++q)
+                w[q] = (f[q] >= 0 && cf_maybe(sh, use_cf, cf_sh, f[q])) ? cbm[f[q] >> 5] : 0u;
+#pragma unroll
+            for (int q = 0; q < FW; ++q) {
+                const bool hitq = f[q] >= 0 && ((w[q] >> (f[q] & 31)) & 1u);
+                if (hitq) {
+                    P.dist[v[q]] = c.level + 1;
+                    if (P.parent) P.parent[v[q]] = f[q];
+                    c.fcnt += 1;
+                    c.fdeg += P.symmetric ? e[q] - b[q] : P.row_ptr[v[q] + 1] - P.row_ptr[v[q]];
+                }
+                const uint64_t hm = __ballot(hitq);
+                const uint64_t rm = __ballot(v[q] >= 0 && !hitq && e[q] - b[q] > 1);
+                if (lane == jw[q]) {
+                    myrest = rm;
+                    if (hm) sh.bu_fm[wv][lane] = hm;
+                }
+            }
+        }
+        // pass 2: the vertices left, listed 128 at a time for bu_list (bit 31
+        // marks those already probed at their probe neighbour)
         int cnt = 0;
-        for (uint64_t tm = todo; tm; tm &= tm - 1) {
+        const uint64_t denses = __ballot(dense);
+        for (uint64_t tm = __ballot(myrest != 0ull); tm; tm &= tm - 1) {
             const int j = __ffsll((unsigned long long)tm) - 1;
-            const uint32_t lo = (uint32_t)readlane_i((int)(uint32_t)myvis, j);
-            const uint32_t hi = (uint32_t)readlane_i((int)(uint32_t)(myvis >> 32), j);
-            const uint64_t vis = ((uint64_t)hi << 32) | lo;
-            const bool act = !((vis >> lane) & 1ull);      // padding bits are set
+            const uint32_t lo = (uint32_t)readlane_i((int)(uint32_t)myrest, j);
+            const uint32_t hi = (uint32_t)readlane_i((int)(uint32_t)(myrest >> 32), j);
+            const bool act = ((((uint64_t)hi << 32) | lo) >> lane) & 1ull;
             const uint64_t m = __ballot(act);
             if (cnt + __popcll(m) > BU_GSZ) {
                 wave_lds_sync();
@@ -904,7 +961,8 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
                 wave_lds_sync();
                 cnt = 0;
             }
-            if (act) lst[cnt + mbcnt64(m)] = (cw + j) * 64 + lane;
+            if (act)
+                lst[cnt + mbcnt64(m)] = ((cw + j) * 64 + lane) | (((denses >> j) & 1ull) ? (int)0x80000000 : 0);
             cnt += __popcll(m);
         }
         if (cnt > 0) {

@@ -23,6 +23,9 @@ constexpr int EB_TE = 1024;              // edges per tile of the edge-balanced 
 constexpr int64_t VFILTER_EDGES = 1 << 20;  // top-down levels with at least this many
                                          // edges load the visited word before a claim
 constexpr int BU_GSZ = 128;              // bottom-up: vertices a wavefront lists at a time
+#ifndef BU_DENSE
+#define BU_DENSE 16                      // bottom-up: a word with this many unvisited vertices
+#endif                                   //   is probed lane per vertex before listing
 constexpr int BU_W1 = 8;                 // bottom-up: entries per vertex in the round after
                                          // the first (x4 per round after that)
 constexpr int BU_WMAX = 8192;            // bottom-up: cap of the per-round entries per vertex
