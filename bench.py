@@ -101,6 +101,10 @@ def main():
     ap.add_argument("--loop", type=int, default=0, help="0 device-resident, 1 host-driven")
     ap.add_argument("--alpha", type=int, default=28, help="direction switch: pull when alpha*deg(F) > deg(U)")
     ap.add_argument("--beta", type=int, default=24, help="direction switch: push when beta*|F| < n, shrinking")
+    ap.add_argument("--claim", type=int, default=0, help="0 visited-bitmap atomicOr, 1 atomicMin on dist")
+    ap.add_argument("--compaction", type=int, default=0,
+                    help="0 direction-optimising path; top-down only: 1 atomic append, 2 sentinel-padded, "
+                         "3 padded + flag/scan/scatter filter, 4 flag/scan/scatter over all vertices")
     ap.add_argument("--no-parent", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the CPU-oracle baseline sample")
@@ -140,6 +144,7 @@ def main():
     bg = fb.BfsGraph(rp, ci)
     bg.set_policy(args.direction, args.advance, args.loop)
     bg.set_switch(args.alpha, args.beta)
+    bg.set_primitives(args.claim, args.compaction)
     dist = torch.empty(g.n, dtype=torch.int32, device=dev)
     parent = None if args.no_parent else torch.empty(g.n, dtype=torch.int32, device=dev)
     sizes = torch.empty(g.n, dtype=torch.int32, device=dev)
@@ -204,6 +209,11 @@ def main():
     dom = max(kinds, key=lambda k: kinds[k]["ms"])
     kd = kinds[dom]
     traffic = measured_traffic(args.workload, kd["kernel"])
+    if args.compaction:
+        # the alternative primitives run a host-driven loop: its time is the
+        # whole loop's (every kernel and the per-level read), not one kernel's
+        kd["kernel"] = "variant level loop (host-driven, all kernels)"
+        traffic = None
     step_gteps = [model[s]["medges"] / t / 1e9 for s, L, t in per_step]
 
     cpu = None
@@ -245,7 +255,8 @@ def main():
         "config": {"workload": WORKLOAD_DESC[args.workload], "n": g.n, "m_csr_entries": g.m,
                    "sources": len(sources), "parent_out": parent is not None,
                    "policy": {"direction": args.direction, "advance": args.advance, "loop": args.loop,
-                              "alpha": args.alpha, "beta": args.beta}},
+                              "alpha": args.alpha, "beta": args.beta, "claim": args.claim,
+                              "compaction": args.compaction}},
         "roofline": {"bound": "hbm", "achieved": round(kd["achieved"], 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(kd["achieved"] / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,

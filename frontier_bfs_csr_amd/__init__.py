@@ -23,10 +23,12 @@ DIR_AUTO, DIR_PUSH, DIR_PULL = 0, 1, 2
 ADV_AUTO, ADV_BINNED, ADV_EDGE = 0, 1, 2
 LOOP_DEVICE, LOOP_HOST, LOOP_CHAIN = 0, 1, 2
 WALK_LANE, WALK_WAVE, WALK_BINNED, WALK_MERGE = 0, 1, 2, 3
+CLAIM_BITMAP, CLAIM_MIN = 0, 1
+COMPACT_DEFAULT, COMPACT_ATOMIC, COMPACT_PADDED, COMPACT_FILTER, COMPACT_FLAGS = 0, 1, 2, 3, 4
 
 EXPORTS = ("bfs_graph_create", "bfs_run", "bfs_graph_destroy", "bfs_last_error",
            "bfs_set_policy", "bfs_last_run_stats", "bfs_set_timing", "bfs_last_run_timing",
-           "bfs_graph_info", "bfs_set_switch", "bfs_last_run_kernel_timing", "bfs_walk_level")
+           "bfs_graph_info", "bfs_set_switch", "bfs_last_run_kernel_timing", "bfs_walk_level", "bfs_set_primitives")
 
 _lib = None
 
@@ -73,6 +75,8 @@ def load():
         lib.bfs_last_run_kernel_timing.restype = i32
         lib.bfs_walk_level.argtypes = [P, P, i32, i32, i32, P, P]
         lib.bfs_walk_level.restype = i32
+        lib.bfs_set_primitives.argtypes = [P, i32, i32]
+        lib.bfs_set_primitives.restype = i32
         _lib = lib
     return _lib
 
@@ -130,6 +134,12 @@ def bfs_graph_destroy(g):
 
 def bfs_set_policy(g, direction=DIR_AUTO, advance=ADV_AUTO, loop=LOOP_DEVICE):
     rc = load().bfs_set_policy(g, int(direction), int(advance), int(loop))
+    if rc < 0:
+        raise BfsError(rc, bfs_last_error())
+
+
+def bfs_set_primitives(g, claim=CLAIM_BITMAP, compaction=COMPACT_DEFAULT):
+    rc = load().bfs_set_primitives(g, int(claim), int(compaction))
     if rc < 0:
         raise BfsError(rc, bfs_last_error())
 
@@ -223,6 +233,9 @@ class BfsGraph:
 
     def set_switch(self, alpha=28, beta=24):
         bfs_set_switch(self.handle, alpha, beta)
+
+    def set_primitives(self, claim=CLAIM_BITMAP, compaction=COMPACT_DEFAULT):
+        bfs_set_primitives(self.handle, claim, compaction)
 
     def stats(self):
         return bfs_last_run_stats(self.handle)

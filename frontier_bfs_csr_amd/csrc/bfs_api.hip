@@ -60,6 +60,13 @@ struct bfs_graph {
     HostCtl *host_ctl = nullptr;   // pinned
     GraphFacts *facts = nullptr;   // device, create only
     int32_t pol_dir = BFS_DIR_AUTO, pol_adv = BFS_ADV_AUTO, pol_loop = BFS_LOOP_DEVICE;
+    int32_t pol_claim = BFS_CLAIM_BITMAP, pol_compact = BFS_COMPACT_DEFAULT;
+    // buffers of the alternative compactions (allocated when one is chosen):
+    // two frontiers, flags/degrees, their scan, scan temporaries
+    int32_t *va = nullptr, *vb = nullptr, *vs = nullptr, *vo = nullptr, *vt = nullptr;
+    int64_t var_cap = 0;
+    VarCtl *vctl = nullptr;        // device: running counters, then the copy the host reads
+    VarCtl *hvctl = nullptr;       // pinned host mirror
     int32_t alpha = ALPHA, beta = BETA;
     uint32_t barrier_ticks = 200000000u;   // 2 s at 100 MHz
     int32_t last_L = 0;
@@ -96,6 +103,10 @@ void free_all(bfs_graph *g) {
                     g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
+    void *vptrs[] = {g->va, g->vb, g->vs, g->vo, g->vt, g->vctl};
+    for (void *p : vptrs)
+        if (p) (void)hipFree(p);
+    if (g->hvctl) (void)hipHostFree(g->hvctl);
     if (g->host_ctl) (void)hipHostFree(g->host_ctl);
     for (hipEvent_t e : g->events) (void)hipEventDestroy(e);
     g->events.clear();
@@ -248,6 +259,115 @@ hipError_t build_in_edges(bfs_graph *g) {
     return e;
 }
 
+// Buffers of the alternative compactions: frontiers of up to max(n, m)
+// entries (a padded frontier holds one entry per frontier edge).
+int alloc_variant_buffers(bfs_graph *g) {
+    if (g->va) return 0;
+    const int64_t cap = (g->m > g->n ? g->m : (int64_t)g->n) + 1;
+    hipError_t e = dalloc(&g->va, cap);
+    if (e == hipSuccess) e = dalloc(&g->vb, cap);
+    if (e == hipSuccess) e = dalloc(&g->vs, cap);
+    if (e == hipSuccess) e = dalloc(&g->vo, cap + 1);
+    if (e == hipSuccess) e = dalloc(&g->vt, scan_tmp_ints(cap));
+    if (e == hipSuccess) e = dalloc(&g->vctl, 2);
+    if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void **>(&g->hvctl), sizeof(VarCtl));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        void *vptrs[] = {g->va, g->vb, g->vs, g->vo, g->vt, g->vctl};
+        for (void *p : vptrs)
+            if (p) (void)hipFree(p);
+        if (g->hvctl) (void)hipHostFree(g->hvctl);
+        g->va = g->vb = g->vs = g->vo = g->vt = nullptr;
+        g->vctl = nullptr;
+        g->hvctl = nullptr;
+        set_error("device allocation of the compaction buffers (5 x %lld ints) failed", (long long)cap);
+        return BFS_ENOMEM;
+    }
+    g->var_cap = cap;
+    return 0;
+}
+
+// Top-down search with the chosen claim and compaction primitives; the host
+// reads {frontier edges, winners} once per level.
+int32_t run_variant(bfs_graph *g, const Params &P, hipStream_t stream) {
+    const bool timing = g->timing != 0;
+    if (timing) {
+        HIP_TRY(ensure_events(g, 3), BFS_EHIP);
+        HIP_TRY(hipEventRecord(g->events[0], stream), BFS_EHIP);
+    }
+    HIP_TRY(launch_init(P, g->grid, stream), BFS_EHIP);
+    HIP_TRY(launch_var_seed(g->va, P.source, P.level_sizes, g->vctl, stream), BFS_EHIP);
+    if (timing) HIP_TRY(hipEventRecord(g->events[1], stream), BFS_EHIP);
+    const int32_t mode = g->pol_compact;
+    int32_t *F = g->va, *Fn = g->vb;
+    int64_t len = 1;
+    int32_t L = 0;
+    for (int32_t k = 0;; ++k) {
+        if (k >= g->n) {
+            set_error("search did not terminate after %d levels", k);
+            return BFS_EDEVICE;
+        }
+        HIP_TRY(launch_var_degrees(P.row_ptr, F, (int32_t)len, g->vs, stream), BFS_EHIP);
+        HIP_TRY(exclusive_scan(g->vs, g->vo, len, g->vt, stream), BFS_EHIP);
+        VarAdvance A;
+        A.row_ptr = P.row_ptr;
+        A.col_idx = P.col_idx;
+        A.F = F;
+        A.len = (int32_t)len;
+        A.offs = g->vo;
+        A.next_level = k + 1;
+        A.claim = g->pol_claim;
+        A.dist = P.dist;
+        A.parent = P.parent;
+        A.visited = P.visited;
+        A.padded = (mode == BFS_COMPACT_PADDED || mode == BFS_COMPACT_FILTER) ? Fn : nullptr;
+        A.compact = (mode == BFS_COMPACT_ATOMIC) ? Fn : nullptr;
+        A.vc = g->vctl;
+        HIP_TRY(launch_var_advance(A, g->grid, stream), BFS_EHIP);
+        HIP_TRY(launch_var_record(g->vo + len, k, P.st_dir, P.st_fdeg, P.st_cap, P.level_sizes, g->vctl,
+                                  g->vctl + 1, stream),
+                BFS_EHIP);
+        if (mode == BFS_COMPACT_FLAGS)
+            HIP_TRY(launch_var_compact_level(P.dist, g->n, k + 1, g->vs, g->vo, g->vt, Fn, stream), BFS_EHIP);
+        HIP_TRY(hipMemcpyAsync(g->hvctl, g->vctl + 1, sizeof(VarCtl), hipMemcpyDeviceToHost, stream), BFS_EHIP);
+        HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+        const int64_t E = g->hvctl->edges;
+        const int64_t w = (int64_t)g->hvctl->winners;
+        if (w == 0) {
+            L = k + 1;
+            break;
+        }
+        if (mode == BFS_COMPACT_FILTER) {
+            // the padded frontier in Fn, compacted into the spent frontier F
+            HIP_TRY(launch_var_compact_padded(Fn, E, g->vs, g->vo, g->vt, F, stream), BFS_EHIP);
+            len = w;
+        } else {
+            len = (mode == BFS_COMPACT_PADDED) ? E : w;
+            int32_t *t = F;
+            F = Fn;
+            Fn = t;
+        }
+    }
+    g->last_L = L;
+    g->last_timed = 0;
+    if (timing) {
+        HIP_TRY(hipEventRecord(g->events[2], stream), BFS_EHIP);
+        HIP_TRY(hipEventSynchronize(g->events[2]), BFS_EHIP);
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, g->events[0], g->events[1]), BFS_EHIP);
+        g->last_init_ms = ms;
+        HIP_TRY(hipEventElapsedTime(&ms, g->events[1], g->events[2]), BFS_EHIP);
+        g->last_level_ms = ms;
+        g->last_launches = L;
+        g->last_kind_ms[0] = ms;
+        g->last_kind_ms[1] = 0.f;
+        g->last_kind_launches[0] = L;
+        g->last_kind_launches[1] = 0;
+        g->last_timed = 1;
+    }
+    return L;
+}
+
 extern "C" {
 
 const char *bfs_last_error(void) { return g_err.c_str(); }
@@ -340,6 +460,30 @@ int32_t bfs_set_policy(bfs_graph *g, int32_t direction, int32_t advance, int32_t
     return 0;
 }
 
+int32_t bfs_set_primitives(bfs_graph *g, int32_t claim, int32_t compaction) {
+    if (!g) {
+        set_error("NULL graph handle");
+        return BFS_EINVAL;
+    }
+    if (claim < BFS_CLAIM_BITMAP || claim > BFS_CLAIM_MIN || compaction < BFS_COMPACT_DEFAULT ||
+        compaction > BFS_COMPACT_FLAGS) {
+        set_error("unknown claim %d or compaction %d", claim, compaction);
+        return BFS_EINVAL;
+    }
+    if (compaction == BFS_COMPACT_DEFAULT && claim != BFS_CLAIM_BITMAP) {
+        set_error("the direction-optimising path claims with the visited bitmap");
+        return BFS_EINVAL;
+    }
+    if (compaction != BFS_COMPACT_DEFAULT) {
+        HIP_TRY(hipSetDevice(g->device), BFS_EHIP);
+        const int rc = alloc_variant_buffers(g);
+        if (rc) return rc;
+    }
+    g->pol_claim = claim;
+    g->pol_compact = compaction;
+    return 0;
+}
+
 int32_t bfs_set_switch(bfs_graph *g, int32_t alpha, int32_t beta) {
     if (!g) {
         set_error("NULL graph handle");
@@ -418,6 +562,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.beta = g->beta;
     P.barrier_ticks = g->barrier_ticks;
 
+    if (g->pol_compact != BFS_COMPACT_DEFAULT) return run_variant(g, P, stream);
     const bool timing = g->timing != 0;
     g->last_timed = 0;
     if (timing) {

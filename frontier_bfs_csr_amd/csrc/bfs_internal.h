@@ -177,6 +177,34 @@ hipError_t exclusive_scan(const int32_t *cnt, int32_t *out, int64_t n, int32_t *
 hipError_t launch_transpose_fill(const int32_t *row_ptr, const int32_t *col_idx, int32_t n,
                                  int32_t *cursor, int32_t *in_col, hipStream_t s);
 
+// alternative claim / compaction primitives (bfs_variants.hip)
+struct VarCtl {
+    int64_t edges;                 // frontier edges of the level just advanced
+    unsigned long long winners;    // its new vertices (the append cursor when compacting by atomics)
+};
+struct VarAdvance {
+    const int32_t *row_ptr, *col_idx;
+    const int32_t *F;              // frontier (may hold -1 sentinels)
+    int32_t len;
+    const int32_t *offs;           // exclusive scan of the frontier's degrees (len + 1)
+    int32_t next_level;
+    int32_t claim;                 // BFS_CLAIM_*
+    int32_t *dist, *parent;
+    uint32_t *visited;
+    int32_t *padded;               // non-null: neighbour or -1 at every edge position
+    int32_t *compact;              // non-null: winners appended (atomic cursor in vc)
+    VarCtl *vc;
+};
+hipError_t launch_var_seed(int32_t *F, int32_t source, int32_t *level_sizes, VarCtl *vc, hipStream_t s);
+hipError_t launch_var_degrees(const int32_t *row_ptr, const int32_t *F, int32_t len, int32_t *deg, hipStream_t s);
+hipError_t launch_var_advance(const VarAdvance &A, int grid, hipStream_t s);
+hipError_t launch_var_record(const int32_t *offs_end, int32_t k, int8_t *st_dir, int64_t *st_fdeg, int32_t st_cap,
+                             int32_t *level_sizes, VarCtl *vc, VarCtl *out, hipStream_t s);
+hipError_t launch_var_compact_padded(const int32_t *x, int64_t len, int32_t *flag, int32_t *offs, int32_t *tmp,
+                                     int32_t *out, hipStream_t s);
+hipError_t launch_var_compact_level(const int32_t *dist, int32_t n, int32_t level, int32_t *flag, int32_t *offs,
+                                    int32_t *tmp, int32_t *out, hipStream_t s);
+
 // isolated neighbour walk of listed vertices (bfs_walk.hip); scratch holds
 // walk_scratch_ints(count) ints, bad is raised for ids outside [0, n)
 int64_t walk_scratch_ints(int64_t count);

@@ -179,6 +179,38 @@ int32_t bfs_last_run_kernel_timing(const bfs_graph *g, float *td_ms, int32_t *td
                                    float *bu_ms, int32_t *bu_launches);
 
 /*
+ * Claim and compaction primitives of the top-down level (Gunrock reading
+ * guide, step 2; "Day 38 - Graph traversal on a GPU", on day 33's
+ * compaction).  claim: BFS_CLAIM_BITMAP (an atomicOr on the visited bitmap
+ * elects the one writer of dist and parent) or BFS_CLAIM_MIN (atomicMin on
+ * dist: the caller that read a larger old value wins).  compaction:
+ * BFS_COMPACT_DEFAULT, the direction-optimising path of bfs_run (claims with
+ * the bitmap, so claim must be BFS_CLAIM_BITMAP); or a top-down-only search
+ * whose level loop reads two counters per level on the host, with the next
+ * frontier built by BFS_COMPACT_ATOMIC (winners appended at a
+ * wavefront-aggregated atomic cursor; order varies), BFS_COMPACT_PADDED (the
+ * idempotent advance: every frontier edge writes its neighbour, or -1 where
+ * it lost, at its own position, and that padded array is the next
+ * frontier, one entry per frontier edge of the level before),
+ * BFS_COMPACT_FILTER (the padded array compacted by flag, exclusive scan and
+ * scatter; order of the edges) or BFS_COMPACT_FLAGS (flag every vertex with
+ * the new level, scan the flags over all n vertices, scatter: the frontier in
+ * id order, at O(n) per level).  dist and level_sizes are those of bfs_run;
+ * parent is a frontier neighbour.  A non-default compaction allocates its
+ * buffers (five arrays of max(n, m) + 1 ints) on this call.  Returns 0;
+ * BFS_EINVAL for a NULL handle or an unknown or unsupported pair;
+ * BFS_ENOMEM if the buffers do not fit.
+ */
+#define BFS_CLAIM_BITMAP    0
+#define BFS_CLAIM_MIN       1
+#define BFS_COMPACT_DEFAULT 0
+#define BFS_COMPACT_ATOMIC  1
+#define BFS_COMPACT_PADDED  2
+#define BFS_COMPACT_FILTER  3
+#define BFS_COMPACT_FLAGS   4
+int32_t bfs_set_primitives(bfs_graph *g, int32_t claim, int32_t compaction);
+
+/*
  * Isolated neighbour walk of one level: the measurement the "Day 38 - Graph
  * traversal on a GPU" page uses to compare thread-to-work mappings without
  * the atomics, frontier build and distance writes of a real level (section
