@@ -263,6 +263,13 @@ def tiny_random(seed, n=None, directed=None, p=None, self_loops=True, duplicates
                  {"directed": directed, "p": p})
 
 
+def edge_weights(m, seed, wmax=255, wmin=1):
+    """One non-negative integer weight per CSR entry, uniform in [wmin, wmax]
+    (numpy PCG64, seeded); the pages supply no weights."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(wmin, wmax + 1, size=int(m), dtype=np.uint64).astype(np.uint32)
+
+
 def random_directed(n, avg_deg, seed):
     """Directed graph with n*avg_deg uniform edges (duplicates and self-loops
     kept), rows in random order."""

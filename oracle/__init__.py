@@ -12,7 +12,9 @@ Frontier Model for Parallel Breadth-First Search" (section 22.1) and
 gates of that program's ``main`` (exact dist, level count, frontier sizes
 summing to the reached count) and the BFS-parent and edge invariants, and
 the neighbour-walk checksum that the Day 38 page's isolated level walk checks
-its kernels against.
+its kernels against, and single-source shortest paths (Dijkstra, with the
+smallest tight in-neighbour as predecessor) for the atomic-min relaxation
+the Gunrock reading guide extends the same lambda to.
 """
 from __future__ import annotations
 
@@ -93,6 +95,8 @@ def _load():
         lib.oracle_check.restype = i32
         lib.oracle_walk_checksum.argtypes = [i32, P, P, i32, P, i32, P]
         lib.oracle_walk_checksum.restype = i32
+        lib.oracle_sssp.argtypes = [i32, P, P, P, i32, P, P]
+        lib.oracle_sssp.restype = i32
         _lib = lib
     return _lib
 
@@ -158,6 +162,24 @@ def walk_checksum(row_ptr, col_idx, vertices, repeats=64):
     if rc != 0:
         raise ValueError(f"oracle_walk_checksum failed with {rc}")
     return out
+
+
+def sssp(row_ptr, col_idx, weights, source):
+    """Shortest-path distances (int64, -1 unreachable) and predecessors (int32:
+    the smallest tight in-neighbour, the source's own id for the source, -1
+    unreachable) from ``source``, with weights[e] >= 0 on CSR entry e."""
+    lib = _load()
+    row_ptr, col_idx = _i32(row_ptr), _i32(col_idx)
+    w = np.ascontiguousarray(weights, dtype=np.uint32)
+    n = row_ptr.shape[0] - 1
+    if w.shape[0] != col_idx.shape[0]:
+        raise ValueError("one weight per CSR entry")
+    dist = np.empty(n, np.int64)
+    pred = np.empty(n, np.int32)
+    rc = lib.oracle_sssp(n, _ptr(row_ptr), _ptr(col_idx), _ptr(w), int(source), _ptr(dist), _ptr(pred))
+    if rc != 0:
+        raise ValueError(f"oracle_sssp failed with {rc}")
+    return dist, pred
 
 
 def check(row_ptr, col_idx, source, ref, dist, parent=None, L=None, sizes=None,

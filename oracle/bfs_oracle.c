@@ -311,3 +311,109 @@ int32_t oracle_walk_checksum(int32_t n, const int32_t *row_ptr, const int32_t *c
     return 0;
 }
 
+
+/*
+ * Single-source shortest paths with non-negative integer edge weights, the
+ * second workload the Gunrock reading guide (step 2) says the same atomic-min
+ * lambda serves, and the next chapter "Chapter 22" points to.  weights[e] is
+ * the weight of CSR entry e (row u, neighbour col_idx[e]).
+ *
+ * Distances: Dijkstra's algorithm with a binary min-heap of (distance,
+ * vertex) pairs and lazy deletion (a popped pair whose distance is above the
+ * vertex's current one is skipped).  dist[v] = -1 when v is unreachable.
+ * Predecessor: among the entries u -> v that are tight (dist[u] + w = dist[v],
+ * u reached), the smallest u; pred[source] = source, -1 when unreachable.
+ * That choice is a property of the distances alone, so every correct solver
+ * that settles ties by the smaller id agrees with it exactly.
+ * Returns 0, -1 on bad arguments, -2 when out of memory.
+ */
+typedef struct { int64_t d; int32_t v; } HeapItem;
+
+static void heap_push(HeapItem *h, int64_t *len, HeapItem x)
+{
+    int64_t i = (*len)++;
+    while (i > 0) {
+        const int64_t p = (i - 1) / 2;
+        if (h[p].d <= x.d) break;
+        h[i] = h[p];
+        i = p;
+    }
+    h[i] = x;
+}
+
+static HeapItem heap_pop(HeapItem *h, int64_t *len)
+{
+    const HeapItem top = h[0];
+    const HeapItem x = h[--(*len)];
+    int64_t i = 0;
+    for (;;) {
+        int64_t c = 2 * i + 1;
+        if (c >= *len) break;
+        if (c + 1 < *len && h[c + 1].d < h[c].d) ++c;
+        if (h[c].d >= x.d) break;
+        h[i] = h[c];
+        i = c;
+    }
+    if (*len > 0) h[i] = x;
+    return top;
+}
+
+int32_t oracle_sssp(int32_t n, const int32_t *row_ptr, const int32_t *col_idx, const uint32_t *weights,
+                    int32_t source, int64_t *dist, int32_t *pred)
+{
+    if (n <= 0 || source < 0 || source >= n || !row_ptr || !dist || !pred) return -1;
+    const int64_t m = row_ptr[n];
+    if (m > 0 && (!col_idx || !weights)) return -1;
+    for (int32_t v = 0; v < n; ++v) { dist[v] = -1; pred[v] = -1; }
+    /* every entry pushes at most one pair, plus the source */
+    HeapItem *h = (HeapItem *)malloc(sizeof(HeapItem) * (size_t)(m + 1));
+    if (!h) return -2;
+    int64_t len = 0;
+    dist[source] = 0;
+    heap_push(h, &len, (HeapItem){0, source});
+    while (len > 0) {
+        const HeapItem it = heap_pop(h, &len);
+        if (it.d > dist[it.v]) continue;          /* stale */
+        const int32_t u = it.v;
+        for (int64_t e = row_ptr[u]; e < row_ptr[u + 1]; ++e) {
+            const int32_t v = col_idx[e];
+#if ORACLE_MUTANT == 11
+            const int64_t nd = it.d + 1;
+#else
+            const int64_t nd = it.d + (int64_t)weights[e];
+#endif
+            if (dist[v] < 0 || nd < dist[v]) {
+                dist[v] = nd;
+                heap_push(h, &len, (HeapItem){nd, v});
+            }
+        }
+    }
+    free(h);
+    /* predecessors: the smallest tight in-neighbour */
+    pred[source] = source;
+    for (int32_t u = 0; u < n; ++u) {
+        if (dist[u] < 0) continue;
+        for (int64_t e = row_ptr[u]; e < row_ptr[u + 1]; ++e) {
+            const int32_t v = col_idx[e];
+            if (v == source) continue;
+#if ORACLE_MUTANT == 11
+            const int64_t w = 1;
+#else
+            const int64_t w = (int64_t)weights[e];
+#endif
+#if ORACLE_MUTANT == 13
+            /* reads the entry backwards: v as the predecessor of u */
+            if (dist[v] >= 0 && dist[v] + w == dist[u] && u != source && (pred[u] < 0 || v < pred[u])) pred[u] = v;
+#else
+            if (dist[u] + w == dist[v]) {
+#if ORACLE_MUTANT == 12
+                if (pred[v] < 0 || u > pred[v]) pred[v] = u;
+#else
+                if (pred[v] < 0 || u < pred[v]) pred[v] = u;
+#endif
+            }
+#endif
+        }
+    }
+    return 0;
+}

@@ -255,8 +255,90 @@ def pin_walk_checksum():
     return None
 
 
+def _bellman_ford(n, row_ptr, col_idx, w, source):
+    """Shortest distances by repeated relaxation of every entry (a method
+    unlike the oracle's Dijkstra): -1 for unreachable."""
+    INF = np.int64(1) << 62
+    d = np.full(n, INF, np.int64)
+    d[source] = 0
+    rows = np.repeat(np.arange(n), np.diff(row_ptr))
+    w = w.astype(np.int64)
+    for _ in range(n):
+        cand = np.where(d[rows] < INF, d[rows] + w, INF)
+        new = d.copy()
+        np.minimum.at(new, col_idx, cand)
+        if (new == d).all():
+            break
+        d = new
+    return np.where(d < INF, d, -1)
+
+
+def _pred_ok(n, row_ptr, col_idx, w, source, dist, pred):
+    """pred[v] is the smallest u with an entry u -> v and dist[u] + w = dist[v]."""
+    rows = np.repeat(np.arange(n), np.diff(row_ptr))
+    tight = (dist[rows] >= 0) & (dist[rows] + w.astype(np.int64) == dist[col_idx]) & (col_idx != source)
+    best = np.full(n, n, np.int64)
+    np.minimum.at(best, col_idx[tight], rows[tight])
+    want = np.where(dist >= 0, np.where(best < n, best, -1), -1)
+    want[source] = source
+    return (pred == want).all()
+
+
+def pin_sssp():
+    """SSSP distances against Bellman-Ford on 200 tiny random graphs with
+    weights 0..9 (duplicates with different weights, self-loops, directed and
+    symmetric); predecessors are the smallest tight in-neighbours; unit
+    weights give the BFS levels; weighted paths and stars have closed forms;
+    sums beyond 32 bits stay exact."""
+    for seed in range(200):
+        g = gg.tiny_random(seed)
+        w = gg.edge_weights(g.m, seed + 1000, wmax=9, wmin=0)
+        for s in g.sources:
+            d, p = oracle.sssp(g.row_ptr, g.col_idx, w, int(s))
+            bf = _bellman_ford(g.n, g.row_ptr, g.col_idx, w, int(s))
+            if not (d == bf).all():
+                return f"sssp tiny {seed} s={s}: dist differs from Bellman-Ford"
+            if not _pred_ok(g.n, g.row_ptr, g.col_idx, w, int(s), d, p):
+                return f"sssp tiny {seed} s={s}: predecessor is not the smallest tight in-neighbour"
+        ones = np.ones(g.m, np.uint32)
+        s = int(g.sources[0])
+        d1, _ = oracle.sssp(g.row_ptr, g.col_idx, ones, s)
+        if not (d1 == oracle.bfs(g.row_ptr, g.col_idx, s)[0]).all():
+            return f"sssp tiny {seed}: unit weights do not give the BFS levels"
+    # weighted path 0-1-...-9 from 0: prefix sums of the forward entries
+    g = gg.path_graph(10)
+    w = gg.edge_weights(g.m, 7, wmax=1000, wmin=0)
+    d, p = oracle.sssp(g.row_ptr, g.col_idx, w, 0)
+    rows = np.repeat(np.arange(g.n), np.diff(g.row_ptr))
+    fwd = {int(r): int(w[e]) for e, r in enumerate(rows) if g.col_idx[e] == r + 1}
+    want = np.concatenate([[0], np.cumsum([fwd[i] for i in range(9)])])
+    if not (d == want).all() or not (p == np.concatenate([[0], np.arange(9)])).all():
+        return f"sssp path: {d.tolist()} != {want.tolist()}"
+    # star from the hub: each leaf at its own entry's weight; from a leaf: via the hub
+    g = gg.star_graph(6)
+    w = np.arange(1, g.m + 1, dtype=np.uint32) * 3
+    d, _ = oracle.sssp(g.row_ptr, g.col_idx, w, 0)
+    want = np.zeros(g.n, np.int64)
+    for e in range(g.row_ptr[0], g.row_ptr[1]):
+        want[g.col_idx[e]] = w[e]
+    if not (d == want).all():
+        return f"sssp star: {d.tolist()} != {want.tolist()}"
+    # all-zero weights: every reachable vertex at 0
+    g = gg.tiny_random(3, directed=True)
+    d, _ = oracle.sssp(g.row_ptr, g.col_idx, np.zeros(g.m, np.uint32), int(g.sources[0]))
+    b = oracle.bfs(g.row_ptr, g.col_idx, int(g.sources[0]))[0]
+    if not ((d >= 0) == (b >= 0)).all() or (d[d >= 0] != 0).any():
+        return "sssp zero weights"
+    # 32-bit weights summed past 2**32
+    g = gg.path_graph(4)
+    d, _ = oracle.sssp(g.row_ptr, g.col_idx, np.full(g.m, 0xFFFFFFFF, np.uint32), 0)
+    if d.tolist() != [0, 0xFFFFFFFF, 2 * 0xFFFFFFFF, 3 * 0xFFFFFFFF]:
+        return f"sssp wide sums {d.tolist()}"
+    return None
+
+
 ALL_PINS = [pin_chapter22_bfs, pin_chapter22_partial_states, pin_pmpp_graph,
-            pin_tiny_random, pin_closed_forms, pin_checker_rejects, pin_walk_checksum]
+            pin_tiny_random, pin_closed_forms, pin_checker_rejects, pin_walk_checksum, pin_sssp]
 
 
 def failing_pins(tiny_count=300):

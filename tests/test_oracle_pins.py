@@ -13,7 +13,7 @@ def test_pin(pin):
     assert pin() is None
 
 
-@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
+@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13])
 def test_pins_reject_planted_mistakes(mutant):
     """Each deliberately broken oracle build fails at least one pin."""
     with tempfile.TemporaryDirectory() as d:
