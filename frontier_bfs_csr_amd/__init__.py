@@ -28,7 +28,8 @@ COMPACT_DEFAULT, COMPACT_ATOMIC, COMPACT_PADDED, COMPACT_FILTER, COMPACT_FLAGS =
 
 EXPORTS = ("bfs_graph_create", "bfs_run", "bfs_graph_destroy", "bfs_last_error",
            "bfs_set_policy", "bfs_last_run_stats", "bfs_set_timing", "bfs_last_run_timing",
-           "bfs_graph_info", "bfs_set_switch", "bfs_last_run_kernel_timing", "bfs_walk_level", "bfs_set_primitives")
+           "bfs_graph_info", "bfs_set_switch", "bfs_last_run_kernel_timing", "bfs_walk_level", "bfs_set_primitives",
+           "bfs_sssp")
 
 _lib = None
 
@@ -77,6 +78,8 @@ def load():
         lib.bfs_walk_level.restype = i32
         lib.bfs_set_primitives.argtypes = [P, i32, i32]
         lib.bfs_set_primitives.restype = i32
+        lib.bfs_sssp.argtypes = [P, i32, P, ctypes.c_uint32, P, P, P]
+        lib.bfs_sssp.restype = i32
         _lib = lib
     return _lib
 
@@ -95,6 +98,17 @@ def _dev_i32(t, name, numel=None):
         raise TypeError(f"{name} must be a contiguous int32 tensor")
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name} needs at least {numel} elements, has {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr() if t.numel() else None)
+
+
+def _dev_tensor(t, name, dtypes):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dtype not in dtypes or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous tensor of {', '.join(map(str, dtypes))}")
     return ctypes.c_void_p(t.data_ptr() if t.numel() else None)
 
 
@@ -136,6 +150,20 @@ def bfs_set_policy(g, direction=DIR_AUTO, advance=ADV_AUTO, loop=LOOP_DEVICE):
     rc = load().bfs_set_policy(g, int(direction), int(advance), int(loop))
     if rc < 0:
         raise BfsError(rc, bfs_last_error())
+
+
+def bfs_sssp(g, source, weights, max_weight, dist, pred=None, stream=None):
+    """Shortest paths from source: weights (device uint32/int32 tensor, one per
+    CSR entry), dist (device int64, n), pred (device int32, n, or None).
+    Returns the number of relaxation rounds."""
+    import torch
+    w = _dev_tensor(weights, "weights", (torch.int32, torch.uint32))
+    d = _dev_tensor(dist, "dist", (torch.int64,))
+    p = _dev_i32(pred, "pred")
+    rc = load().bfs_sssp(g, int(source), w, int(max_weight), d, p, _stream_handle(stream))
+    if rc < 0:
+        raise BfsError(rc, bfs_last_error())
+    return rc
 
 
 def bfs_set_primitives(g, claim=CLAIM_BITMAP, compaction=COMPACT_DEFAULT):
@@ -236,6 +264,9 @@ class BfsGraph:
 
     def set_primitives(self, claim=CLAIM_BITMAP, compaction=COMPACT_DEFAULT):
         bfs_set_primitives(self.handle, claim, compaction)
+
+    def sssp(self, source, weights, max_weight, dist, pred=None, stream=None):
+        return bfs_sssp(self.handle, source, weights, max_weight, dist, pred, stream)
 
     def stats(self):
         return bfs_last_run_stats(self.handle)

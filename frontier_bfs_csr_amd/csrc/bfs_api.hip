@@ -67,6 +67,11 @@ struct bfs_graph {
     int64_t var_cap = 0;
     VarCtl *vctl = nullptr;        // device: running counters, then the copy the host reads
     VarCtl *hvctl = nullptr;       // pinned host mirror
+    // shortest-path buffers (allocated on the first bfs_sssp call)
+    unsigned long long *skey = nullptr;
+    uint32_t *snbm = nullptr;
+    int32_t *sf0 = nullptr, *sf1 = nullptr, *scnt = nullptr, *soffs = nullptr, *stmp = nullptr;
+    SsspCtl *sctl = nullptr, *hsctl = nullptr;
     int32_t alpha = ALPHA, beta = BETA;
     uint32_t barrier_ticks = 200000000u;   // 2 s at 100 MHz
     int32_t last_L = 0;
@@ -107,6 +112,10 @@ void free_all(bfs_graph *g) {
     for (void *p : vptrs)
         if (p) (void)hipFree(p);
     if (g->hvctl) (void)hipHostFree(g->hvctl);
+    void *sptrs[] = {g->skey, g->snbm, g->sf0, g->sf1, g->scnt, g->soffs, g->stmp, g->sctl};
+    for (void *p : sptrs)
+        if (p) (void)hipFree(p);
+    if (g->hsctl) (void)hipHostFree(g->hsctl);
     if (g->host_ctl) (void)hipHostFree(g->host_ctl);
     for (hipEvent_t e : g->events) (void)hipEventDestroy(e);
     g->events.clear();
@@ -366,6 +375,34 @@ int32_t run_variant(bfs_graph *g, const Params &P, hipStream_t stream) {
         g->last_timed = 1;
     }
     return L;
+}
+
+int alloc_sssp_buffers(bfs_graph *g) {
+    if (g->skey) return 0;
+    const int64_t n = g->n, nwords = (n + 31) / 32;
+    hipError_t e = dalloc(&g->skey, n);
+    if (e == hipSuccess) e = dalloc(&g->snbm, nwords);
+    if (e == hipSuccess) e = dalloc(&g->sf0, n);
+    if (e == hipSuccess) e = dalloc(&g->sf1, n);
+    if (e == hipSuccess) e = dalloc(&g->scnt, n + 1);
+    if (e == hipSuccess) e = dalloc(&g->soffs, n + 1);
+    if (e == hipSuccess) e = dalloc(&g->stmp, scan_tmp_ints(n + 1));
+    if (e == hipSuccess) e = dalloc(&g->sctl, 1);
+    if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void **>(&g->hsctl), sizeof(SsspCtl));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        void *sptrs[] = {g->skey, g->snbm, g->sf0, g->sf1, g->scnt, g->soffs, g->stmp, g->sctl};
+        for (void *p : sptrs)
+            if (p) (void)hipFree(p);
+        if (g->hsctl) (void)hipHostFree(g->hsctl);
+        g->skey = nullptr;
+        g->snbm = nullptr;
+        g->sf0 = g->sf1 = g->scnt = g->soffs = g->stmp = nullptr;
+        g->sctl = g->hsctl = nullptr;
+        set_error("device allocation of the shortest-path buffers failed");
+        return BFS_ENOMEM;
+    }
+    return 0;
 }
 
 extern "C" {
@@ -698,6 +735,95 @@ int32_t bfs_walk_level(bfs_graph *g, const int32_t *vertices, int32_t count, int
         g->last_timed = 1;
     }
     return 0;
+}
+
+int32_t bfs_sssp(bfs_graph *g, int32_t source, const uint32_t *weights, uint32_t max_weight,
+                 int64_t *dist_out, int32_t *pred_out, hipStream_t stream) {
+    g_err.clear();
+    if (!g) {
+        set_error("NULL graph handle");
+        return BFS_EINVAL;
+    }
+    if (!dist_out || (g->m > 0 && !weights)) {
+        set_error("dist_out and weights must be device pointers");
+        return BFS_EINVAL;
+    }
+    if (source < 0 || source >= g->n) {
+        set_error("source %d is outside [0, %d)", source, g->n);
+        return BFS_EINVAL;
+    }
+    if ((uint64_t)g->n * (uint64_t)max_weight >= 0xffffffffull) {
+        set_error("n * max_weight = %llu does not stay below 2^32 - 1",
+                  (unsigned long long)g->n * (unsigned long long)max_weight);
+        return BFS_EINVAL;
+    }
+    HIP_TRY(hipSetDevice(g->device), BFS_EHIP);
+    {
+        const int rc = alloc_sssp_buffers(g);
+        if (rc) return rc;
+    }
+    const int32_t n = g->n, nwords = (int32_t)(((int64_t)n + 31) / 32);
+    const bool timing = g->timing != 0;
+    g->last_timed = 0;
+    if (timing) {
+        HIP_TRY(ensure_events(g, 2), BFS_EHIP);
+        HIP_TRY(hipEventRecord(g->events[0], stream), BFS_EHIP);
+    }
+    HIP_TRY(launch_sssp_init(g->skey, g->snbm, n, nwords, source, g->sf0, g->sctl, stream), BFS_EHIP);
+    int32_t *F = g->sf0, *Fn = g->sf1;
+    int64_t len = 1;
+    int32_t rounds = 0;
+    for (;;) {
+        if (rounds > n) {
+            set_error("shortest paths did not settle after %d rounds", rounds);
+            return BFS_EDEVICE;
+        }
+        ++rounds;
+        HIP_TRY(launch_var_degrees(g->row_ptr, F, (int32_t)len, g->scnt, stream), BFS_EHIP);
+        HIP_TRY(exclusive_scan(g->scnt, g->soffs, len, g->stmp, stream), BFS_EHIP);
+        SsspRelax R;
+        R.row_ptr = g->row_ptr;
+        R.col_idx = g->col_idx;
+        R.weights = weights;
+        R.max_weight = max_weight;
+        R.source = source;
+        R.F = F;
+        R.len = (int32_t)len;
+        R.offs = g->soffs;
+        R.key = g->skey;
+        R.nbm = g->snbm;
+        R.sc = g->sctl;
+        HIP_TRY(launch_sssp_relax(R, g->grid, stream), BFS_EHIP);
+        HIP_TRY(launch_sssp_compact(g->snbm, nwords, g->scnt, g->soffs, g->stmp, Fn, g->sctl, stream), BFS_EHIP);
+        HIP_TRY(hipMemcpyAsync(g->hsctl, g->sctl, sizeof(SsspCtl), hipMemcpyDeviceToHost, stream), BFS_EHIP);
+        HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+        if (g->hsctl->err) {
+            set_error("an edge weight is above max_weight = %u", max_weight);
+            return BFS_EINVAL;
+        }
+        len = g->hsctl->len;
+        if (len == 0) break;
+        int32_t *t = F;
+        F = Fn;
+        Fn = t;
+    }
+    HIP_TRY(launch_sssp_output(g->skey, n, dist_out, pred_out, stream), BFS_EHIP);
+    if (timing) {
+        HIP_TRY(hipEventRecord(g->events[1], stream), BFS_EHIP);
+        HIP_TRY(hipEventSynchronize(g->events[1]), BFS_EHIP);
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, g->events[0], g->events[1]), BFS_EHIP);
+        g->last_init_ms = 0.f;
+        g->last_level_ms = ms;
+        g->last_launches = rounds;
+        g->last_kind_ms[0] = ms;
+        g->last_kind_ms[1] = 0.f;
+        g->last_kind_launches[0] = rounds;
+        g->last_kind_launches[1] = 0;
+        g->last_timed = 1;
+    }
+    HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+    return rounds;
 }
 
 int32_t bfs_last_run_stats(const bfs_graph *g, int32_t cap, int8_t *dir, int64_t *frontier_edges) {

@@ -205,6 +205,31 @@ hipError_t launch_var_compact_padded(const int32_t *x, int64_t len, int32_t *fla
 hipError_t launch_var_compact_level(const int32_t *dist, int32_t n, int32_t level, int32_t *flag, int32_t *offs,
                                     int32_t *tmp, int32_t *out, hipStream_t s);
 
+// single-source shortest paths (bfs_sssp.hip)
+struct SsspCtl {
+    int32_t err;                   // a weight above the declared maximum was seen
+    int32_t len;                   // length of the frontier just built
+};
+struct SsspRelax {
+    const int32_t *row_ptr, *col_idx;
+    const uint32_t *weights;
+    uint32_t max_weight;
+    int32_t source;
+    const int32_t *F;              // frontier, id order
+    int32_t len;
+    const int32_t *offs;           // exclusive scan of the frontier's degrees (len + 1)
+    unsigned long long *key;       // (distance << 32) | predecessor, all ones = unreached
+    uint32_t *nbm;                 // next-frontier bitmap
+    SsspCtl *sc;
+};
+hipError_t launch_sssp_init(unsigned long long *key, uint32_t *nbm, int32_t n, int32_t nwords, int32_t source,
+                            int32_t *F, SsspCtl *sc, hipStream_t s);
+hipError_t launch_sssp_relax(const SsspRelax &R, int grid, hipStream_t s);
+hipError_t launch_sssp_compact(uint32_t *nbm, int32_t nwords, int32_t *cnt, int32_t *offs, int32_t *tmp,
+                               int32_t *F, SsspCtl *sc, hipStream_t s);
+hipError_t launch_sssp_output(const unsigned long long *key, int32_t n, int64_t *dist, int32_t *pred,
+                              hipStream_t s);
+
 // isolated neighbour walk of listed vertices (bfs_walk.hip); scratch holds
 // walk_scratch_ints(count) ints, bad is raised for ids outside [0, n)
 int64_t walk_scratch_ints(int64_t count);

@@ -211,6 +211,27 @@ int32_t bfs_last_run_kernel_timing(const bfs_graph *g, float *td_ms, int32_t *td
 int32_t bfs_set_primitives(bfs_graph *g, int32_t claim, int32_t compaction);
 
 /*
+ * Single-source shortest paths over the same CSR and frontier machinery: the
+ * atomic-min relaxation that the Gunrock reading guide (step 2) extends the
+ * BFS lambda to, where a neighbour wins only with a strictly smaller
+ * distance.  weights (device, m entries, uint32) holds the weight of each CSR
+ * entry (row u to col_idx[e]); every weight must be at most max_weight, and
+ * n * max_weight must stay below 2^32 - 1 (distances are kept in 32 bits).
+ * dist_out (device, n int64): the shortest distance, -1 if unreachable.
+ * pred_out (device, n int32, or NULL): the smallest u with an entry u -> v
+ * and dist[u] + w = dist[v]; the source's own id for the source; -1 if
+ * unreachable.  Both are unique, so results compare exactly.  Rounds of
+ * frontier relaxation run until no distance drops; the host reads one counter
+ * per round.  Uses the handle's SSSP buffers (about 24n bytes, allocated on
+ * the first call); must not overlap other calls on the handle.  Returns the
+ * number of rounds (>= 1); BFS_EINVAL for a NULL handle or buffer, a source
+ * outside [0, n), a max_weight that breaks the bound, or a weight above
+ * max_weight (then the outputs are unspecified); BFS_ENOMEM; BFS_EHIP.
+ */
+int32_t bfs_sssp(bfs_graph *g, int32_t source, const uint32_t *weights, uint32_t max_weight,
+                 int64_t *dist_out, int32_t *pred_out, hipStream_t stream);
+
+/*
  * Isolated neighbour walk of one level: the measurement the "Day 38 - Graph
  * traversal on a GPU" page uses to compare thread-to-work mappings without
  * the atomics, frontier build and distance writes of a real level (section

@@ -42,6 +42,7 @@ def test_host_side_argument_errors():
     assert lib.bfs_last_run_kernel_timing(None, None, None, None, None) == fb.BFS_EINVAL
     assert lib.bfs_walk_level(None, None, 0, 0, 64, None, None) == fb.BFS_EINVAL
     assert lib.bfs_set_primitives(None, 0, 1) == fb.BFS_EINVAL
+    assert lib.bfs_sssp(None, 0, None, 1, None, None, None) == fb.BFS_EINVAL
     assert lib.bfs_last_run_stats(None, 0, None, None) == fb.BFS_EINVAL
     assert lib.bfs_graph_info(None, None, None, None, None, None) == fb.BFS_EINVAL
     lib.bfs_graph_destroy(None)   # no-op
