@@ -74,6 +74,9 @@ __global__ __launch_bounds__(BLOCK) void sssp_relax_kernel(SsspRelax R) {
             const uint32_t dv = (uint32_t)(R.key[v] >> 32);
             const uint32_t nd = dv + w;
             const unsigned long long nk = ((unsigned long long)nd << 32) | (uint32_t)v;
+            // a plain read first: most relaxations of a heavy round lose, and
+            // keys only fall, so a key already at or below nk stays so
+            if (nk >= R.key[u]) continue;
             const unsigned long long old = atomicMin(R.key + u, nk);
             if (nd < (uint32_t)(old >> 32)) atomicOr(R.nbm + (u >> 5), 1u << (u & 31));
         }
