@@ -3,6 +3,7 @@
 // include/frontier_bfs.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -30,6 +31,7 @@ void set_error(const char *fmt, ...) {
 
 struct HostCtl {
     int32_t done, L, err, err_info;
+    uint8_t ran[RAN_CAP];   // the device's record of the launches that ran a level
 };
 
 }  // namespace
@@ -61,6 +63,10 @@ struct bfs_graph {
     GraphFacts *facts = nullptr;   // device, create only
     int32_t pol_dir = BFS_DIR_AUTO, pol_adv = BFS_ADV_AUTO, pol_loop = BFS_LOOP_DEVICE;
     int32_t pol_claim = BFS_CLAIM_BITMAP, pol_compact = BFS_COMPACT_DEFAULT;
+    // launch kinds (1 top-down, 2 bottom-up) that cover the working launches
+    // of the searches on this handle: each search's sequence of working
+    // launches is a subsequence of it.  The next search enqueues it first.
+    std::vector<uint8_t> plan;
     // buffers of the alternative compactions (allocated when one is chosen):
     // two frontiers, flags/degrees, their scan, scan temporaries
     int32_t *va = nullptr, *vb = nullptr, *vs = nullptr, *vo = nullptr, *vt = nullptr;
@@ -266,6 +272,34 @@ hipError_t build_in_edges(bfs_graph *g) {
     (void)hipFree(tmp);
     if (e == hipSuccess) g->can_pull = 1;
     return e;
+}
+
+// The shortest sequence holding both a and b as subsequences (a shortest
+// common supersequence, by the textbook dynamic programme); b alone when that
+// is more than 4 longer than b, so a plan stays close to recent searches.
+std::vector<uint8_t> merge_plan(const std::vector<uint8_t> &a, const std::vector<uint8_t> &b) {
+    const size_t p = a.size(), q = b.size();
+    if (p == 0) return b;
+    // len[i][j]: shortest supersequence of a[i..] and b[j..]
+    std::vector<std::vector<int32_t>> len(p + 1, std::vector<int32_t>(q + 1, 0));
+    for (size_t i = p + 1; i-- > 0;)
+        for (size_t j = q + 1; j-- > 0;) {
+            if (i == p) len[i][j] = (int32_t)(q - j);
+            else if (j == q) len[i][j] = (int32_t)(p - i);
+            else if (a[i] == b[j]) len[i][j] = 1 + len[i + 1][j + 1];
+            else len[i][j] = 1 + std::min(len[i + 1][j], len[i][j + 1]);
+        }
+    if (len[0][0] > (int32_t)q + 4) return b;
+    std::vector<uint8_t> out;
+    size_t i = 0, j = 0;
+    while (i < p || j < q) {
+        if (i == p) out.push_back(b[j++]);
+        else if (j == q) out.push_back(a[i++]);
+        else if (a[i] == b[j]) { out.push_back(a[i]); ++i; ++j; }
+        else if (len[i + 1][j] <= len[i][j + 1]) out.push_back(a[i++]);
+        else out.push_back(b[j++]);
+    }
+    return out;
 }
 
 // Buffers of the alternative compactions: frontiers of up to max(n, m)
@@ -494,6 +528,7 @@ int32_t bfs_set_policy(bfs_graph *g, int32_t direction, int32_t advance, int32_t
     g->pol_dir = direction;
     g->pol_adv = advance;
     g->pol_loop = loop;
+    g->plan.clear();
     return 0;
 }
 
@@ -518,6 +553,7 @@ int32_t bfs_set_primitives(bfs_graph *g, int32_t claim, int32_t compaction) {
     }
     g->pol_claim = claim;
     g->pol_compact = compaction;
+    g->plan.clear();
     return 0;
 }
 
@@ -533,6 +569,7 @@ int32_t bfs_set_switch(bfs_graph *g, int32_t alpha, int32_t beta) {
     }
     g->alpha = alpha;
     g->beta = beta;
+    g->plan.clear();
     return 0;
 }
 
@@ -610,23 +647,36 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     if (timing) HIP_TRY(hipEventRecord(g->events[1], stream), BFS_EHIP);
     const bool host_loop = g->pol_loop == BFS_LOOP_HOST;
     int64_t k = 0;
-    // a first batch of 12 launches covers most searches of under ten levels
-    int64_t batch = host_loop ? 1 : 12;
+    // Launch kinds: searches on one graph tend to repeat their pattern of
+    // directions, so the first batch is the plan (a shortest sequence that
+    // holds the working launches of the recent searches in order) plus one
+    // top-down launch (it finds the end after a last bottom-up level); without
+    // a plan, a batch of 12 that alternates top-down and bottom-up, which
+    // covers most searches of under ten levels.  Later batches alternate.  A launch whose level belongs to the other direction
+    // passes it on, so the order only costs time, never results.
+    const std::vector<uint8_t> plan = host_loop ? std::vector<uint8_t>() : g->plan;
+    const int64_t prefix = plan.empty() ? 0 : (int64_t)plan.size() + 1;
+    int64_t batch = host_loop ? 1 : (prefix ? prefix : 12);
+    bool prev_bu = true;   // so that alternation starts top-down
+    std::vector<uint8_t> kinds;
     float level_ms = 0.f, kind_ms[2] = {0.f, 0.f};
     int32_t kind_launches[2] = {0, 0};
-    // launches alternate top-down (even index) and bottom-up (odd index); each
-    // pair runs at least one level or finds the empty frontier, and L <= n,
-    // so launch 2n + 1 has found it
-    const int64_t kmax = 2 * (int64_t)g->n + 2;
+    // outside the prefix, launches alternate top-down and bottom-up; each pair
+    // runs at least one level or finds the empty frontier, and L <= n, so
+    // launch prefix + 2n + 1 has found it
+    const int64_t kmax = 2 * (int64_t)g->n + 2 + prefix;
     for (;;) {
         const int64_t k0 = k;
+        kinds.clear();
         if (timing) {
             HIP_TRY(ensure_events(g, 2 + (size_t)batch + 1), BFS_EHIP);
             HIP_TRY(hipEventRecord(g->events[2], stream), BFS_EHIP);
         }
         for (int64_t i = 0; i < batch && k <= kmax; ++i, ++k) {
-            HIP_TRY(launch_level(P, (int32_t)k, (k & 1) ? g->grid_bu : g->grid, stream),
-                    BFS_EHIP);   // k = launch index
+            const bool bu = k < prefix ? (k < (int64_t)plan.size() && plan[k] == 2) : !prev_bu;
+            prev_bu = bu;
+            kinds.push_back(bu ? 1 : 0);
+            HIP_TRY(launch_level(P, (int32_t)k, bu, bu ? g->grid_bu : g->grid, stream), BFS_EHIP);   // k = launch index
             if (timing) HIP_TRY(hipEventRecord(g->events[3 + i], stream), BFS_EHIP);
         }
         HIP_TRY(hipMemcpyAsync(g->host_ctl, g->ctl, sizeof(HostCtl), hipMemcpyDeviceToHost, stream),
@@ -637,12 +687,13 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
                 float ms = 0.f;
                 HIP_TRY(hipEventElapsedTime(&ms, g->events[2 + i], g->events[3 + i]), BFS_EHIP);
                 level_ms += ms;
-                kind_ms[(k0 + i) & 1] += ms;
-                kind_launches[(k0 + i) & 1] += 1;
+                kind_ms[kinds[i]] += ms;
+                kind_launches[kinds[i]] += 1;
             }
         }
-        const HostCtl h = *g->host_ctl;
+        const HostCtl &h = *g->host_ctl;
         if (h.err) {
+            g->plan.clear();
             if (h.err == ERR_BARRIER_TIMEOUT)
                 set_error("small-frontier barrier wait exceeded its limit (%u ticks)", g->barrier_ticks);
             else
@@ -651,6 +702,15 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
         }
         if (h.done) {
             g->last_L = h.L;
+            // this search's working launches, merged into the plan
+            if (host_loop || k > RAN_CAP) {
+                g->plan.clear();
+            } else {
+                std::vector<uint8_t> seq;
+                for (int64_t i = 0; i < k; ++i)
+                    if (h.ran[i]) seq.push_back(h.ran[i]);
+                g->plan = merge_plan(g->plan, seq);
+            }
             if (timing) {
                 float ms = 0.f;
                 HIP_TRY(hipEventElapsedTime(&ms, g->events[0], g->events[1]), BFS_EHIP);
@@ -666,10 +726,11 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
             return h.L;
         }
         if (k > kmax) {
+            g->plan.clear();
             set_error("search did not terminate after %lld level launches", (long long)k);
             return BFS_EDEVICE;
         }
-        if (!host_loop && batch < 1024) batch *= 2;
+        if (!host_loop && batch < 1024) batch = batch < 12 ? 12 : batch * 2;
     }
 }
 

@@ -1007,6 +1007,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
             P.ctr[(size_t)i * CTR_STRIDE] = 0ull;
         if (threadIdx.x == 0) {
             P.ctl->done = 0; P.ctl->L = 0; P.ctl->err = 0; P.ctl->err_info = 0;
+            for (int i = 0; i < RAN_CAP; ++i) P.ctl->ran[i] = 0;
             P.ctl->lvl[0] = 0; P.ctl->lvl[1] = 0;
             P.ctl->bar_count = 0; P.ctl->bar_gen = 0;
             for (int k = 0; k < NSLOTS; ++k) {
@@ -1286,6 +1287,7 @@ __global__ __launch_bounds__(BLOCK, 4) void bfs_td_kernel(Params P, int32_t laun
         }
         const bool small = sh.small;
         run_level<false>(P, sh, k, blockIdx.x, G);
+        if (blockIdx.x == 0 && threadIdx.x == 0 && launch < RAN_CAP) P.ctl->ran[launch] = 1;
         ++k;
         if (!small) break;
         small_barrier(P, G);
@@ -1304,6 +1306,7 @@ __global__ __launch_bounds__(BLOCK, 6) void bfs_bu_kernel(Params P, int32_t laun
         return;
     }
     run_level<true>(P, sh, k, blockIdx.x, (int)gridDim.x);
+    if (blockIdx.x == 0 && threadIdx.x == 0 && launch < RAN_CAP) P.ctl->ran[launch] = 2;
     set_next_level(P, launch, k + 1);
 }
 
@@ -1390,8 +1393,8 @@ hipError_t launch_init(const Params &P, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_level(const Params &P, int32_t launch_index, int grid, hipStream_t s) {
-    if (launch_index & 1)
+hipError_t launch_level(const Params &P, int32_t launch_index, bool bottom_up, int grid, hipStream_t s) {
+    if (bottom_up)
         hipLaunchKernelGGL(bfs_bu_kernel, dim3(grid), dim3(BLOCK), 0, s, P, launch_index);
     else
         hipLaunchKernelGGL(bfs_td_kernel, dim3(grid), dim3(BLOCK), 0, s, P, launch_index);

@@ -73,11 +73,16 @@ struct SlotInfo {
     int64_t edges_before;    // sum of degrees of the vertices in levels < this one
 };
 
+constexpr int RAN_CAP = 64;               // launches whose kind of work is recorded
+
 struct Ctl {
     int32_t done;         // set by the kernel that finds an empty frontier
     int32_t L;            // number of non-empty levels
     int32_t err;          // nonzero: internal limit exceeded (see ERR_*)
     int32_t err_info;
+    // ran[i]: launch i ran a level top-down (1) or bottom-up (2), else 0;
+    // read by the host with the status words, to order the next search's launches
+    uint8_t ran[RAN_CAP];
     int32_t lvl[2];       // level the launch with index i starts at: lvl[i & 1]
     int32_t pad0[2];
     SlotInfo slot[NSLOTS];
@@ -147,7 +152,7 @@ struct Params {
 hipError_t launch_init(const Params &P, int grid, hipStream_t s);
 // launch `launch_index` of the level chain: even indexes run the top-down
 // kernel, odd ones the bottom-up kernel
-hipError_t launch_level(const Params &P, int32_t launch_index, int grid, hipStream_t s);
+hipError_t launch_level(const Params &P, int32_t launch_index, bool bottom_up, int grid, hipStream_t s);
 // resident workgroups per compute unit of the top-down or bottom-up kernel
 int level_kernel_blocks_per_cu(bool bottom_up);
 

@@ -136,6 +136,40 @@ def test_timing_hooks():
             bg.set_timing(False)
 
 
+def test_launch_plan_follows_last_search():
+    """A search enqueues the previous search's working launches (plus one
+    top-down launch) first: the repeated search uses no more launches, and
+    searches whose direction pattern differs from the last one, or that run
+    longer than the recorded launches, still give the oracle's result."""
+    import frontier_bfs_csr_amd as fb
+    g = gg.rmat(15, 16, seed=7, nsrc=4)
+    rp, ci = to_dev(g)
+    with fb.BfsGraph(rp, ci) as bg:
+        bg.set_timing(True)
+        s0 = int(g.sources[0])
+        run_hip(bg, g.n, s0)
+        first = bg.timing()[2]
+        run_hip(bg, g.n, s0)
+        again = bg.timing()[2]
+        assert again <= first, (first, again)
+        leaves = np.nonzero(np.diff(g.row_ptr) == 1)[0][:3]
+        for s in list(g.sources) + [int(x) for x in leaves] + [s0]:
+            L, dist, parent, sizes = run_hip(bg, g.n, int(s))
+            ref = oracle.bfs(g.row_ptr, g.col_idx, int(s))
+            oracle.assert_bfs_ok(g.row_ptr, g.col_idx, int(s), ref, dist, parent, L, sizes[:L],
+                                 label=f"plan rmat15 s={s}")
+            kt = bg.kernel_timing()
+            assert kt["td"][1] + kt["bu"][1] == bg.timing()[2]
+    for h in (gg.grid_full(50, 40), gg.disjoint_union(gg.star_graph(3000), gg.path_graph(200))):
+        rp, ci = to_dev(h)
+        with fb.BfsGraph(rp, ci) as bg:
+            for s in (0, h.n - 1, 0, h.n // 2, h.n - 1):
+                L, dist, parent, sizes = run_hip(bg, h.n, s)
+                ref = oracle.bfs(h.row_ptr, h.col_idx, s)
+                oracle.assert_bfs_ok(h.row_ptr, h.col_idx, s, ref, dist, parent, L, sizes[:L],
+                                     label=f"plan {h.name} s={s}")
+
+
 def test_optional_outputs():
     import torch
     import frontier_bfs_csr_amd as fb
