@@ -505,16 +505,22 @@ __device__ __forceinline__ void td_edge_balanced(Ctx &c, const Seg *cq, const Se
     int32_t *s_off = sh.work;
     int32_t *s_v = sh.work + (EB_TE + 1);
     int32_t *s_beg = sh.work + 2 * (EB_TE + 1);
-    const int total = sh.uprefix[NLISTS * STRIPES];
+    const int tiles = sh.uprefix[NLISTS * STRIPES];
+    // fewer tiles than workgroups: each tile is cut into 2 or 4 parts, each
+    // part one workgroup's unit (all parts stage the tile's segments)
+    const int spl = (4 * tiles <= c.G) ? 4 : ((2 * tiles <= c.G) ? 2 : 1);
+    const int total = tiles * spl;
     for (int u = c.wg; u < total; u += c.G) {
+        const int ut = u / spl, part = u % spl;
         int r = 0;
-        while (sh.uprefix[r + 1] <= u) ++r;
+        while (sh.uprefix[r + 1] <= ut) ++r;
         const int l = r / STRIPES, s = r % STRIPES;
-        const int t = u - sh.uprefix[r];
+        const int t = ut - sh.uprefix[r];
         const int E = sh.ledges[r];
         const int N = sh.lcount[r];
         const int a = t * EB_TE;
-        const int b = min(a + EB_TE, E);   // at most STEP_CLAIMS winners
+        const int pa = a + part * (EB_TE / spl);                 // this part's edges
+        const int pb = min(pa + EB_TE / spl, E);                  // (at most STEP_CLAIMS winners)
         const int32_t *ts = cts + (size_t)r * P.tscap;
         const int i0 = ts[t];
         const int i1 = (a + EB_TE < E) ? ts[t + 1] : N - 1;
@@ -532,13 +538,13 @@ __device__ __forceinline__ void td_edge_balanced(Ctx &c, const Seg *cq, const Se
         static_assert(EB_TE % BLOCK == 0 && EB_TE <= STEP_CLAIMS, "one step per tile");
         constexpr int NB = EB_TE / BLOCK;
         {
-            const int e0 = a + (int)threadIdx.x;
+            const int e0 = pa + (int)threadIdx.x;
             int tv[NB], owner[NB];
             bool ok[NB];
 #pragma unroll
             for (int q = 0; q < NB; ++q) {
                 const int e = e0 + q * BLOCK;
-                ok[q] = e < b;
+                ok[q] = e < pb;
                 // last j with s_off[j] <= e
                 int lo = 0, hi = ns;
                 while (hi - lo > 1) {
@@ -1156,20 +1162,21 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
             sh.vfilter = sh.fdeg >= VFILTER_EDGES;
         }
     }
-    // unit prefix tables
-    if (threadIdx.x == 0) {
-        int acc = 0;
-        for (int r = 0; r < NLISTS * STRIPES; ++r) {
-            sh.uprefix[r] = acc;
+    // unit prefix tables: one lane per (list, stripe) and a wavefront scan
+    // (a serial loop here waits out one LDS round trip per entry)
+    if (threadIdx.x < WAVE) {
+        const int r = threadIdx.x;
+        int units = 0;
+        if (r < NLISTS * STRIPES) {
             const int l = r / STRIPES;
-            int units;
             if (sh.adv_eb) units = (sh.ledges[r] + EB_TE - 1) / EB_TE;
             else if (l == L_TILE) units = sh.lcount[r];
             else if (l == L_MID) units = (sh.lcount[r] + WAVES - 1) / WAVES;
             else units = (sh.lcount[r] + BLOCK - 1) / BLOCK;
-            acc += units;
         }
-        sh.uprefix[NLISTS * STRIPES] = acc;
+        const int incl = wave_incl_scan_i32(units);
+        if (r < NLISTS * STRIPES) sh.uprefix[r] = incl - units;
+        if (r == NLISTS * STRIPES - 1) sh.uprefix[NLISTS * STRIPES] = incl;
     }
     // bookkeeping of level k by workgroup 0
     if (wg == 0) {
