@@ -934,17 +934,30 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
 #pragma unroll
             for (int q = 0; q < FW; ++q)
                 w[q] = (f[q] >= 0 && cf_maybe(sh, use_cf, cf_sh, f[q])) ? cbm[f[q] >> 5] : 0u;
+            // a miss with more in-neighbours tries its second probe neighbour
+            bool h1[FW];
+            int f2[FW];
 #pragma unroll
             for (int q = 0; q < FW; ++q) {
-                const bool hitq = f[q] >= 0 && ((w[q] >> (f[q] & 31)) & 1u);
+                h1[q] = f[q] >= 0 && ((w[q] >> (f[q] & 31)) & 1u);
+                f2[q] = (!h1[q] && v[q] >= 0 && e[q] - b[q] > 1) ? P.snb[v[q]] : -1;
+            }
+#pragma unroll
+            for (int q = 0; q < FW; ++q)
+                w[q] = (f2[q] >= 0 && cf_maybe(sh, use_cf, cf_sh, f2[q])) ? cbm[f2[q] >> 5] : 0u;
+#pragma unroll
+            for (int q = 0; q < FW; ++q) {
+                const int par = h1[q] ? f[q] : ((f2[q] >= 0 && ((w[q] >> (f2[q] & 31)) & 1u)) ? f2[q] : -1);
+                const bool hitq = par >= 0;
                 if (hitq) {
                     P.dist[v[q]] = c.level + 1;
-                    if (P.parent) P.parent[v[q]] = f[q];
+                    if (P.parent) P.parent[v[q]] = par;
                     c.fcnt += 1;
                     c.fdeg += P.symmetric ? e[q] - b[q] : P.row_ptr[v[q] + 1] - P.row_ptr[v[q]];
                 }
                 const uint64_t hm = __ballot(hitq);
-                const uint64_t rm = __ballot(v[q] >= 0 && !hitq && e[q] - b[q] > 1);
+                // two probes settle a vertex with two in-neighbours
+                const uint64_t rm = __ballot(v[q] >= 0 && !hitq && e[q] - b[q] > 2);
                 if (lane == jw[q]) {
                     myrest = rm;
                     if (hm) sh.bu_fm[wv][lane] = hm;
@@ -1507,41 +1520,51 @@ __global__ __launch_bounds__(256) void transpose_fill_kernel(const int32_t *row_
 }
 
 // Probe-neighbour index: for every vertex v the in-neighbour of highest
-// out-degree (the first in CSR order among equals), -1 without in-neighbours.
-// Hubs are reached in the first levels, so this is the in-neighbour most
-// likely to be in a bottom-up level's frontier.  One wavefront per vertex.
+// out-degree (the first in CSR order among equals), and the one after it
+// (second highest), -1 where there is none.  Hubs are reached in the first
+// levels, so these are the in-neighbours most likely to be in a bottom-up
+// level's frontier.  One wavefront per vertex; each lane keeps its best two
+// entries as keys (out-degree << 32 | ~entry), merged across the wavefront.
+__device__ __forceinline__ void top2_insert(unsigned long long &k1, unsigned long long &k2, unsigned long long x) {
+    if (x > k1) {
+        k2 = k1;
+        k1 = x;
+    } else if (x > k2) {
+        k2 = x;
+    }
+}
+
 __global__ __launch_bounds__(256) void probe_nb_kernel(const int32_t *row_ptr, const int32_t *in_row_ptr,
-                                                       const int32_t *in_col, int32_t n, int32_t *pnb) {
+                                                       const int32_t *in_col, int32_t n, int32_t *pnb,
+                                                       int32_t *snb) {
     const int lane = lane_id();
     const int64_t nw = (int64_t)gridDim.x * (blockDim.x / WAVE);
     for (int64_t v = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE; v < n; v += nw) {
         const int b = in_row_ptr[v], e = in_row_ptr[v + 1];
-        int best_d = -1, best_j = 0x7fffffff;
+        unsigned long long k1 = 0ull, k2 = 0ull;   // 0: none (a real key has ~entry > 0)
         for (int j = b + lane; j < e; j += WAVE) {
             const int u = in_col[j];
-            const int d = row_ptr[u + 1] - row_ptr[u];
-            if (d > best_d) {   // a lane's entries rise, so the first among equals stays
-                best_d = d;
-                best_j = j;
-            }
+            const uint32_t d = (uint32_t)(row_ptr[u + 1] - row_ptr[u]);
+            top2_insert(k1, k2, ((unsigned long long)d << 32) | (uint32_t)(0x7fffffff - j));
         }
 #pragma unroll
         for (int off = WAVE / 2; off > 0; off >>= 1) {
-            const int od = __shfl_xor(best_d, off, WAVE);
-            const int oj = __shfl_xor(best_j, off, WAVE);
-            if (od > best_d || (od == best_d && oj < best_j)) {
-                best_d = od;
-                best_j = oj;
-            }
+            const unsigned long long o1 = __shfl_xor(k1, off, WAVE);
+            const unsigned long long o2 = __shfl_xor(k2, off, WAVE);
+            top2_insert(k1, k2, o1);
+            top2_insert(k1, k2, o2);
         }
-        if (lane == 0) pnb[v] = best_d >= 0 ? in_col[best_j] : -1;
+        if (lane == 0) {
+            pnb[v] = k1 ? in_col[0x7fffffff - (int)(uint32_t)(k1 & 0xffffffffull)] : -1;
+            snb[v] = k2 ? in_col[0x7fffffff - (int)(uint32_t)(k2 & 0xffffffffull)] : -1;
+        }
     }
 }
 
 hipError_t launch_build_probe_nb(const int32_t *row_ptr, const int32_t *in_row_ptr, const int32_t *in_col,
-                                 int32_t n, int32_t *pnb, hipStream_t s) {
+                                 int32_t n, int32_t *pnb, int32_t *snb, hipStream_t s) {
     hipLaunchKernelGGL(probe_nb_kernel, dim3(grid_for(n, 4 * 16)), dim3(256), 0, s, row_ptr, in_row_ptr,
-                       in_col, n, pnb);
+                       in_col, n, pnb, snb);
     return hipGetLastError();
 }
 

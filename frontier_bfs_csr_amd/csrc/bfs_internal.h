@@ -121,6 +121,7 @@ struct Params {
     const int32_t *in_row_ptr;
     const int32_t *in_col_idx;
     const int32_t *pnb;       // n entries: in-neighbour of highest out-degree, -1 if none
+    const int32_t *snb;       // n entries: in-neighbour of second highest out-degree, -1 if none
     uint32_t *fbm0, *fbm1;    // frontier bitmaps, 2*nwp words each
     Seg *q0, *q1;             // STRIPES regions of qcap segments (small from the front,
                               // mid from the back)
@@ -173,7 +174,7 @@ hipError_t launch_check_symmetry(const int32_t *row_ptr, const int32_t *col_idx,
 hipError_t launch_build_vis_init(const int32_t *row_ptr, int32_t n, int32_t mark_isolated,
                                  uint32_t *vis_init, hipStream_t s);
 hipError_t launch_build_probe_nb(const int32_t *row_ptr, const int32_t *in_row_ptr, const int32_t *in_col,
-                                 int32_t n, int32_t *pnb, hipStream_t s);
+                                 int32_t n, int32_t *pnb, int32_t *snb, hipStream_t s);
 // transpose (in-edge CSR) of a CSR: in-degree counts, exclusive scan, scatter
 hipError_t launch_in_degree(const int32_t *col_idx, int32_t m, int32_t *cnt, hipStream_t s);
 // exclusive scan of cnt[0, n) into out[0, n]; tmp holds scan_tmp_ints(n) ints
