@@ -172,7 +172,7 @@ def bfs_set_primitives(g, claim=CLAIM_BITMAP, compaction=COMPACT_DEFAULT):
         raise BfsError(rc, bfs_last_error())
 
 
-def bfs_set_switch(g, alpha=28, beta=24):
+def bfs_set_switch(g, alpha=40, beta=48):
     rc = load().bfs_set_switch(g, int(alpha), int(beta))
     if rc < 0:
         raise BfsError(rc, bfs_last_error())
@@ -259,7 +259,7 @@ class BfsGraph:
     def walk(self, vertices, out, mapping=WALK_WAVE, repeats=64, stream=None):
         bfs_walk_level(self.handle, vertices, out, mapping, repeats, stream)
 
-    def set_switch(self, alpha=28, beta=24):
+    def set_switch(self, alpha=40, beta=48):
         bfs_set_switch(self.handle, alpha, beta)
 
     def set_primitives(self, claim=CLAIM_BITMAP, compaction=COMPACT_DEFAULT):

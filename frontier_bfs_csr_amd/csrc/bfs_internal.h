@@ -35,8 +35,8 @@ constexpr int CF_WORDS = 4096;           // coarse frontier map: at most 4096 wo
 // when the frontier's edges exceed 1/alpha of the unexplored vertices' edges;
 // come back top-down when the frontier is under n/beta and shrinking.  These
 // are the defaults; bfs_set_switch changes them per handle.
-constexpr int ALPHA = 28;
-constexpr int BETA = 24;
+constexpr int ALPHA = 40;
+constexpr int BETA = 48;
 
 // lists of a frontier queue
 constexpr int L_SMALL = 0;               // degree in [1, T_LANE)

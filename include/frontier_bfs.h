@@ -128,9 +128,10 @@ int32_t bfs_set_policy(bfs_graph *g, int32_t direction, int32_t advance, int32_t
 
 /*
  * Direction-switch parameters of the automatic policy, for later bfs_run calls
- * on this handle (defaults 28 and 24: Beamer, Asanovic and Patterson, SC 2012,
+ * on this handle (defaults 40 and 48: Beamer, Asanovic and Patterson, SC 2012,
  * use 14 and 24 on CPUs; the bottom-up pass here is cheap enough relative to
- * the top-down one that pulling earlier measured best on R-MAT scale 24).  After a top-down level, the next level pulls when
+ * the top-down one that pulling earlier and pushing again later measured
+ * best on the R-MAT and Erdos-Renyi graphs).  After a top-down level, the next level pulls when
  * alpha * (sum of degrees of the frontier) exceeds the degree sum of the
  * vertices not yet reached; after a bottom-up level, it pushes again when
  * beta * |frontier| < n and the frontier shrank.  The PMPP chapter 15 notes
