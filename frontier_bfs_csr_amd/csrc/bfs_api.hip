@@ -857,6 +857,10 @@ int32_t bfs_sssp(bfs_graph *g, int32_t source, const uint32_t *weights, uint32_t
         R.key = g->skey;
         R.nbm = g->snbm;
         R.sc = g->sctl;
+        R.round = rounds - 1;
+        R.st_dir = g->st_dir;
+        R.st_fdeg = g->st_fdeg;
+        R.st_cap = g->st_cap;
         HIP_TRY(launch_sssp_relax(R, g->grid, stream), BFS_EHIP);
         HIP_TRY(launch_sssp_compact(g->snbm, nwords, g->scnt, g->soffs, g->stmp, Fn, g->sctl, stream), BFS_EHIP);
         HIP_TRY(hipMemcpyAsync(g->hsctl, g->sctl, sizeof(SsspCtl), hipMemcpyDeviceToHost, stream), BFS_EHIP);
@@ -872,6 +876,7 @@ int32_t bfs_sssp(bfs_graph *g, int32_t source, const uint32_t *weights, uint32_t
         Fn = t;
     }
     HIP_TRY(launch_sssp_output(g->skey, n, dist_out, pred_out, stream), BFS_EHIP);
+    g->last_L = rounds;   // bfs_last_run_stats: the frontier edges of each round
     if (timing) {
         HIP_TRY(hipEventRecord(g->events[1], stream), BFS_EHIP);
         HIP_TRY(hipEventSynchronize(g->events[1]), BFS_EHIP);

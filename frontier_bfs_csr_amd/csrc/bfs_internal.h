@@ -227,6 +227,10 @@ struct SsspRelax {
     unsigned long long *key;       // (distance << 32) | predecessor, all ones = unreached
     uint32_t *nbm;                 // next-frontier bitmap
     SsspCtl *sc;
+    int32_t round;                 // this round's number, for the per-round stats
+    int8_t *st_dir;
+    int64_t *st_fdeg;              // frontier edges of each round (the relaxations it tries)
+    int32_t st_cap;
 };
 hipError_t launch_sssp_init(unsigned long long *key, uint32_t *nbm, int32_t n, int32_t nwords, int32_t source,
                             int32_t *F, SsspCtl *sc, hipStream_t s);

@@ -50,6 +50,10 @@ __global__ __launch_bounds__(BLOCK) void sssp_relax_kernel(SsspRelax R) {
     K = K < 1 ? 1 : (K > SSSP_K ? SSSP_K : K);
     const int64_t runs = (E + K - 1) / K;
     const int lane = (int)__lane_id();
+    if (blockIdx.x == 0 && threadIdx.x == 0 && R.round < R.st_cap) {
+        R.st_dir[R.round] = 0;
+        R.st_fdeg[R.round] = E;
+    }
     bool bad = false;
     for (int64_t t0 = (int64_t)blockIdx.x * BLOCK + (threadIdx.x & ~(WAVE - 1)); t0 < runs; t0 += nth) {
         const int64_t t = t0 + lane;

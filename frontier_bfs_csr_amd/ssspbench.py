@@ -4,7 +4,9 @@ give no weights, so every CSR entry gets a seeded uniform weight in [1, 255]
 (numpy PCG64).  Per source: a warm-up call, then --runs timed calls (wall
 time around the call, which returns after the last round); distances and
 predecessors of the first --check sources are compared with the oracle's
-Dijkstra, whose time is the CPU baseline.
+Dijkstra, whose time is the CPU baseline.  Algorithmic bytes per call count
+init, output and 16 bytes per relaxation tried (bfs_last_run_stats gives the
+frontier edges of every round), against 8 TB/s.
 
     python -m frontier_bfs_csr_amd.ssspbench [--workload c2] [--sources 8]
 
@@ -25,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 WMAX = 255
+
 
 
 def main():
@@ -62,6 +65,12 @@ def main():
                 t0 = time.perf_counter()
                 rounds = bg.sssp(s, wd, WMAX, dist, pred)
                 ts.append(time.perf_counter() - t0)
+            _, _, fe = bg.stats()
+            relax = int(fe.sum())
+            # algorithmic bytes, counted low: init (8n keys), output (12n) and,
+            # per frontier edge, the neighbour id, weight and target key (16);
+            # the frontier vertices' own reads are left out
+            alg = 8 * g.n + 12 * g.n + 16 * relax
             d = dist.cpu().numpy()
             reached = d >= 0
             # edges in the source's component (each undirected edge once on
@@ -69,7 +78,8 @@ def main():
             medges = int(deg[reached].sum()) // (2 if g.symmetric else 1)
             ms = float(np.mean(ts)) * 1e3
             row = {"source": s, "rounds": rounds, "ms": round(ms, 4), "reached": int(reached.sum()),
-                   "gteps": round(medges / (ms * 1e-3) / 1e9, 3), "max_dist": int(d.max())}
+                   "gteps": round(medges / (ms * 1e-3) / 1e9, 3), "max_dist": int(d.max()),
+                   "relaxations": relax, "alg_GB_per_s": round(alg / (ms * 1e-3) / 1e9, 1)}
             if k < args.check:
                 import oracle   # the parity check and CPU baseline: the oracle as it stands
                 t0 = time.perf_counter()
@@ -79,7 +89,8 @@ def main():
                 row["oracle_ms"] = round(cpu_s * 1e3, 1)
                 cpu.append((medges, cpu_s))
             rows.append(row)
-            print(f"[sssp] source {s}: {rounds} rounds, {ms:.3f} ms, {row['gteps']} GTEPS"
+            print(f"[sssp] source {s}: {rounds} rounds, {relax} relaxations, {ms:.3f} ms, {row['gteps']} GTEPS, "
+                  f"{row['alg_GB_per_s']} GB/s algorithmic"
                   + (f", oracle {row['oracle_ms']} ms, equal {row['oracle_equal']}" if k < args.check else ""),
                   file=sys.stderr, flush=True)
     ms_all = [r["ms"] for r in rows]
@@ -88,6 +99,8 @@ def main():
            "gteps_hmean": round(len(rows) / sum(1.0 / r["gteps"] for r in rows), 3),
            "rounds_median": int(np.median([r["rounds"] for r in rows])),
            "cpu_oracle_gteps": round(sum(e for e, _ in cpu) / sum(t for _, t in cpu) / 1e9, 4) if cpu else None,
+           "alg_GB_per_s_median": round(float(np.median([r["alg_GB_per_s"] for r in rows])), 1),
+           "roofline_frac_median": round(float(np.median([r["alg_GB_per_s"] for r in rows])) / 8000.0, 4),
            "oracle_equal_all": all(r.get("oracle_equal", True) for r in rows), "sources": rows}
     print(json.dumps(out))
 

@@ -223,7 +223,8 @@ int32_t bfs_set_primitives(bfs_graph *g, int32_t claim, int32_t compaction);
  * and dist[u] + w = dist[v]; the source's own id for the source; -1 if
  * unreachable.  Both are unique, so results compare exactly.  Rounds of
  * frontier relaxation run until no distance drops; the host reads one counter
- * per round.  Uses the handle's SSSP buffers (about 24n bytes, allocated on
+ * per round; bfs_last_run_stats then reports the rounds, each with the
+ * frontier edges it relaxed.  Uses the handle's SSSP buffers (about 24n bytes, allocated on
  * the first call); must not overlap other calls on the handle.  Returns the
  * number of rounds (>= 1); BFS_EINVAL for a NULL handle or buffer, a source
  * outside [0, n), a max_weight that breaks the bound, or a weight above

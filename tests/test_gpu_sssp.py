@@ -32,6 +32,10 @@ def _check(g, w, maxw, sources, label):
             rounds, d, p = _run(bg, g, w_dev, maxw, s)
             wd, wp = oracle.sssp(g.row_ptr, g.col_idx, w, int(s))
             assert rounds >= 1
+            Ls, dirs, fe = bg.stats()        # per round: the frontier edges relaxed
+            assert Ls == rounds and fe.shape[0] == rounds and (fe >= 0).all()
+            deg = np.diff(g.row_ptr)
+            assert fe[0] == deg[int(s)]
             bad = np.nonzero(d != wd)[0]
             assert bad.size == 0, (label, s, bad[:5], d[bad[:5]], wd[bad[:5]])
             bad = np.nonzero(p != wp)[0]
