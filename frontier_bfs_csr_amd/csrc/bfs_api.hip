@@ -49,6 +49,7 @@ struct bfs_graph {
     uint32_t *cf = nullptr;        // 3 coarse frontier maps
     int32_t *pnb = nullptr;        // in-neighbour of highest out-degree of each vertex
     int32_t *snb = nullptr;        // ... and of second highest
+    uint8_t *deg8 = nullptr;       // in-degrees in a byte (255: 255 or more)
     int32_t *in_row_ptr = nullptr, *in_col = nullptr;   // transpose (directed graphs)
     int32_t can_pull = 0;          // in-edges available
     int32_t cf_sh = 0, cf_words = 0;
@@ -111,7 +112,7 @@ hipError_t dalloc(T **p, size_t count) {
 }
 
 void free_all(bfs_graph *g) {
-    void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->cf, g->pnb, g->snb, g->in_row_ptr, g->in_col, g->q0, g->q1, g->t0, g->t1,
+    void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->cf, g->pnb, g->snb, g->deg8, g->in_row_ptr, g->in_col, g->q0, g->q1, g->t0, g->t1,
                     g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
@@ -160,6 +161,7 @@ int alloc_workspace(bfs_graph *g) {
         {dalloc(&g->cf, 3 * (int64_t)CF_WORDS), "coarse frontier maps"},
         {dalloc(&g->pnb, n), "probe-neighbour index"},
         {dalloc(&g->snb, n), "probe-neighbour index"},
+        {dalloc(&g->deg8, n), "byte degrees"},
         {dalloc(&g->q0, (size_t)STRIPES * g->qcap), "frontier queue"},
         {dalloc(&g->q1, (size_t)STRIPES * g->qcap), "frontier queue"},
         {dalloc(&g->t0, (size_t)STRIPES * g->tcap), "tile queue"},
@@ -478,6 +480,7 @@ bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *co
         // the source) and start out visited
         if (e == hipSuccess) e = launch_build_vis_init(g->can_pull ? irp : row_ptr, n, g->can_pull, g->vis_init, 0);
         if (e == hipSuccess && g->can_pull) e = launch_build_probe_nb(row_ptr, irp, icol, n, g->pnb, g->snb, 0);
+        if (e == hipSuccess && g->can_pull) e = launch_build_deg8(irp, n, g->deg8, 0);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) {
             set_error("building the visited template, in-edges and probe-neighbour index failed: %s",
@@ -606,6 +609,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.vis_init = g->vis_init;
     P.pnb = g->pnb;
     P.snb = g->snb;
+    P.deg8 = g->deg8;
     P.in_row_ptr = g->symmetric ? g->row_ptr : g->in_row_ptr;
     P.in_col_idx = g->symmetric ? g->col_idx : g->in_col;
     P.can_pull = g->can_pull;

@@ -911,7 +911,7 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
         const bool dense = lane < nw && __popcll(~myvis) >= BU_DENSE;
         uint64_t myrest = dense ? 0ull : ~myvis;
         for (uint64_t todo = __ballot(dense); todo;) {
-            int jw[FW], v[FW], f[FW], b[FW], e[FW];
+            int jw[FW], v[FW], f[FW], dg[FW];
             uint32_t w[FW];
 #pragma unroll
             for (int q = 0; q < FW; ++q) {
@@ -928,8 +928,7 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
 #pragma unroll
             for (int q = 0; q < FW; ++q) {
                 f[q] = (v[q] >= 0) ? P.pnb[v[q]] : -1;
-                b[q] = (v[q] >= 0) ? P.in_row_ptr[v[q]] : 0;
-                e[q] = (v[q] >= 0) ? P.in_row_ptr[v[q] + 1] : 0;
+                dg[q] = (v[q] >= 0) ? (int)P.deg8[v[q]] : 0;   // in-degree, 255 meaning 255 or more
             }
 #pragma unroll
             for (int q = 0; q < FW; ++q)
@@ -940,7 +939,7 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
 #pragma unroll
             for (int q = 0; q < FW; ++q) {
                 h1[q] = f[q] >= 0 && ((w[q] >> (f[q] & 31)) & 1u);
-                f2[q] = (!h1[q] && v[q] >= 0 && e[q] - b[q] > 1) ? P.snb[v[q]] : -1;
+                f2[q] = (!h1[q] && v[q] >= 0 && dg[q] > 1) ? P.snb[v[q]] : -1;
             }
 #pragma unroll
             for (int q = 0; q < FW; ++q)
@@ -953,11 +952,11 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
                     P.dist[v[q]] = c.level + 1;
                     if (P.parent) P.parent[v[q]] = par;
                     c.fcnt += 1;
-                    c.fdeg += P.symmetric ? e[q] - b[q] : P.row_ptr[v[q] + 1] - P.row_ptr[v[q]];
+                    c.fdeg += (P.symmetric && dg[q] < 255) ? dg[q] : P.row_ptr[v[q] + 1] - P.row_ptr[v[q]];
                 }
                 const uint64_t hm = __ballot(hitq);
                 // two probes settle a vertex with two in-neighbours
-                const uint64_t rm = __ballot(v[q] >= 0 && !hitq && e[q] - b[q] > 2);
+                const uint64_t rm = __ballot(v[q] >= 0 && !hitq && dg[q] > 2);
                 if (lane == jw[q]) {
                     myrest = rm;
                     if (hm) sh.bu_fm[wv][lane] = hm;
@@ -1559,6 +1558,19 @@ __global__ __launch_bounds__(256) void probe_nb_kernel(const int32_t *row_ptr, c
             snb[v] = k2 ? in_col[0x7fffffff - (int)(uint32_t)(k2 & 0xffffffffull)] : -1;
         }
     }
+}
+
+__global__ __launch_bounds__(256) void deg8_kernel(const int32_t *in_row_ptr, int32_t n, uint8_t *deg8) {
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n; v += nth) {
+        const int d = in_row_ptr[v + 1] - in_row_ptr[v];
+        deg8[v] = (uint8_t)(d < 255 ? d : 255);
+    }
+}
+
+hipError_t launch_build_deg8(const int32_t *in_row_ptr, int32_t n, uint8_t *deg8, hipStream_t s) {
+    hipLaunchKernelGGL(deg8_kernel, dim3(grid_for(n, 256 * 4)), dim3(256), 0, s, in_row_ptr, n, deg8);
+    return hipGetLastError();
 }
 
 hipError_t launch_build_probe_nb(const int32_t *row_ptr, const int32_t *in_row_ptr, const int32_t *in_col,
