@@ -522,7 +522,10 @@ __device__ __forceinline__ void td_edge_balanced(Ctx &c, const Seg *cq, const Se
         const int pa = a + part * (EB_TE / spl);                 // this part's edges
         const int pb = min(pa + EB_TE / spl, E);                  // (at most STEP_CLAIMS winners)
         const int32_t *ts = cts + (size_t)r * P.tscap;
-        const int i0 = ts[t];
+        // tile 0 starts at segment 0 (segments and edges are reserved together
+        // from one counter, so the segment at index 0 holds edge offset 0): a
+        // list with one tile needs no table read
+        const int i0 = t ? ts[t] : 0;
         const int i1 = (a + EB_TE < E) ? ts[t + 1] : N - 1;
         int ns = i1 - i0 + 1;   // <= EB_TE + 1: every segment has an edge
         if (ns > EB_TE + 1 || ns < 1) {
@@ -1059,9 +1062,25 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
 __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) {
     const int lane = lane_id();
     const int slot = k % NSLOTS;
-    const int done = P.ctl->done;
+    // every word the decision reads is loaded here, before any is used, so
+    // the wavefront waits out one memory round trip instead of a chain of them
     unsigned long long cv = 0;
     if (lane < NCTR) cv = *ctr_at(P, slot, lane);
+    int done = 0, err = 0, cf_prev2 = 0;
+    SlotInfo prev{0, 0, 0, 0, 0, 0, 0};
+    int64_t reached_before = 0, edges_before = 0;
+    if (lane == 0) {
+        done = P.ctl->done;
+        err = P.ctl->err;
+        // the coarse map of level k+2 was written by level k-2 if it set wcf
+        // (the slot ring still holds level k-2's record at level k)
+        if (k >= 2) cf_prev2 = P.ctl->slot[(k + NSLOTS - 2) % NSLOTS].wcf;
+        if (k > 0) {
+            prev = P.ctl->slot[(k + NSLOTS - 1) % NSLOTS];
+            reached_before = P.ctl->slot[slot].reached_before;
+            edges_before = P.ctl->slot[slot].edges_before;
+        }
+    }
     const bool is_vc = lane >= VC_BASE && lane < NCTR;
     const int64_t fsize = wave_sum<int64_t>(is_vc ? (int64_t)(cv >> 32) : 0);
     const int64_t fdeg = wave_sum<int64_t>(is_vc ? (int64_t)(cv & 0xffffffffull) : 0);
@@ -1073,18 +1092,13 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
         sh.fsize = (int32_t)fsize; sh.fdeg = fdeg;
         sh.small = 0;
         sh.use_cf = 0;
-        // the coarse map of level k+2 was written by level k-2 if it set wcf
-        // (the slot ring still holds level k-2's record at level k)
-        sh.cf_clear = (k >= 2) ? P.ctl->slot[(k + NSLOTS - 2) % NSLOTS].wcf : 0;
-        if (done || P.ctl->err) {
+        sh.cf_clear = cf_prev2;
+        if (done || err) {
             sh.mode = 0;
         } else if (fsize == 0) {
             sh.mode = 1;
         } else {
             sh.mode = 2;
-            const SlotInfo prev = (k > 0) ? P.ctl->slot[(k + NSLOTS - 1) % NSLOTS] : SlotInfo{0, 0, 0, 0, 0, 0};
-            const int64_t reached_before = (k > 0) ? P.ctl->slot[slot].reached_before : 0;
-            const int64_t edges_before = (k > 0) ? P.ctl->slot[slot].edges_before : 0;
             const bool has_queue = (k == 0) || prev.dir == DIR_TD;
             const bool has_bm = (k == 0) || prev.dir == DIR_BU || prev.wbits;
             bool want_pull;
