@@ -1030,7 +1030,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
             P.ctl->done = 0; P.ctl->L = 0; P.ctl->err = 0; P.ctl->err_info = 0;
             for (int i = 0; i < RAN_CAP; ++i) P.ctl->ran[i] = 0;
             P.ctl->lvl[0] = 0; P.ctl->lvl[1] = 0;
-            P.ctl->bar_count = 0; P.ctl->bar_gen = 0;
+            P.ctl->bar_count = 0ull;
             for (int k = 0; k < NSLOTS; ++k) {
                 P.ctl->slot[k].dir = 0; P.ctl->slot[k].wbits = 0; P.ctl->slot[k].wcf = 0;
                 P.ctl->slot[k].input_bm = 0; P.ctl->slot[k].fsize = 0;
@@ -1145,22 +1145,25 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
 }
 
 // Barrier among the G workgroups of the small-frontier mode (all resident:
-// the others exit at once).  Release before arriving, acquire after leaving,
-// both at device scope so queues, bitmaps and counters written before it are
-// seen after it.  The wait is bounded: past the limit it records
-// ERR_BARRIER_TIMEOUT and returns, and every workgroup then leaves its loop.
+// the others exit at once).  The arrival count only grows: arrivals
+// [jG, (j+1)G) make up the j-th barrier of the search, since no workgroup can
+// arrive at barrier j+1 before barrier j is complete, so the count before a
+// workgroup's own arrival names its barrier and the barrier opens when the
+// count reaches (j+1)G -- the last arrival opens it with its own atomic, and
+// no second word has to be written and read.  Release before arriving,
+// acquire after leaving, both at device scope, so queues, bitmaps and
+// counters written before it are seen after it.  The wait is bounded: past
+// the limit it records ERR_BARRIER_TIMEOUT and returns, and every workgroup
+// then leaves its loop.
 __device__ __forceinline__ void small_barrier(const Params &P, int G) {
     __syncthreads();
     if (threadIdx.x == 0) {
         __threadfence();
-        const uint32_t gen = __hip_atomic_load(&P.ctl->bar_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t arrived = atomicAdd(&P.ctl->bar_count, 1u);
-        if (arrived == (uint32_t)G - 1) {
-            __hip_atomic_store(&P.ctl->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&P.ctl->bar_gen, gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
+        const unsigned long long before = atomicAdd(&P.ctl->bar_count, 1ull);
+        const unsigned long long open_at = (before / (unsigned long long)G + 1ull) * (unsigned long long)G;
+        if (before + 1ull < open_at) {
             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-            while (__hip_atomic_load(&P.ctl->bar_gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+            while (__hip_atomic_load(&P.ctl->bar_count, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < open_at) {
                 __builtin_amdgcn_s_sleep(2);
                 if (__builtin_amdgcn_s_memrealtime() - t0 > P.barrier_ticks) {
                     atomicCAS(&P.ctl->err, 0, ERR_BARRIER_TIMEOUT);

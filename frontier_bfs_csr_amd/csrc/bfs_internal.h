@@ -86,9 +86,9 @@ struct Ctl {
     int32_t lvl[2];       // level the launch with index i starts at: lvl[i & 1]
     int32_t pad0[2];
     SlotInfo slot[NSLOTS];
-    // barrier of the small-frontier mode, each word alone in 128 bytes
-    alignas(128) uint32_t bar_count;
-    alignas(128) uint32_t bar_gen;
+    // arrivals at the barrier of the small-frontier mode (only grows within a
+    // search), alone in its 128 bytes
+    alignas(128) unsigned long long bar_count;
     alignas(128) uint32_t pad1;
 };
 
