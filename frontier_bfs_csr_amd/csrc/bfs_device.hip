@@ -116,6 +116,7 @@ struct TdLds : LevelCommon {
     int32_t ntiles;
     unsigned long long list_base[NLISTS];
     int32_t cnt;                      // staged count (may exceed CAP: overflow spilled)
+    int32_t spilled;                  // some lane appended directly this level (its tallies are per thread)
     int32_t nbig;
     int32_t fl_cnt[WAVES], fl_more[WAVES];   // from-bitmap lists: count, words left
     int32_t vfilter;                  // claims first load the visited words
@@ -214,6 +215,7 @@ __device__ __forceinline__ void emit_single(Ctx &c, int v, int beg, int len) {
     const Params &P = *c.P;
     c.fcnt += 1;
     c.fdeg += len;
+    c.sh->spilled = 1;
     const int l = list_of(len);
     if (l < 0) return;
     const int nseg = (l == L_TILE) ? (len + TILE - 1) / TILE : 1;
@@ -331,8 +333,6 @@ __device__ __forceinline__ void flush(Ctx &c) {
     uint64_t tot0 = 0, tot1 = 0, tot2 = 0;
     for (int i = i0; i < min(i0 + EPT, cnt); ++i) {
         const int len = sh.slen[i];
-        c.fcnt += 1;
-        c.fdeg += len;
         const int l = list_of(len);
         if (l == L_SMALL) tot0 += (1ull << 32) | (uint32_t)len;
         else if (l == L_MID) tot1 += (1ull << 32) | (uint32_t)len;
@@ -361,6 +361,13 @@ __device__ __forceinline__ void flush(Ctx &c) {
         if (all != 0)
             sh.list_base[l] = atomicAdd(ctr_at(P, c.nslot, l * STRIPES + c.stripe), (unsigned long long)all);
         if (l == L_TILE) sh.ntiles = (int32_t)(all >> 32);
+    } else if (threadIdx.x == NLISTS) {
+        // the flushed vertices and their edges go straight into the level
+        // tallies (the staged vertices of every list, whole or in pieces)
+        uint64_t edges = 0;
+        for (int l = 0; l < NLISTS; ++l)
+            for (int w = 0; w < WAVES; ++w) edges += sh.scan_tmp[l][w] & 0xffffffffull;
+        atomicAdd(ctr_at(P, c.nslot, VC_BASE + c.stripe), ((unsigned long long)cnt << 32) | edges);
     }
     __syncthreads();
     // small and mid vertices: one segment each, written by their thread; big
@@ -1185,6 +1192,7 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
     if constexpr (!BU) {
         if (threadIdx.x == 0) {
             sh.cnt = 0;
+            sh.spilled = 0;
             sh.nbig = 0;
             // a visited-word load before each claim pays on levels with many
             // edges (it spares the atomics of targets already reached)
@@ -1264,7 +1272,11 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
         if (sh.cnt > 0) flush(c);
     }
 
-    // workgroup tallies -> one striped atomic
+    // workgroup tallies -> one striped atomic (a top-down level's flushes
+    // added theirs already; only direct appends are left)
+    if constexpr (!BU) {
+        if (!sh.spilled) return;
+    }
     const int64_t wc = wave_sum<int64_t>((int64_t)c.fcnt);
     const int64_t wd = wave_sum<int64_t>(c.fdeg);
     __syncthreads();
