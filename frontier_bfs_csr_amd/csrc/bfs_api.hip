@@ -31,7 +31,7 @@ void set_error(const char *fmt, ...) {
 
 struct HostCtl {
     int32_t done, L, err, err_info;
-    uint8_t ran[RAN_CAP];   // the device's record of the launches that ran a level
+    uint8_t ran[RAN_CAP];   // the device's record of the launches that ran a level or found the end
 };
 
 }  // namespace
@@ -656,13 +656,15 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     int64_t k = 0;
     // Launch kinds: searches on one graph tend to repeat their pattern of
     // directions, so the first batch is the plan (a shortest sequence that
-    // holds the working launches of the recent searches in order) plus one
-    // top-down launch (it finds the end after a last bottom-up level); without
+    // holds the working launches of the recent searches in order: those that
+    // ran a level or found the empty frontier; a search whose last level ran
+    // in the small-frontier mode finds its end in that same launch); without
     // a plan, a batch of 12 that alternates top-down and bottom-up, which
-    // covers most searches of under ten levels.  Later batches alternate.  A launch whose level belongs to the other direction
-    // passes it on, so the order only costs time, never results.
+    // covers most searches of under ten levels.  Later batches alternate.  A
+    // launch whose level belongs to the other direction passes it on, so the
+    // order only costs time, never results.
     const std::vector<uint8_t> plan = host_loop ? std::vector<uint8_t>() : g->plan;
-    const int64_t prefix = plan.empty() ? 0 : (int64_t)plan.size() + 1;
+    const int64_t prefix = (int64_t)plan.size();
     int64_t batch = host_loop ? 1 : (prefix ? prefix : 12);
     bool prev_bu = true;   // so that alternation starts top-down
     std::vector<uint8_t> kinds;

@@ -1299,7 +1299,11 @@ __device__ __forceinline__ int level_launch_start(const Params &P, LevelCommon &
     __syncthreads();
     if (sh.mode == 0) return -1;
     if (sh.mode == 1) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) { P.ctl->L = k; P.ctl->done = 1; }
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            P.ctl->L = k;
+            P.ctl->done = 1;
+            if (launch < RAN_CAP) P.ctl->ran[launch] = 2;
+        }
         return -1;
     }
     return k;
@@ -1323,7 +1327,11 @@ __global__ __launch_bounds__(BLOCK, 4) void bfs_td_kernel(Params P, int32_t laun
         __syncthreads();
         if (sh.mode == 0) return;    // over, or an error was recorded
         if (sh.mode == 1) {
-            if (blockIdx.x == 0 && threadIdx.x == 0) { P.ctl->L = k; P.ctl->done = 1; }
+            if (blockIdx.x == 0 && threadIdx.x == 0) {
+                P.ctl->L = k;
+                P.ctl->done = 1;
+                if (launch < RAN_CAP) P.ctl->ran[launch] = 1;
+            }
             return;
         }
         if (G == 0) {

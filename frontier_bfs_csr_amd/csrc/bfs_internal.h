@@ -80,8 +80,9 @@ struct Ctl {
     int32_t L;            // number of non-empty levels
     int32_t err;          // nonzero: internal limit exceeded (see ERR_*)
     int32_t err_info;
-    // ran[i]: launch i ran a level top-down (1) or bottom-up (2), else 0;
-    // read by the host with the status words, to order the next search's launches
+    // ran[i]: launch i ran a level, or found the empty frontier, in the
+    // top-down (1) or bottom-up (2) kernel, else 0; read by the host with the
+    // status words, to order the next search's launches
     uint8_t ran[RAN_CAP];
     int32_t lvl[2];       // level the launch with index i starts at: lvl[i & 1]
     int32_t pad0[2];

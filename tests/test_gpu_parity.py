@@ -137,10 +137,11 @@ def test_timing_hooks():
 
 
 def test_launch_plan_follows_last_search():
-    """A search enqueues the previous search's working launches (plus one
-    top-down launch) first: the repeated search uses no more launches, and
-    searches whose direction pattern differs from the last one, or that run
-    longer than the recorded launches, still give the oracle's result."""
+    """A search enqueues the recent searches' working launches (those that ran
+    a level or found the end) first: the repeated search uses no more
+    launches, and searches whose direction pattern differs from the last one,
+    or that run longer than the recorded launches, still give the oracle's
+    result."""
     import frontier_bfs_csr_amd as fb
     g = gg.rmat(15, 16, seed=7, nsrc=4)
     rp, ci = to_dev(g)
