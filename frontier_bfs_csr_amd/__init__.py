@@ -88,37 +88,55 @@ def bfs_last_error() -> str:
     return load().bfs_last_error().decode()
 
 
+_torch = None
+# raw handle -> (n, m) of its graph, for the size checks of the calls on it
+_handle_sizes = {}
+
+
+def _t():
+    global _torch
+    if _torch is None:
+        import torch
+        _torch = torch
+    return _torch
+
+
 def _dev_i32(t, name, numel=None):
-    import torch
+    """Device address of a contiguous int32 CUDA tensor with at least `numel`
+    elements (the kernels write every one of those), or None."""
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+    torch = _t()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA tensor")
-    if t.dtype != torch.int32 or not t.is_contiguous():
+    if t.dtype is not torch.int32 or not t.is_contiguous():
         raise TypeError(f"{name} must be a contiguous int32 tensor")
-    if numel is not None and t.numel() < numel:
-        raise ValueError(f"{name} needs at least {numel} elements, has {t.numel()}")
-    return ctypes.c_void_p(t.data_ptr() if t.numel() else None)
+    k = t.numel()
+    if numel is not None and k < numel:
+        raise ValueError(f"{name} needs at least {numel} elements, has {k}")
+    return t.data_ptr() if k else None
 
 
-def _dev_tensor(t, name, dtypes):
-    import torch
+def _dev_tensor(t, name, dtypes, numel=None):
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+    torch = _t()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA tensor")
     if t.dtype not in dtypes or not t.is_contiguous():
         raise TypeError(f"{name} must be a contiguous tensor of {', '.join(map(str, dtypes))}")
-    return ctypes.c_void_p(t.data_ptr() if t.numel() else None)
+    k = t.numel()
+    if numel is not None and k < numel:
+        raise ValueError(f"{name} needs at least {numel} elements, has {k}")
+    return t.data_ptr() if k else None
 
 
 def _stream_handle(stream):
-    import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = _t().cuda.current_stream()
     if isinstance(stream, int):
-        return ctypes.c_void_p(stream)
-    return ctypes.c_void_p(stream.cuda_stream)
+        return stream
+    return stream.cuda_stream
 
 
 def bfs_graph_create(n, row_ptr, col_idx):
@@ -129,13 +147,16 @@ def bfs_graph_create(n, row_ptr, col_idx):
     h = load().bfs_graph_create(int(n), rp, ci)
     if not h:
         raise BfsError(BFS_EINVAL, bfs_last_error())
+    _handle_sizes[h] = (int(n), bfs_graph_info(h)["m"])
     return h
 
 
 def bfs_run(g, source, dist, parent=None, level_sizes=None, stream=None):
-    """One BFS from `source` into the int32 CUDA tensors; returns L."""
-    L = load().bfs_run(g, int(source), _dev_i32(dist, "dist"), _dev_i32(parent, "parent"),
-                       _dev_i32(level_sizes, "level_sizes"), _stream_handle(stream))
+    """One BFS from `source` into the int32 CUDA tensors (each of at least n
+    elements); returns L."""
+    n = _handle_sizes.get(g, (None,))[0]
+    L = load().bfs_run(g, int(source), _dev_i32(dist, "dist", n), _dev_i32(parent, "parent", n),
+                       _dev_i32(level_sizes, "level_sizes", n), _stream_handle(stream))
     if L < 0:
         raise BfsError(L, bfs_last_error())
     return L
@@ -143,6 +164,7 @@ def bfs_run(g, source, dist, parent=None, level_sizes=None, stream=None):
 
 def bfs_graph_destroy(g):
     if g:
+        _handle_sizes.pop(g, None)
         load().bfs_graph_destroy(g)
 
 
@@ -156,10 +178,11 @@ def bfs_sssp(g, source, weights, max_weight, dist, pred=None, stream=None):
     """Shortest paths from source: weights (device uint32/int32 tensor, one per
     CSR entry), dist (device int64, n), pred (device int32, n, or None).
     Returns the number of relaxation rounds."""
-    import torch
-    w = _dev_tensor(weights, "weights", (torch.int32, torch.uint32))
-    d = _dev_tensor(dist, "dist", (torch.int64,))
-    p = _dev_i32(pred, "pred")
+    torch = _t()
+    n, m = _handle_sizes.get(g, (None, None))
+    w = _dev_tensor(weights, "weights", (torch.int32, torch.uint32), m)
+    d = _dev_tensor(dist, "dist", (torch.int64,), n)
+    p = _dev_i32(pred, "pred", n)
     rc = load().bfs_sssp(g, int(source), w, int(max_weight), d, p, _stream_handle(stream))
     if rc < 0:
         raise BfsError(rc, bfs_last_error())

@@ -235,6 +235,12 @@ def test_run_argument_errors():
                 bg.run(bad, d)
             assert ei.value.code == fb.BFS_EINVAL
         assert (d.cpu().numpy() == 9).all()   # untouched on EINVAL
+        # the binding refuses output tensors shorter than n before any launch
+        short = torch.full((g.n - 1,), 9, dtype=torch.int32, device="cuda")
+        for kw in ({"dist": short}, {"dist": d, "parent": short}, {"dist": d, "level_sizes": short}):
+            with pytest.raises(ValueError):
+                bg.run(0, **kw)
+        assert (short.cpu().numpy() == 9).all() and (d.cpu().numpy() == 9).all()
         with pytest.raises(fb.BfsError):
             bg.set_policy(7)                   # unknown direction
         with pytest.raises(fb.BfsError):

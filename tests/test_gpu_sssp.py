@@ -94,3 +94,10 @@ def test_sssp_arguments():
         assert (dist.cpu().numpy() == oracle.sssp(g.row_ptr, g.col_idx, w.cpu().numpy().view(np.uint32), 0)[0]).all()
         with pytest.raises(TypeError):
             bg.sssp(0, w, 10, torch.zeros(g.n, dtype=torch.int32, device="cuda"))
+        # weights shorter than m, or outputs shorter than n, are refused
+        with pytest.raises(ValueError):
+            bg.sssp(0, w[:-1], 10, dist)
+        with pytest.raises(ValueError):
+            bg.sssp(0, w, 10, dist[:-1])
+        with pytest.raises(ValueError):
+            bg.sssp(0, w, 10, dist, torch.zeros(g.n - 1, dtype=torch.int32, device="cuda"))
