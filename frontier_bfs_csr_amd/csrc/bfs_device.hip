@@ -96,7 +96,7 @@ struct LevelCommon {
     uint64_t scan_tmp[3][WAVES];
     // decision
     int32_t mode;                     // 0 exit, 1 finish, 2 run
-    int32_t dir, input_bm, wbits, wcf, clear_bm, adv_eb, small, use_cf, cf_clear;
+    int32_t dir, input_bm, wbits, wcf, clear_bm, adv_eb, small, use_cf, cf_clear, noq;
     int32_t fsize;
     int64_t fdeg, reached_before, edges_before;
     int32_t lcount[NLISTS * STRIPES];  // segments per (list, stripe)
@@ -149,6 +149,7 @@ struct CtxT {
     uint32_t *nbm;          // bitmap of level k+1 (top-down with wbits)
     uint32_t *ncf;          // coarse map of level k+1 (top-down with wcf)
     int32_t wcf;
+    int32_t noq;            // no queue: winners are tallied per thread, not staged
     Seg *nq, *nt;           // queues of level k+1
     int32_t *nts;
     // per-thread tallies of new frontier vertices
@@ -297,6 +298,14 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
                 atomicOr(c.ncf + (cb >> 5), 1u << (cb & 31));
             }
         }
+    }
+    if (c.noq) {
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            c.fcnt += win[q] ? 1 : 0;
+            c.fdeg += win[q] ? len[q] - beg[q] : 0;
+        }
+        return;
     }
 #pragma unroll
     for (int q = 0; q < CB; ++q) stage(c, win[q], v[q], beg[q], len[q] - beg[q]);
@@ -1040,7 +1049,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
             P.ctl->bar_count = 0ull;
             for (int k = 0; k < NSLOTS; ++k) {
                 P.ctl->slot[k].dir = 0; P.ctl->slot[k].wbits = 0; P.ctl->slot[k].wcf = 0;
-                P.ctl->slot[k].input_bm = 0; P.ctl->slot[k].fsize = 0;
+                P.ctl->slot[k].input_bm = 0; P.ctl->slot[k].fsize = 0; P.ctl->slot[k].noq = 0;
                 P.ctl->slot[k].reached_before = 0; P.ctl->slot[k].edges_before = 0;
             }
         }
@@ -1048,7 +1057,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
         if (threadIdx.x == 0) {
             Ctx c;
             c.P = &P; c.sh = nullptr; c.level = -1; c.wg = 0; c.G = 1; c.stripe = 0; c.nslot = 0; c.wbits = 0;
-            c.nbm = nullptr; c.ncf = nullptr; c.wcf = 0; c.nq = P.q0; c.nt = P.t0; c.nts = P.ts0; c.fcnt = 0; c.fdeg = 0;
+            c.nbm = nullptr; c.ncf = nullptr; c.wcf = 0; c.noq = 0; c.nq = P.q0; c.nt = P.t0; c.nts = P.ts0; c.fcnt = 0; c.fdeg = 0;
             const int beg = P.row_ptr[s];
             const int len = P.row_ptr[s + 1] - beg;
             const int l = list_of(len);
@@ -1099,6 +1108,7 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
         sh.fsize = (int32_t)fsize; sh.fdeg = fdeg;
         sh.small = 0;
         sh.use_cf = 0;
+        sh.noq = 0;
         sh.cf_clear = cf_prev2;
         if (done || err) {
             sh.mode = 0;
@@ -1106,7 +1116,7 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
             sh.mode = 1;
         } else {
             sh.mode = 2;
-            const bool has_queue = (k == 0) || prev.dir == DIR_TD;
+            const bool has_queue = (k == 0) || (prev.dir == DIR_TD && !prev.noq);
             const bool has_bm = (k == 0) || prev.dir == DIR_BU || prev.wbits;
             bool want_pull;
             if (P.pol_dir == BFS_DIR_PULL) {
@@ -1147,6 +1157,11 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
             // a top-down level sets the next coarse map only when its edges (a
             // bound on the next frontier) are few enough for the map to filter
             sh.wcf = sh.wbits && (fdeg << P.cf_sh) <= 2 * (int64_t)P.n;
+            // a wide level whose next level may pull writes its new vertices
+            // to the next bitmap only: the pull needs no queue, and should
+            // the next level stay top-down it reads the bitmap, as after a
+            // bottom-up level
+            sh.noq = sh.wbits && !sh.small && fdeg >= NOQ_EDGES;
         }
     }
 }
@@ -1225,6 +1240,7 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
             P.ctl->slot[slot].wcf = sh.wcf;
             P.ctl->slot[slot].input_bm = sh.input_bm;
             P.ctl->slot[slot].fsize = sh.fsize;
+            P.ctl->slot[slot].noq = sh.noq;
             P.ctl->slot[(k + 1) % NSLOTS].reached_before = sh.reached_before + sh.fsize;
             P.ctl->slot[(k + 1) % NSLOTS].edges_before = sh.edges_before + sh.fdeg;
         }
@@ -1242,6 +1258,7 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
     c.nslot = (k + 1) % NSLOTS;
     c.wbits = sh.wbits;
     c.wcf = sh.wcf;
+    c.noq = sh.noq;
     const int cur = k & 1;
     uint32_t *cbm = cur ? P.fbm1 : P.fbm0;
     uint32_t *obm = cur ? P.fbm0 : P.fbm1;
@@ -1275,7 +1292,7 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
     // workgroup tallies -> one striped atomic (a top-down level's flushes
     // added theirs already; only direct appends are left)
     if constexpr (!BU) {
-        if (!sh.spilled) return;
+        if (!sh.spilled && !sh.noq) return;
     }
     const int64_t wc = wave_sum<int64_t>((int64_t)c.fcnt);
     const int64_t wd = wave_sum<int64_t>(c.fdeg);

@@ -20,6 +20,8 @@ constexpr int CAP = 2048;                // LDS staging capacity for new frontie
 constexpr int STEP_CLAIMS = CAP / 2;     // claims between flush checks: a flush starts at
                                          // CAP / 2 staged, so a step never overfills
 constexpr int EB_TE = 1024;              // edges per tile of the edge-balanced advance
+constexpr int64_t NOQ_EDGES = 1 << 17;       // top-down levels with at least this many frontier
+                                              // edges whose next level may pull skip the queue
 constexpr int64_t VFILTER_EDGES = 1 << 20;  // top-down levels with at least this many
                                          // edges load the visited word before a claim
 constexpr int BU_GSZ = 128;              // bottom-up: vertices a wavefront lists at a time
@@ -69,6 +71,7 @@ struct SlotInfo {
     int32_t input_bm;     // this level's frontier came as a bitmap only
     int32_t fsize;        // this level's frontier size
     int32_t wcf;          // this level's new vertices were also set in the next coarse map
+    int32_t noq;          // this level wrote its new vertices to the next bitmap only (no queue)
     int64_t reached_before;  // vertices in levels < this one
     int64_t edges_before;    // sum of degrees of the vertices in levels < this one
 };

@@ -115,6 +115,32 @@ def test_switch_parameters(alpha, beta):
                     assert dirs[1] == 1, dirs
 
 
+def test_queue_free_wide_levels():
+    """A wide top-down level whose next level may pull writes its new vertices
+    to the next bitmap only.  From the centre of a star of 200,000 leaves
+    beside an R-MAT component (so that the remaining edges outweigh the
+    leaves), alpha = 1 or 4 keeps the leaf level top-down, and it expands from
+    that bitmap; the path is taken (a top-down level of at least 2^17 frontier
+    edges followed by a top-down level) and results never change."""
+    import frontier_bfs_csr_amd as fb
+    g = gg.disjoint_union(gg.star_graph(200_001), gg.rmat(16, 16, seed=23, nsrc=1))
+    rp, ci = to_dev(g)
+    seen = 0
+    with fb.BfsGraph(rp, ci) as bg:
+        for alpha in (1, 4, 40):
+            bg.set_switch(alpha, 48)
+            for s in (0, 1, 5, 200_001 + 7):
+                print(f"[gpu] queue-free levels alpha={alpha} source={s}", flush=True)
+                L, dist, parent, sizes = run_hip(bg, g.n, s)
+                ref = oracle.bfs(g.row_ptr, g.col_idx, s)
+                oracle.assert_bfs_ok(g.row_ptr, g.col_idx, s, ref, dist, parent, L, sizes[:L],
+                                     symmetric=True, label=f"{g.name} s={s} alpha={alpha}")
+                _, dirs, fdeg = bg.stats()
+                seen += sum(1 for k in range(L - 1)
+                            if dirs[k] == 0 and dirs[k + 1] == 0 and fdeg[k] >= 1 << 17)
+    assert seen > 0
+
+
 def test_timing_hooks():
     """Per-launch timing splits the level launches between the two kernels."""
     import frontier_bfs_csr_amd as fb
