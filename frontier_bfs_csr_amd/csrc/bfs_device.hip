@@ -1023,9 +1023,24 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
     const int tid = blockIdx.x * BLOCK + threadIdx.x;
     const int nth = gridDim.x * BLOCK;
     const int s = P.source;
-    for (int i = tid; i < P.n; i += nth) {
-        P.dist[i] = (i == s) ? 0 : -1;
-        if (P.parent) P.parent[i] = (i == s) ? s : -1;
+    {
+        typedef int v4i __attribute__((ext_vector_type(4)));
+        const bool al = ((reinterpret_cast<uintptr_t>(P.dist) |
+                          (P.parent ? reinterpret_cast<uintptr_t>(P.parent) : 0)) & 15) == 0;
+        const int lim = al ? (P.n >> 2) : 0;
+        v4i *d4 = reinterpret_cast<v4i *>(P.dist);
+        v4i *p4 = reinterpret_cast<v4i *>(P.parent);
+        for (int i = tid; i < lim; i += nth) {
+            v4i a = {-1, -1, -1, -1};
+            v4i b = a;
+            if ((s >> 2) == i) { a[s & 3] = 0; b[s & 3] = s; }
+            __builtin_nontemporal_store(a, d4 + i);
+            if (P.parent) __builtin_nontemporal_store(b, p4 + i);
+        }
+        for (int i = 4 * lim + tid; i < P.n; i += nth) {
+            P.dist[i] = (i == s) ? 0 : -1;
+            if (P.parent) P.parent[i] = (i == s) ? s : -1;
+        }
     }
     uint64_t *vis64 = reinterpret_cast<uint64_t *>(P.visited);
     const uint64_t *init64 = reinterpret_cast<const uint64_t *>(P.vis_init);
