@@ -734,8 +734,8 @@ __device__ __forceinline__ int probe_first(const BuLds &sh, const uint32_t *cbm,
 __device__ __forceinline__ void bu_found(BuCtx &c, int wbase, int v, int u, int d) {
     const Params &P = *c.P;
     if (!P.symmetric) d = P.row_ptr[v + 1] - P.row_ptr[v];
-    P.dist[v] = c.level + 1;
-    if (P.parent) P.parent[v] = u;
+    __builtin_nontemporal_store(c.level + 1, P.dist + v);   // streaming, as in the word pass
+    if (P.parent) __builtin_nontemporal_store(u, P.parent + v);
     atomicOr(&c.sh->bu_fm[wave_id()][(v >> 6) - wbase], 1ull << (v & 63));
     c.fcnt += 1;
     c.fdeg += d;
@@ -968,8 +968,10 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
                 const int par = h1[q] ? f[q] : ((f2[q] >= 0 && ((w[q] >> (f2[q] & 31)) & 1u)) ? f2[q] : -1);
                 const bool hitq = par >= 0;
                 if (hitq) {
-                    P.dist[v[q]] = c.level + 1;
-                    if (P.parent) P.parent[v[q]] = par;
+                    // outputs are never read back: streaming stores keep them
+                    // out of the caches the pass reads through
+                    __builtin_nontemporal_store(c.level + 1, P.dist + v[q]);
+                    if (P.parent) __builtin_nontemporal_store(par, P.parent + v[q]);
                     c.fcnt += 1;
                     c.fdeg += (P.symmetric && dg[q] < 255) ? dg[q] : P.row_ptr[v[q] + 1] - P.row_ptr[v[q]];
                 }
@@ -1024,6 +1026,9 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
     const int nth = gridDim.x * BLOCK;
     const int s = P.source;
     {
+        // dist and parent: 16-byte streaming stores (no level kernel reads
+        // them, and 8n bytes left in the caches would evict what the levels
+        // read), entry by entry when the caller's arrays are not 16-byte aligned
         typedef int v4i __attribute__((ext_vector_type(4)));
         const bool al = ((reinterpret_cast<uintptr_t>(P.dist) |
                           (P.parent ? reinterpret_cast<uintptr_t>(P.parent) : 0)) & 15) == 0;

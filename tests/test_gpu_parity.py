@@ -295,3 +295,27 @@ def test_unaligned_col_idx():
                 ref = oracle.bfs(g.row_ptr, g.col_idx, int(s))
                 oracle.assert_bfs_ok(g.row_ptr, g.col_idx, int(s), ref, dist, parent, L, sizes[:L],
                                      label=f"unaligned s={s} {pol}")
+
+
+def test_unaligned_outputs():
+    """dist and parent starting 4 bytes past a 16-byte boundary: the start of
+    a search then initialises them entry by entry; the sources include the
+    first and last vertices (an aligned group's first lane and the tail)."""
+    import torch
+    import frontier_bfs_csr_amd as fb
+    g = gg.rmat(13, 16, seed=33, nsrc=3)
+    rp, ci = to_dev(g)
+    db = torch.full((g.n + 1,), 5, dtype=torch.int32, device="cuda")
+    pb = torch.full((g.n + 1,), 5, dtype=torch.int32, device="cuda")
+    dist, parent = db[1:], pb[1:]
+    assert dist.data_ptr() % 16 != 0 and parent.data_ptr() % 16 != 0
+    sizes = torch.zeros(g.n, dtype=torch.int32, device="cuda")
+    deg = np.diff(g.row_ptr)
+    last = int(np.nonzero(deg)[0][-1])
+    with fb.BfsGraph(rp, ci) as bg:
+        for s in list(g.sources) + [int(np.nonzero(deg)[0][0]), last]:
+            L = bg.run(int(s), dist, parent, sizes)
+            ref = oracle.bfs(g.row_ptr, g.col_idx, int(s))
+            oracle.assert_bfs_ok(g.row_ptr, g.col_idx, int(s), ref, dist.cpu().numpy(), parent.cpu().numpy(),
+                                 L, sizes[:L].cpu().numpy(), label=f"unaligned outputs s={s}")
+            assert int(db[0]) == 5 and int(pb[0]) == 5   # nothing written before the arrays
