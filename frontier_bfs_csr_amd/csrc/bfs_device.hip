@@ -67,14 +67,29 @@ __device__ __forceinline__ unsigned long long *ctr_at(const Params &P, int slot,
     return P.ctr + ((size_t)slot * NCTR + (size_t)idx) * CTR_STRIDE;
 }
 
-__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) {
-        uint64_t y = __shfl_up(x, (unsigned)d, WAVE);
-        if (lane >= d) x += y;
-    }
+// Inclusive prefix sum over the 64 lanes of a wavefront (all lanes active)
+// with DPP moves, register to register: shifts right by 1, 2, 4 and 8 lanes
+// within each row of 16 (a lane shifted in from outside its row reads 0),
+// then lane 15 of each row added into the next row and lane 31 into the two
+// upper rows.  A shuffle would take a round trip through the LDS crossbar
+// per step.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
     return x;
+}
+
+// The same over a pair of 32-bit counts packed in 64 bits (high: items, low:
+// edges): callers keep each field's wavefront total below 2^32, so the
+// halves are scanned apart with no carry between them.
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
+    const uint32_t lo = wave_incl_scan_u32((uint32_t)x);
+    const uint32_t hi = wave_incl_scan_u32((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
 template <typename T>
@@ -676,13 +691,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 __device__ __forceinline__ int wave_incl_scan_i32(int x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) {
-        const int y = __shfl_up(x, (unsigned)d, WAVE);
-        if (lane >= d) x += y;
-    }
-    return x;
+    return (int)wave_incl_scan_u32((uint32_t)x);
 }
 
 constexpr int BU_NOHIT = 0x7fffffff;
@@ -1118,8 +1127,12 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
         }
     }
     const bool is_vc = lane >= VC_BASE && lane < NCTR;
-    const int64_t fsize = wave_sum<int64_t>(is_vc ? (int64_t)(cv >> 32) : 0);
-    const int64_t fdeg = wave_sum<int64_t>(is_vc ? (int64_t)(cv & 0xffffffffull) : 0);
+    // |F| <= n and deg(F) <= m, both below 2^31: 32-bit sums, read from the
+    // last lane of the scans
+    const int64_t fsize = (uint32_t)readlane_i(
+        (int)wave_incl_scan_u32(is_vc ? (uint32_t)(cv >> 32) : 0u), WAVE - 1);
+    const int64_t fdeg = (uint32_t)readlane_i(
+        (int)wave_incl_scan_u32(is_vc ? (uint32_t)(cv & 0xffffffffull) : 0u), WAVE - 1);
     if (lane < VC_BASE) {
         sh.lcount[lane] = (int32_t)(cv >> 32);
         sh.ledges[lane] = (int32_t)(cv & 0xffffffffull);
