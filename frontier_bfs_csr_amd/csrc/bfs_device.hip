@@ -92,12 +92,6 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T x) {
-#pragma unroll
-    for (int d = WAVE / 2; d > 0; d >>= 1) x += __shfl_xor(x, d, WAVE);
-    return x;
-}
 
 // ---------------------------------------------------------- LDS layout -----
 
@@ -1213,12 +1207,16 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
 __device__ __forceinline__ void small_barrier(const Params &P, int G) {
     __syncthreads();
     if (threadIdx.x == 0) {
-        __threadfence();
-        const unsigned long long before = atomicAdd(&P.ctl->bar_count, 1ull);
+        // one release before arriving and one acquire after the barrier
+        // opens; the arrival and the polls are relaxed device-scope atomics
+        // (coherent, so a poll sees the last arrival without a fence of its own)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const unsigned long long before =
+            __hip_atomic_fetch_add(&P.ctl->bar_count, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const unsigned long long open_at = (before / (unsigned long long)G + 1ull) * (unsigned long long)G;
         if (before + 1ull < open_at) {
             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-            while (__hip_atomic_load(&P.ctl->bar_count, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < open_at) {
+            while (__hip_atomic_load(&P.ctl->bar_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < open_at) {
                 __builtin_amdgcn_s_sleep(2);
                 if (__builtin_amdgcn_s_memrealtime() - t0 > P.barrier_ticks) {
                     atomicCAS(&P.ctl->err, 0, ERR_BARRIER_TIMEOUT);
@@ -1226,7 +1224,7 @@ __device__ __forceinline__ void small_barrier(const Params &P, int G) {
                 }
             }
         }
-        __threadfence();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
 }
@@ -1327,8 +1325,9 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
     if constexpr (!BU) {
         if (!sh.spilled && !sh.noq) return;
     }
-    const int64_t wc = wave_sum<int64_t>((int64_t)c.fcnt);
-    const int64_t wd = wave_sum<int64_t>(c.fdeg);
+    // a workgroup's vertices and their edges number below 2^31: 32-bit scans
+    const int64_t wc = (uint32_t)readlane_i((int)wave_incl_scan_u32((uint32_t)c.fcnt), WAVE - 1);
+    const int64_t wd = (uint32_t)readlane_i((int)wave_incl_scan_u32((uint32_t)c.fdeg), WAVE - 1);
     __syncthreads();
     if (lane == 0) { sh.scan_tmp[0][wave_id()] = (uint64_t)wc; sh.scan_tmp[1][wave_id()] = (uint64_t)wd; }
     __syncthreads();
