@@ -99,13 +99,15 @@ const char *bfs_last_error(void);
 #define BFS_ADV_BINNED 1
 #define BFS_ADV_EDGE   2
 
-/* Level loop.  Level launches alternate between a top-down kernel and a
- * bottom-up kernel; each reads the level to run and the frontier from device
- * memory, runs that level if its direction is the kernel's own and otherwise
- * leaves it to the next launch.
- *   DEVICE (default): launches are enqueued ahead in growing batches and the
- *     host waits once per batch; a small top-down level (up to 16,384
- *     vertices and 65,536 edges) runs on 32 workgroups that carry on level
+/* Level loop.  Level launches go to a top-down kernel or a bottom-up kernel;
+ * each reads the level to run and the frontier from device memory, runs that
+ * level if its direction is the kernel's own and otherwise leaves it to the
+ * next launch.
+ *   DEVICE (default): launches are enqueued ahead in batches and the host
+ *     waits once per batch; the first batch follows the handle's record of
+ *     its recent searches' launches (else 12 alternating launches), later
+ *     batches alternate and grow.  A small top-down level (up to 16,384
+ *     vertices and 16,384 edges) runs on 32 workgroups that carry on level
  *     after level with a barrier among themselves, so a long thin search is a
  *     handful of launches.
  *   HOST: the host waits for every launch before the next one, as bfs.cu's
