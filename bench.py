@@ -100,7 +100,7 @@ def main():
     ap.add_argument("--advance", type=int, default=0, help="0 auto, 1 binned, 2 edge-balanced")
     ap.add_argument("--loop", type=int, default=0, help="0 device-resident, 1 host-driven")
     ap.add_argument("--alpha", type=int, default=40, help="direction switch: pull when alpha*deg(F) > deg(U)")
-    ap.add_argument("--beta", type=int, default=48, help="direction switch: push when beta*|F| < n, shrinking")
+    ap.add_argument("--beta", type=int, default=96, help="direction switch: push when beta*|F| < n, shrinking")
     ap.add_argument("--claim", type=int, default=0, help="0 visited-bitmap atomicOr, 1 atomicMin on dist")
     ap.add_argument("--compaction", type=int, default=0,
                     help="0 direction-optimising path; top-down only: 1 atomic append, 2 sentinel-padded, "

@@ -195,7 +195,7 @@ def bfs_set_primitives(g, claim=CLAIM_BITMAP, compaction=COMPACT_DEFAULT):
         raise BfsError(rc, bfs_last_error())
 
 
-def bfs_set_switch(g, alpha=40, beta=48):
+def bfs_set_switch(g, alpha=40, beta=96):
     rc = load().bfs_set_switch(g, int(alpha), int(beta))
     if rc < 0:
         raise BfsError(rc, bfs_last_error())
@@ -282,7 +282,7 @@ class BfsGraph:
     def walk(self, vertices, out, mapping=WALK_WAVE, repeats=64, stream=None):
         bfs_walk_level(self.handle, vertices, out, mapping, repeats, stream)
 
-    def set_switch(self, alpha=40, beta=48):
+    def set_switch(self, alpha=40, beta=96):
         bfs_set_switch(self.handle, alpha, beta)
 
     def set_primitives(self, claim=CLAIM_BITMAP, compaction=COMPACT_DEFAULT):

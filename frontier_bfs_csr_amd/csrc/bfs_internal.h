@@ -38,7 +38,7 @@ constexpr int CF_WORDS = 4096;           // coarse frontier map: at most 4096 wo
 // come back top-down when the frontier is under n/beta and shrinking.  These
 // are the defaults; bfs_set_switch changes them per handle.
 constexpr int ALPHA = 40;
-constexpr int BETA = 48;
+constexpr int BETA = 96;
 
 // lists of a frontier queue
 constexpr int L_SMALL = 0;               // degree in [1, T_LANE)

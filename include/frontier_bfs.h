@@ -130,7 +130,7 @@ int32_t bfs_set_policy(bfs_graph *g, int32_t direction, int32_t advance, int32_t
 
 /*
  * Direction-switch parameters of the automatic policy, for later bfs_run calls
- * on this handle (defaults 40 and 48: Beamer, Asanovic and Patterson, SC 2012,
+ * on this handle (defaults 40 and 96: Beamer, Asanovic and Patterson, SC 2012,
  * use 14 and 24 on CPUs; the bottom-up pass here is cheap enough relative to
  * the top-down one that pulling earlier and pushing again later measured
  * best on the R-MAT and Erdos-Renyi graphs).  After a top-down level, the next level pulls when
