@@ -1401,8 +1401,10 @@ __global__ __launch_bounds__(BLOCK, 4) void bfs_td_kernel(Params P, int32_t laun
 }
 
 // Bottom-up launch: runs the level it stands at when that level is
-// bottom-up, else passes it on.
-__global__ __launch_bounds__(BLOCK, 6) void bfs_bu_kernel(Params P, int32_t launch) {
+// bottom-up, else passes it on.  The launch bounds hold it to 64 VGPRs, so
+// that with its 35 KB of LDS four workgroups share a compute unit (the pass
+// waits on scattered reads; a fourth workgroup hides more of that latency).
+__global__ __launch_bounds__(BLOCK, 8) void bfs_bu_kernel(Params P, int32_t launch) {
     __shared__ BuLds sh;
     const int k = level_launch_start(P, sh, launch);
     if (k < 0) return;

@@ -24,7 +24,7 @@ constexpr int64_t NOQ_EDGES = 1 << 17;       // top-down levels with at least th
                                               // edges whose next level may pull skip the queue
 constexpr int64_t VFILTER_EDGES = 1 << 20;  // top-down levels with at least this many
                                          // edges load the visited word before a claim
-constexpr int BU_GSZ = 128;              // bottom-up: vertices a wavefront lists at a time
+constexpr int BU_GSZ = 64;                // bottom-up: vertices a wavefront lists at a time
 #ifndef BU_DENSE
 #define BU_DENSE 16                      // bottom-up: a word with this many unvisited vertices
 #endif                                   //   is probed lane per vertex before listing
