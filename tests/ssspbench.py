@@ -8,9 +8,12 @@ Dijkstra, whose time is the CPU baseline.  Algorithmic bytes per call count
 init, output and 16 bytes per relaxation tried (bfs_last_run_stats gives the
 frontier edges of every round), against 8 TB/s.
 
-    python -m frontier_bfs_csr_amd.ssspbench [--workload c2] [--sources 8]
+    python tests/ssspbench.py [--workload c2] [--sources 8]
 
 Prints a table to stderr and one JSON line to stdout.
+
+It lives with the tests because it checks every result against the oracle
+(test infrastructure); the library itself never calls the oracle.
 """
 from __future__ import annotations
 

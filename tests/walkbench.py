@@ -9,9 +9,12 @@ with HIP events on the search stream (mean), and its per-vertex checksums are
 compared with the oracle's.  Beside the times it prints the analytic lane-slot
 model extended to 64 lanes: the share of issued lane slots that walk an entry.
 
-    python -m frontier_bfs_csr_amd.walkbench [--workload c1] [--repeats 64]
+    python tests/walkbench.py [--workload c1] [--repeats 64]
 
 Prints the table to stderr and one JSON line to stdout.
+
+It lives with the tests because it checks every result against the oracle
+(test infrastructure); the library itself never calls the oracle.
 """
 from __future__ import annotations
 
