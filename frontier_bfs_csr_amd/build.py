@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfrontier_bfs.so")
-SOURCES = ["bfs_device.hip", "bfs_walk.hip", "bfs_variants.hip", "bfs_sssp.hip", "bfs_api.hip"]
+SOURCES = ["bfs_device.hip", "bfs_small.hip", "bfs_walk.hip", "bfs_variants.hip", "bfs_sssp.hip", "bfs_api.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

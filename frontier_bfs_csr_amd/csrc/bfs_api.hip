@@ -646,6 +646,34 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     if (g->pol_compact != BFS_COMPACT_DEFAULT) return run_variant(g, P, stream);
     const bool timing = g->timing != 0;
     g->last_timed = 0;
+    if (g->n <= ONE_N && g->pol_dir == BFS_DIR_AUTO && g->pol_adv == BFS_ADV_AUTO &&
+        g->pol_loop == BFS_LOOP_DEVICE) {
+        // a graph this small is searched by one workgroup in one launch (its
+        // timing counts as one top-down launch; the launch plan is untouched)
+        if (timing) {
+            HIP_TRY(ensure_events(g, 3), BFS_EHIP);
+            HIP_TRY(hipEventRecord(g->events[0], stream), BFS_EHIP);
+        }
+        HIP_TRY(launch_one(P, stream), BFS_EHIP);
+        if (timing) HIP_TRY(hipEventRecord(g->events[1], stream), BFS_EHIP);
+        HIP_TRY(hipMemcpyAsync(g->host_ctl, g->ctl, sizeof(HostCtl), hipMemcpyDeviceToHost, stream), BFS_EHIP);
+        HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+        const int32_t L = g->host_ctl->L;
+        g->last_L = L;
+        if (timing) {
+            float ms = 0.f;
+            HIP_TRY(hipEventElapsedTime(&ms, g->events[0], g->events[1]), BFS_EHIP);
+            g->last_init_ms = 0.f;
+            g->last_level_ms = ms;
+            g->last_launches = 1;
+            g->last_kind_ms[0] = ms;
+            g->last_kind_ms[1] = 0.f;
+            g->last_kind_launches[0] = 1;
+            g->last_kind_launches[1] = 0;
+            g->last_timed = 1;
+        }
+        return L;
+    }
     if (timing) {
         HIP_TRY(ensure_events(g, 4), BFS_EHIP);
         HIP_TRY(hipEventRecord(g->events[0], stream), BFS_EHIP);

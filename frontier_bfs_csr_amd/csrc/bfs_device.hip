@@ -67,22 +67,6 @@ __device__ __forceinline__ unsigned long long *ctr_at(const Params &P, int slot,
     return P.ctr + ((size_t)slot * NCTR + (size_t)idx) * CTR_STRIDE;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wavefront (all lanes active)
-// with DPP moves, register to register: shifts right by 1, 2, 4 and 8 lanes
-// within each row of 16 (a lane shifted in from outside its row reads 0),
-// then lane 15 of each row added into the next row and lane 31 into the two
-// upper rows.  A shuffle would take a round trip through the LDS crossbar
-// per step.
-__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
-    return x;
-}
-
 // The same over a pair of 32-bit counts packed in 64 bits (high: items, low:
 // edges): callers keep each field's wavefront total below 2^32, so the
 // halves are scanned apart with no carry between them.

@@ -110,6 +110,22 @@ constexpr int SMALL_G = 32;
 constexpr int SMALL_F = SMALL_G * BLOCK;
 constexpr int SMALL_E = SMALL_F;
 
+// Inclusive prefix sum over the 64 lanes of a wavefront (all lanes active)
+// with DPP moves, register to register: shifts right by 1, 2, 4 and 8 lanes
+// within each row of 16 (a lane shifted in from outside its row reads 0),
+// then lane 15 of each row added into the next row and lane 31 into the two
+// upper rows.  A shuffle would take a round trip through the LDS crossbar
+// per step.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
+    return x;
+}
+
 struct Params {
     const int32_t *row_ptr;
     const int32_t *col_idx;
@@ -158,6 +174,10 @@ struct Params {
 
 // host-side launch helpers (bfs_device.hip)
 hipError_t launch_init(const Params &P, int grid, hipStream_t s);
+// Graphs of at most ONE_N vertices are searched by one workgroup with the
+// visited bits and both frontiers in LDS (bfs_small.hip).
+constexpr int ONE_N = 3584;
+hipError_t launch_one(const Params &P, hipStream_t s);
 // launch `launch_index` of the level chain: even indexes run the top-down
 // kernel, odd ones the bottom-up kernel
 hipError_t launch_level(const Params &P, int32_t launch_index, bool bottom_up, int grid, hipStream_t s);

@@ -97,11 +97,14 @@ def test_c5_workload_sampled():
 @pytest.mark.parametrize("alpha,beta", [(1, 1), (1, 10**6), (10**6, 1), (10**6, 10**6), (4, 64)])
 def test_switch_parameters(alpha, beta):
     """The automatic policy under extreme direction-switch parameters: results
-    never change; a huge alpha pulls from the second level on."""
+    never change; a huge alpha pulls from the second level on.  (The
+    edge-balanced advance is named explicitly: it keeps the small C1 graph on
+    the multi-workgroup path, whose direction switch this checks.)"""
     import frontier_bfs_csr_amd as fb
     for g in (gg.rmat(14, 16, seed=21, nsrc=3), gg.c1_chung_lu()):
         rp, ci = to_dev(g)
         with fb.BfsGraph(rp, ci) as bg:
+            bg.set_policy(fb.DIR_AUTO, fb.ADV_EDGE, fb.LOOP_DEVICE)
             bg.set_switch(alpha, beta)
             for s in g.sources[:3]:
                 s = int(s)
@@ -319,3 +322,41 @@ def test_unaligned_outputs():
             oracle.assert_bfs_ok(g.row_ptr, g.col_idx, int(s), ref, dist.cpu().numpy(), parent.cpu().numpy(),
                                  L, sizes[:L].cpu().numpy(), label=f"unaligned outputs s={s}")
             assert int(db[0]) == 5 and int(pb[0]) == 5   # nothing written before the arrays
+
+
+def test_single_workgroup_small_graphs():
+    """Graphs of at most 3,584 vertices under the default policy are searched
+    by one workgroup in one launch (visited bits and frontiers in LDS): the
+    oracle's results on both sides of that bound, on directed graphs, from a
+    source of degree 0, and on a dense graph whose levels take many edge
+    passes; the run is one top-down launch and the statistics are top-down."""
+    import frontier_bfs_csr_amd as fb
+    cases = [
+        (gg.random_directed(3584, 12, 41), True),    # exactly at the bound
+        (gg.random_directed(3585, 12, 42), False),   # one vertex above it
+        (gg.rmat(11, 16, seed=43, nsrc=4), True),
+        (gg.complete_graph(600), True),              # 359,400 entries: 44 passes on level 1
+        (gg.disjoint_union(gg.star_graph(2000), gg.path_graph(300)), True),
+        (gg.c1_chung_lu(), True),
+    ]
+    for g, one in cases:
+        rp, ci = to_dev(g)
+        with fb.BfsGraph(rp, ci) as bg:
+            bg.set_timing(True)
+            deg = np.diff(g.row_ptr)
+            srcs = [int(x) for x in g.sources[:3]]
+            if (deg == 0).any():
+                srcs.append(int(np.nonzero(deg == 0)[0][0]))   # a source of degree 0
+            for s in srcs:
+                print(f"[gpu] single workgroup {g.name} n={g.n} source={s}", flush=True)
+                L, dist, parent, sizes = run_hip(bg, g.n, s)
+                ref = oracle.bfs(g.row_ptr, g.col_idx, s)
+                oracle.assert_bfs_ok(g.row_ptr, g.col_idx, s, ref, dist, parent, L, sizes[:L],
+                                     symmetric=g.symmetric, label=f"single workgroup {g.name} s={s}")
+                kt = bg.kernel_timing()
+                Ls, dirs, fdeg = bg.stats()
+                assert Ls == L
+                if one:
+                    assert kt["td"][1] == 1 and kt["bu"][1] == 0, kt
+                    assert (dirs == 0).all()
+                    assert int(fdeg[0]) == int(deg[s])
