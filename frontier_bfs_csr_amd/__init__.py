@@ -25,6 +25,9 @@ LOOP_DEVICE, LOOP_HOST, LOOP_CHAIN = 0, 1, 2
 WALK_LANE, WALK_WAVE, WALK_BINNED, WALK_MERGE = 0, 1, 2, 3
 CLAIM_BITMAP, CLAIM_MIN = 0, 1
 COMPACT_DEFAULT, COMPACT_ATOMIC, COMPACT_PADDED, COMPACT_FILTER, COMPACT_FLAGS = 0, 1, 2, 3, 4
+# graphs of at most this many vertices are searched by one workgroup under the
+# default policy (the library's ONE_N; bfs_small.hip)
+SMALL_GRAPH_N = 3584
 
 EXPORTS = ("bfs_graph_create", "bfs_run", "bfs_graph_destroy", "bfs_last_error",
            "bfs_set_policy", "bfs_last_run_stats", "bfs_set_timing", "bfs_last_run_timing",
