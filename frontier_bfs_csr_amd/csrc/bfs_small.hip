@@ -4,7 +4,7 @@
 // queue, flush reservation, barrier) around a few hundred edges; here the
 // visited bits, both frontier queues and the frontier's degree offsets sit in
 // LDS, a claim is an LDS atomicOr, and a level costs the row-pointer reads,
-// the adjacency reads and two workgroup barriers.  Same level-synchronous
+// the adjacency reads and three workgroup barriers.  Same level-synchronous
 // method: the frontier's edges are dealt out edge-balanced (owner by the last
 // offset not above the edge, as in the edge-balanced advance), every neighbour
 // is claimed once, and the winner writes dist and parent and joins the next
