@@ -360,3 +360,17 @@ def test_single_workgroup_small_graphs():
                     assert kt["td"][1] == 1 and kt["bu"][1] == 0, kt
                     assert (dirs == 0).all()
                     assert int(fdeg[0]) == int(deg[s])
+
+
+def test_sources_across_components():
+    """One handle, its launch plan learnt from the searches before, with
+    sources in turn in an R-MAT component (which pulls), on a path, and of
+    degree 0, under several policies; outputs start out holding garbage, so
+    an entry a search leaves unwritten shows."""
+    big = gg.rmat(14, 16, seed=21, nsrc=3)
+    assert (np.diff(big.row_ptr) == 0).any()   # isolated vertices in the pulled part
+    g = gg.disjoint_union(gg.disjoint_union(big, gg.path_graph(40)), gg.path_graph(1))
+    b = [int(s) for s in big.sources]
+    srcs = b + [big.n + 5, g.n - 1, b[0], big.n + 39, g.n - 1, b[1], b[2]]
+    check_graph(g, sources=srcs, policies=["auto"])
+    check_graph(g, sources=[b[0], big.n + 20, b[1]], policies=["pull", "auto", "push_edge", "auto"])
