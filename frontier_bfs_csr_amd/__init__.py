@@ -32,7 +32,7 @@ SMALL_GRAPH_N = 3584
 EXPORTS = ("bfs_graph_create", "bfs_run", "bfs_graph_destroy", "bfs_last_error",
            "bfs_set_policy", "bfs_last_run_stats", "bfs_set_timing", "bfs_last_run_timing",
            "bfs_graph_info", "bfs_set_switch", "bfs_last_run_kernel_timing", "bfs_walk_level", "bfs_set_primitives",
-           "bfs_sssp")
+           "bfs_sssp", "bfs_last_run_launch_timing")
 
 _lib = None
 
@@ -77,6 +77,8 @@ def load():
         lib.bfs_last_run_kernel_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32),
                                                    ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
         lib.bfs_last_run_kernel_timing.restype = i32
+        lib.bfs_last_run_launch_timing.argtypes = [P, i32, P, P]
+        lib.bfs_last_run_launch_timing.restype = i32
         lib.bfs_walk_level.argtypes = [P, P, i32, i32, i32, P, P]
         lib.bfs_walk_level.restype = i32
         lib.bfs_set_primitives.argtypes = [P, i32, i32]
@@ -256,6 +258,20 @@ def bfs_last_run_kernel_timing(g):
     return {"td": (a.value, c.value), "bu": (b.value, d.value)}
 
 
+def bfs_last_run_launch_timing(g):
+    """(ms[float32], ran[uint8]) per level launch of the last timed run."""
+    cnt = load().bfs_last_run_launch_timing(g, 0, None, None)
+    if cnt < 0:
+        raise BfsError(cnt, bfs_last_error())
+    ms = np.zeros(cnt, np.float32)
+    ran = np.zeros(cnt, np.uint8)
+    rc = load().bfs_last_run_launch_timing(g, cnt, ms.ctypes.data_as(ctypes.c_void_p),
+                                           ran.ctypes.data_as(ctypes.c_void_p))
+    if rc < 0:
+        raise BfsError(rc, bfs_last_error())
+    return ms, ran
+
+
 def bfs_graph_info(g):
     m, srt, sym, mx, pr = (ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(),
                            ctypes.c_int32())
@@ -308,6 +324,9 @@ class BfsGraph:
 
     def kernel_timing(self):
         return bfs_last_run_kernel_timing(self.handle)
+
+    def launch_timing(self):
+        return bfs_last_run_launch_timing(self.handle)
 
     def close(self):
         if self.handle:

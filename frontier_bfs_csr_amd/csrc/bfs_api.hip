@@ -92,6 +92,8 @@ struct bfs_graph {
     int32_t last_kind_launches[2] = {0, 0};
     std::vector<hipEvent_t> events;   // [0,1] init, then one before and one after each
                                       // launch of a batch
+    std::vector<float> launch_ms;     // each level launch of the last timed run
+    std::vector<uint8_t> launch_ran;  // ... and the device's record of its work
 };
 
 namespace {
@@ -142,10 +144,10 @@ hipError_t ensure_events(bfs_graph *g, size_t count) {
 int alloc_workspace(bfs_graph *g) {
     const int64_t n = g->n, m = g->m;
     const int64_t nwp = (n + 63) / 64;
-    g->qcap = n;
-    g->tcap = m / TILE + m / T_WG + 1;
-    g->tscap = m / EB_TE + 2;
-    g->st_cap = (int32_t)((n + 1) < (1 << 22) ? (n + 1) : (1 << 22));
+    g->qcap = queue_cap(n);
+    g->tcap = tile_cap(m);
+    g->tscap = tstart_cap(m);
+    g->st_cap = (int32_t)stats_cap(n);
     // coarse frontier map: the finest power-of-two grain that fits CF_WORDS words
     g->cf_sh = 0;
     while (((n + (1LL << g->cf_sh) - 1) >> g->cf_sh) > (int64_t)CF_WORDS * 32) ++g->cf_sh;
@@ -410,6 +412,8 @@ int32_t run_variant(bfs_graph *g, const Params &P, hipStream_t stream) {
         g->last_kind_ms[1] = 0.f;
         g->last_kind_launches[0] = L;
         g->last_kind_launches[1] = 0;
+        g->launch_ms.clear();
+        g->launch_ran.clear();
         g->last_timed = 1;
     }
     return L;
@@ -670,6 +674,8 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
             g->last_kind_ms[1] = 0.f;
             g->last_kind_launches[0] = 1;
             g->last_kind_launches[1] = 0;
+            g->launch_ms.assign(1, ms);
+            g->launch_ran.assign(1, 1);
             g->last_timed = 1;
         }
         return L;
@@ -698,6 +704,8 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     std::vector<uint8_t> kinds;
     float level_ms = 0.f, kind_ms[2] = {0.f, 0.f};
     int32_t kind_launches[2] = {0, 0};
+    g->launch_ms.clear();
+    g->launch_ran.clear();
     // outside the prefix, launches alternate top-down and bottom-up; each pair
     // runs at least one level or finds the empty frontier, and L <= n, so
     // launch prefix + 2n + 1 has found it
@@ -726,6 +734,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
                 level_ms += ms;
                 kind_ms[kinds[i]] += ms;
                 kind_launches[kinds[i]] += 1;
+                g->launch_ms.push_back(ms);
             }
         }
         const HostCtl &h = *g->host_ctl;
@@ -758,6 +767,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
                     g->last_kind_ms[t] = kind_ms[t];
                     g->last_kind_launches[t] = kind_launches[t];
                 }
+                for (int64_t i = 0; i < k; ++i) g->launch_ran.push_back(i < RAN_CAP ? h.ran[i] : 0);
                 g->last_timed = 1;
             }
             return h.L;
@@ -830,6 +840,8 @@ int32_t bfs_walk_level(bfs_graph *g, const int32_t *vertices, int32_t count, int
         g->last_launches = 1;
         g->last_kind_ms[0] = g->last_kind_ms[1] = 0.f;
         g->last_kind_launches[0] = g->last_kind_launches[1] = 0;
+        g->launch_ms.clear();
+        g->launch_ran.clear();
         g->last_timed = 1;
     }
     return 0;
@@ -923,6 +935,8 @@ int32_t bfs_sssp(bfs_graph *g, int32_t source, const uint32_t *weights, uint32_t
         g->last_kind_ms[1] = 0.f;
         g->last_kind_launches[0] = rounds;
         g->last_kind_launches[1] = 0;
+        g->launch_ms.clear();
+        g->launch_ran.clear();
         g->last_timed = 1;
     }
     HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
@@ -965,6 +979,20 @@ int32_t bfs_last_run_kernel_timing(const bfs_graph *g, float *td_ms, int32_t *td
     if (bu_ms) *bu_ms = g->last_kind_ms[1];
     if (bu_launches) *bu_launches = g->last_kind_launches[1];
     return 0;
+}
+
+int32_t bfs_last_run_launch_timing(const bfs_graph *g, int32_t cap, float *ms, uint8_t *ran) {
+    if (!g || !g->last_timed || cap < 0) {
+        set_error(g ? (cap < 0 ? "negative capacity" : "the last run was not timed (bfs_set_timing)")
+                    : "NULL graph handle");
+        return BFS_EINVAL;
+    }
+    const int64_t cnt = (int64_t)g->launch_ms.size();
+    for (int64_t i = 0; i < cnt && i < cap; ++i) {
+        if (ms) ms[i] = g->launch_ms[i];
+        if (ran) ran[i] = i < (int64_t)g->launch_ran.size() ? g->launch_ran[i] : 0;
+    }
+    return (int32_t)cnt;
 }
 
 int32_t bfs_last_run_timing(const bfs_graph *g, float *init_ms, float *level_ms,

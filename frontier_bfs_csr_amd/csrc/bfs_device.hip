@@ -1479,6 +1479,7 @@ __global__ __launch_bounds__(256) void vis_init_kernel(const int32_t *row_ptr, i
 
 // ------------------------------------------------------ host helpers -------
 
+
 hipError_t launch_init(const Params &P, int grid, hipStream_t s) {
     hipLaunchKernelGGL(bfs_init_kernel, dim3(grid), dim3(BLOCK), 0, s, P);
     return hipGetLastError();

@@ -172,6 +172,14 @@ struct Params {
     uint32_t barrier_ticks;   // small-mode barrier wait limit (100 MHz ticks)
 };
 
+// Workspace capacities (segments or entries per stripe region) for a graph of
+// n vertices and m CSR entries; the handle's workspace and the fixed scratch
+// of the allocation-free entry point both follow them.
+constexpr int64_t queue_cap(int64_t n) { return n; }
+constexpr int64_t tile_cap(int64_t m) { return m / TILE + m / T_WG + 1; }
+constexpr int64_t tstart_cap(int64_t m) { return m / EB_TE + 2; }
+constexpr int64_t stats_cap(int64_t n) { return (n + 1) < (1 << 22) ? (n + 1) : (1 << 22); }
+
 // host-side launch helpers (bfs_device.hip)
 hipError_t launch_init(const Params &P, int grid, hipStream_t s);
 // Graphs of at most ONE_N vertices are searched by one workgroup with the

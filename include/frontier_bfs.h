@@ -182,6 +182,22 @@ int32_t bfs_last_run_kernel_timing(const bfs_graph *g, float *td_ms, int32_t *td
                                    float *bu_ms, int32_t *bu_launches);
 
 /*
+ * The level launches of the last timed bfs_run one by one (host memory, either
+ * may be NULL; the first min(cap, count) entries are written): ms[i] = launch
+ * i's time between HIP events recorded just before and just after it on the
+ * run's stream; ran[i] = the device's record of its work: 1 the top-down
+ * kernel ran a level or found the empty frontier, 2 the bottom-up kernel did,
+ * 0 it passed its level on or exited at once (launches from index 64 on are
+ * not recorded and read 0).  A top-down launch in the small-frontier mode may
+ * run several levels.  The per-level launch table of the "Day 38 - Graph
+ * traversal on a GPU" page (section "What a level-synchronous search actually
+ * launches") is what this reproduces.  Returns the number of launches, or
+ * BFS_EINVAL if the last run was not timed or cap < 0.  The walk, shortest
+ * paths and the non-default compactions record no launches (count 0).
+ */
+int32_t bfs_last_run_launch_timing(const bfs_graph *g, int32_t cap, float *ms, uint8_t *ran);
+
+/*
  * Claim and compaction primitives of the top-down level (Gunrock reading
  * guide, step 2; "Day 38 - Graph traversal on a GPU", on day 33's
  * compaction).  claim: BFS_CLAIM_BITMAP (an atomicOr on the visited bitmap
