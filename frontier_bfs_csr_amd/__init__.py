@@ -32,7 +32,7 @@ SMALL_GRAPH_N = 3584
 EXPORTS = ("bfs_graph_create", "bfs_run", "bfs_graph_destroy", "bfs_last_error",
            "bfs_set_policy", "bfs_last_run_stats", "bfs_set_timing", "bfs_last_run_timing",
            "bfs_graph_info", "bfs_set_switch", "bfs_last_run_kernel_timing", "bfs_walk_level", "bfs_set_primitives",
-           "bfs_sssp", "bfs_last_run_launch_timing")
+           "bfs_sssp", "bfs_last_run_launch_timing", "bfs_run_noalloc")
 
 _lib = None
 
@@ -77,6 +77,8 @@ def load():
         lib.bfs_last_run_kernel_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32),
                                                    ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
         lib.bfs_last_run_kernel_timing.restype = i32
+        lib.bfs_run_noalloc.argtypes = [i32, P, P, i32, P, P, P, P]
+        lib.bfs_run_noalloc.restype = i32
         lib.bfs_last_run_launch_timing.argtypes = [P, i32, P, P]
         lib.bfs_last_run_launch_timing.restype = i32
         lib.bfs_walk_level.argtypes = [P, P, i32, i32, i32, P, P]
@@ -162,6 +164,23 @@ def bfs_run(g, source, dist, parent=None, level_sizes=None, stream=None):
     n = _handle_sizes.get(g, (None,))[0]
     L = load().bfs_run(g, int(source), _dev_i32(dist, "dist", n), _dev_i32(parent, "parent", n),
                        _dev_i32(level_sizes, "level_sizes", n), _stream_handle(stream))
+    if L < 0:
+        raise BfsError(L, bfs_last_error())
+    return L
+
+
+# bounds of bfs_run_noalloc (its fixed scratch is sized for them)
+NOALLOC_MAX_N = 1 << 16
+NOALLOC_MAX_M = 1 << 21
+
+
+def bfs_run_noalloc(row_ptr, col_idx, source, dist, parent=None, level_sizes=None, stream=None):
+    """One BFS without a handle or any device allocation (graphs of at most
+    NOALLOC_MAX_N vertices and NOALLOC_MAX_M entries); returns L."""
+    n = int(row_ptr.numel()) - 1
+    L = load().bfs_run_noalloc(n, _dev_i32(row_ptr, "row_ptr", n + 1), _dev_i32(col_idx, "col_idx"),
+                               int(source), _dev_i32(dist, "dist", n), _dev_i32(parent, "parent", n),
+                               _dev_i32(level_sizes, "level_sizes", n), _stream_handle(stream))
     if L < 0:
         raise BfsError(L, bfs_last_error())
     return L

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -447,6 +448,88 @@ int alloc_sssp_buffers(bfs_graph *g) {
     return 0;
 }
 
+// ---- allocation-free search: fixed scratch in a file-scope device array ----
+//
+// bfs_run_noalloc searches a graph of at most NA_N vertices and NA_M CSR
+// entries without a handle: its workspace (graph facts, control block,
+// counters, bitmaps, probe-neighbour index, queues, tile tables, per-level
+// record) is carved out of `scratch`, one array per device that lives until
+// the process ends.  Host code never passes `scratch` itself to a kernel: the
+// array's device address comes from hipGetSymbolAddress, once per device.
+namespace {
+
+constexpr int64_t NA_N = 1 << 16;          // most vertices
+constexpr int64_t NA_M = 1 << 21;          // most CSR entries
+constexpr int64_t NA_NWP = (NA_N + 63) / 64;
+
+constexpr int64_t na_round(int64_t b) { return (b + 255) / 256 * 256; }
+// byte offsets of the pieces of the scratch array
+constexpr int64_t NA_FACTS = 0;
+constexpr int64_t NA_CTL = NA_FACTS + na_round(sizeof(GraphFacts));
+constexpr int64_t NA_CTR = NA_CTL + na_round(sizeof(Ctl));
+constexpr int64_t NA_VIS = NA_CTR + na_round((int64_t)NSLOTS * NCTR * CTR_STRIDE * 8);
+constexpr int64_t NA_VIS_INIT = NA_VIS + na_round(2 * NA_NWP * 4);
+constexpr int64_t NA_FBM0 = NA_VIS_INIT + na_round(2 * NA_NWP * 4);
+constexpr int64_t NA_FBM1 = NA_FBM0 + na_round(2 * NA_NWP * 4);
+constexpr int64_t NA_CF = NA_FBM1 + na_round(2 * NA_NWP * 4);
+constexpr int64_t NA_PNB = NA_CF + na_round(3 * (int64_t)CF_WORDS * 4);
+constexpr int64_t NA_SNB = NA_PNB + na_round(NA_N * 4);
+constexpr int64_t NA_DEG8 = NA_SNB + na_round(NA_N * 4);
+constexpr int64_t NA_Q0 = NA_DEG8 + na_round(NA_N);
+constexpr int64_t NA_Q1 = NA_Q0 + na_round(STRIPES * queue_cap(NA_N) * (int64_t)sizeof(Seg));
+constexpr int64_t NA_T0 = NA_Q1 + na_round(STRIPES * queue_cap(NA_N) * (int64_t)sizeof(Seg));
+constexpr int64_t NA_T1 = NA_T0 + na_round(STRIPES * tile_cap(NA_M) * (int64_t)sizeof(Seg));
+constexpr int64_t NA_TS0 = NA_T1 + na_round(STRIPES * tile_cap(NA_M) * (int64_t)sizeof(Seg));
+constexpr int64_t NA_TS1 = NA_TS0 + na_round((int64_t)NLISTS * STRIPES * tstart_cap(NA_M) * 4);
+constexpr int64_t NA_STDIR = NA_TS1 + na_round((int64_t)NLISTS * STRIPES * tstart_cap(NA_M) * 4);
+constexpr int64_t NA_STFDEG = NA_STDIR + na_round(stats_cap(NA_N));
+constexpr int64_t NA_BYTES = NA_STFDEG + na_round(stats_cap(NA_N) * 8);
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[NA_BYTES];
+
+namespace {
+
+constexpr int NA_MAX_DEV = 64;
+struct NaDevice {
+    int ready = 0;
+    unsigned char *ptr = nullptr;   // this device's copy of `scratch`
+    int grid = 0, grid_bu = 0;
+};
+NaDevice g_na[NA_MAX_DEV];
+std::mutex g_na_mu;
+
+// Set-up on the current device, once: the scratch array's device address and
+// the level kernels' grids.
+int na_setup(int dev, NaDevice **out) {
+    if (dev < 0 || dev >= NA_MAX_DEV) {
+        set_error("device %d is beyond the %d devices the allocation-free search supports", dev, NA_MAX_DEV);
+        return BFS_EINVAL;
+    }
+    std::lock_guard<std::mutex> lock(g_na_mu);
+    NaDevice &d = g_na[dev];
+    if (!d.ready) {
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            set_error("hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+            return BFS_EHIP;
+        }
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        d.ptr = static_cast<unsigned char *>(p);
+        d.grid = cus * level_kernel_blocks_per_cu(false);
+        d.grid_bu = cus * level_kernel_blocks_per_cu(true);
+        d.ready = 1;
+    }
+    *out = &d;
+    return 0;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *bfs_last_error(void) { return g_err.c_str(); }
@@ -778,6 +861,172 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
             return BFS_EDEVICE;
         }
         if (!host_loop && batch < 1024) batch = batch < 12 ? 12 : batch * 2;
+    }
+}
+
+int32_t bfs_run_noalloc(int32_t n, const int32_t *row_ptr, const int32_t *col_idx, int32_t source,
+                        int32_t *dist_out, int32_t *parent_out, int32_t *level_sizes_out, hipStream_t stream) {
+    g_err.clear();
+    if (n < 1 || n > NA_N) {
+        set_error("n = %d is outside [1, %lld], the allocation-free search's limit", n, (long long)NA_N);
+        return BFS_EINVAL;
+    }
+    if (!row_ptr || !dist_out) {
+        set_error("row_ptr and dist_out must be device pointers");
+        return BFS_EINVAL;
+    }
+    if (source < 0 || source >= n) {
+        set_error("source %d is outside [0, %d)", source, n);
+        return BFS_EINVAL;
+    }
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev), BFS_EHIP);
+    NaDevice *d = nullptr;
+    {
+        const int rc = na_setup(dev, &d);
+        if (rc) return rc;
+    }
+    unsigned char *base = d->ptr;
+    GraphFacts *facts = reinterpret_cast<GraphFacts *>(base + NA_FACTS);
+    // the graph, checked as bfs_graph_create checks it
+    int32_t ends[2] = {-1, -1};
+    HIP_TRY(hipMemcpyAsync(&ends[0], row_ptr, sizeof(int32_t), hipMemcpyDeviceToHost, stream), BFS_EHIP);
+    HIP_TRY(hipMemcpyAsync(&ends[1], row_ptr + n, sizeof(int32_t), hipMemcpyDeviceToHost, stream), BFS_EHIP);
+    HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+    if (ends[0] != 0) {
+        set_error("invalid CSR: row_ptr[0] = %d, expected 0", ends[0]);
+        return BFS_EINVAL;
+    }
+    if (ends[1] < 0 || ends[1] > NA_M) {
+        set_error("row_ptr[%d] = %d: the allocation-free search takes 0 to %lld CSR entries", n, ends[1],
+                  (long long)NA_M);
+        return BFS_EINVAL;
+    }
+    const int32_t m = ends[1];
+    if (m > 0 && !col_idx) {
+        set_error("col_idx must be a device pointer when row_ptr[n] = %d > 0", m);
+        return BFS_EINVAL;
+    }
+    GraphFacts h;
+    HIP_TRY(launch_facts_reset(facts, stream), BFS_EHIP);
+    HIP_TRY(launch_check_rows(row_ptr, n, facts, stream), BFS_EHIP);
+    HIP_TRY(hipMemcpyAsync(&h, facts, sizeof(h), hipMemcpyDeviceToHost, stream), BFS_EHIP);
+    HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+    if (h.bad_row != ~0ull) {
+        set_error("invalid CSR: row_ptr is decreasing at index %llu (row_ptr[i] > row_ptr[i+1])",
+                  (unsigned long long)h.bad_row);
+        return BFS_EINVAL;
+    }
+    if (m > 0) {
+        HIP_TRY(launch_check_cols(row_ptr, col_idx, n, facts, stream), BFS_EHIP);
+        HIP_TRY(hipMemcpyAsync(&h, facts, sizeof(h), hipMemcpyDeviceToHost, stream), BFS_EHIP);
+        HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+        if (h.bad_col != ~0ull) {
+            set_error("invalid CSR: col_idx[%llu] is outside [0, %d)", (unsigned long long)h.bad_col, n);
+            return BFS_EINVAL;
+        }
+        if (!h.unsorted) {
+            HIP_TRY(launch_check_symmetry(row_ptr, col_idx, n, facts, stream), BFS_EHIP);
+            HIP_TRY(hipMemcpyAsync(&h, facts, sizeof(h), hipMemcpyDeviceToHost, stream), BFS_EHIP);
+            HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+        }
+    }
+    // pull needs in-edges: a symmetric graph is its own; any other graph is
+    // searched push-only here (no room for a transpose)
+    const int32_t symmetric = (!h.unsorted && !h.asymmetric) ? 1 : 0;
+    const int64_t nwp = ((int64_t)n + 63) / 64;
+    Params P;
+    std::memset(&P, 0, sizeof(P));
+    P.row_ptr = row_ptr;
+    P.col_idx = col_idx;
+    P.n = n;
+    P.m = m;
+    P.nwp = (int32_t)nwp;
+    P.source = source;
+    P.dist = dist_out;
+    P.parent = parent_out;
+    P.level_sizes = level_sizes_out;
+    P.visited = reinterpret_cast<uint32_t *>(base + NA_VIS);
+    P.vis_init = reinterpret_cast<uint32_t *>(base + NA_VIS_INIT);
+    P.pnb = reinterpret_cast<int32_t *>(base + NA_PNB);
+    P.snb = reinterpret_cast<int32_t *>(base + NA_SNB);
+    P.deg8 = reinterpret_cast<uint8_t *>(base + NA_DEG8);
+    P.in_row_ptr = symmetric ? row_ptr : nullptr;
+    P.in_col_idx = symmetric ? col_idx : nullptr;
+    P.can_pull = symmetric;
+    P.fbm0 = reinterpret_cast<uint32_t *>(base + NA_FBM0);
+    P.fbm1 = reinterpret_cast<uint32_t *>(base + NA_FBM1);
+    P.cf = reinterpret_cast<uint32_t *>(base + NA_CF);
+    P.cf_sh = 0;
+    while ((((int64_t)n + (1LL << P.cf_sh) - 1) >> P.cf_sh) > (int64_t)CF_WORDS * 32) ++P.cf_sh;
+    P.cf_words = (int32_t)(((((int64_t)n + (1LL << P.cf_sh) - 1) >> P.cf_sh) + 31) / 32);
+    P.q0 = reinterpret_cast<Seg *>(base + NA_Q0);
+    P.q1 = reinterpret_cast<Seg *>(base + NA_Q1);
+    P.t0 = reinterpret_cast<Seg *>(base + NA_T0);
+    P.t1 = reinterpret_cast<Seg *>(base + NA_T1);
+    P.ts0 = reinterpret_cast<int32_t *>(base + NA_TS0);
+    P.ts1 = reinterpret_cast<int32_t *>(base + NA_TS1);
+    P.qcap = queue_cap(n);
+    P.tcap = tile_cap(m);
+    P.tscap = tstart_cap(m);
+    P.ctr = reinterpret_cast<unsigned long long *>(base + NA_CTR);
+    P.ctl = reinterpret_cast<Ctl *>(base + NA_CTL);
+    P.st_dir = reinterpret_cast<int8_t *>(base + NA_STDIR);
+    P.st_fdeg = reinterpret_cast<int64_t *>(base + NA_STFDEG);
+    P.st_cap = (int32_t)stats_cap(n);
+    P.symmetric = symmetric;
+    P.col_vec = (reinterpret_cast<uintptr_t>(col_idx) % 16) == 0;
+    P.in_col_vec = symmetric && P.col_vec;
+    P.pol_dir = BFS_DIR_AUTO;
+    P.pol_adv = BFS_ADV_AUTO;
+    P.small_mode = 1;
+    P.alpha = ALPHA;
+    P.beta = BETA;
+    P.max_deg = h.max_degree;
+    P.barrier_ticks = 200000000u;   // 2 s at 100 MHz, as a handle's default
+    // the graph-derived tables a handle builds at creation
+    HIP_TRY(launch_build_vis_init(row_ptr, n, symmetric, reinterpret_cast<uint32_t *>(base + NA_VIS_INIT),
+                                  stream), BFS_EHIP);
+    if (symmetric) {
+        HIP_TRY(launch_build_probe_nb(row_ptr, row_ptr, col_idx, n, reinterpret_cast<int32_t *>(base + NA_PNB),
+                                      reinterpret_cast<int32_t *>(base + NA_SNB), stream), BFS_EHIP);
+        HIP_TRY(launch_build_deg8(row_ptr, n, reinterpret_cast<uint8_t *>(base + NA_DEG8), stream), BFS_EHIP);
+    }
+    int32_t hc[4] = {0, 0, 0, 0};   // done, L, err, err_info
+    if (n <= ONE_N) {
+        HIP_TRY(launch_one(P, stream), BFS_EHIP);
+        HIP_TRY(hipMemcpyAsync(hc, P.ctl, sizeof(hc), hipMemcpyDeviceToHost, stream), BFS_EHIP);
+        HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+        return hc[1];
+    }
+    HIP_TRY(launch_init(P, d->grid, stream), BFS_EHIP);
+    // the level launches as in bfs_run's default loop, without a learnt plan:
+    // batches that alternate top-down and bottom-up (top-down only when the
+    // graph cannot pull), growing from 12 to 1024 launches
+    const int64_t kmax = 2 * (int64_t)n + 2;
+    int64_t k = 0, batch = 12;
+    bool prev_bu = true;
+    for (;;) {
+        for (int64_t i = 0; i < batch && k <= kmax; ++i, ++k) {
+            const bool bu = symmetric ? !prev_bu : false;
+            prev_bu = bu;
+            HIP_TRY(launch_level(P, (int32_t)k, bu, bu ? d->grid_bu : d->grid, stream), BFS_EHIP);
+        }
+        HIP_TRY(hipMemcpyAsync(hc, P.ctl, sizeof(hc), hipMemcpyDeviceToHost, stream), BFS_EHIP);
+        HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+        if (hc[2]) {
+            if (hc[2] == ERR_BARRIER_TIMEOUT)
+                set_error("small-frontier barrier wait exceeded its limit");
+            else
+                set_error("device reported internal error %d (info %d)", hc[2], hc[3]);
+            return BFS_EDEVICE;
+        }
+        if (hc[0]) return hc[1];
+        if (k > kmax) {
+            set_error("search did not terminate after %lld level launches", (long long)k);
+            return BFS_EDEVICE;
+        }
+        if (batch < 1024) batch *= 2;
     }
 }
 

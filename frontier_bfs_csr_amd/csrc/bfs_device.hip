@@ -1477,8 +1477,23 @@ __global__ __launch_bounds__(256) void vis_init_kernel(const int32_t *row_ptr, i
     }
 }
 
+__global__ void facts_reset_kernel(GraphFacts *f) {
+    if (threadIdx.x == 0) {
+        f->bad_row = ~0ull;
+        f->bad_col = ~0ull;
+        f->unsorted = 0u;
+        f->asymmetric = 0u;
+        f->max_degree = 0;
+        f->pad = 0;
+    }
+}
+
 // ------------------------------------------------------ host helpers -------
 
+hipError_t launch_facts_reset(GraphFacts *f, hipStream_t s) {
+    hipLaunchKernelGGL(facts_reset_kernel, dim3(1), dim3(64), 0, s, f);
+    return hipGetLastError();
+}
 
 hipError_t launch_init(const Params &P, int grid, hipStream_t s) {
     hipLaunchKernelGGL(bfs_init_kernel, dim3(grid), dim3(BLOCK), 0, s, P);

@@ -201,6 +201,9 @@ struct GraphFacts {
     int32_t max_degree;
     int32_t pad;
 };
+// sets f to "no bad row, no bad column, sorted, symmetric, degree 0" (a fill
+// kernel, so that nothing here records a memset)
+hipError_t launch_facts_reset(GraphFacts *f, hipStream_t s);
 hipError_t launch_check_rows(const int32_t *row_ptr, int32_t n, GraphFacts *f, hipStream_t s);
 hipError_t launch_check_cols(const int32_t *row_ptr, const int32_t *col_idx, int32_t n,
                              GraphFacts *f, hipStream_t s);

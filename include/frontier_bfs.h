@@ -78,6 +78,29 @@ bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *co
 int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent_out,
                 int32_t *level_sizes_out, hipStream_t stream);
 
+/*
+ * bfs_run without a handle and without any device allocation, for callers
+ * that cannot allocate (code under HIP graph capture of its neighbours, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments and
+ * results as bfs_graph_create followed by bfs_run with the default policy,
+ * for a graph of at most 65,536 vertices and 2,097,152 CSR entries: the graph
+ * is validated as bfs_graph_create validates it (BFS_EINVAL, with the first
+ * bad index in bfs_last_error), then searched by the same kernels, the
+ * direction switching included when the graph is symmetric with sorted rows
+ * (any other graph is searched push-only: dist, L and level sizes do not
+ * change).  The workspace (about 20 MB) is one fixed device array per GPU,
+ * created with the library's code object and held until the process ends;
+ * nothing is allocated or freed on any call.  Every call on one GPU shares
+ * that array and leaves its contents behind, so calls that overlap on one GPU
+ * (other threads, other streams) race and must be serialised by the caller.
+ * Reads a few words back to the host per call and synchronises `stream`
+ * before returning.  Returns L >= 1, or BFS_EINVAL (a bound exceeded, an
+ * invalid graph or argument; outputs untouched), BFS_EHIP or BFS_EDEVICE.
+ */
+int32_t bfs_run_noalloc(int32_t n, const int32_t *row_ptr, const int32_t *col_idx, int32_t source,
+                        int32_t *dist_out, int32_t *parent_out, int32_t *level_sizes_out,
+                        hipStream_t stream);
+
 /* Frees the workspace.  NULL is a no-op.  Synchronises the device first. */
 void bfs_graph_destroy(bfs_graph *g);
 

@@ -46,6 +46,20 @@ def test_host_side_argument_errors():
     assert lib.bfs_last_run_stats(None, 0, None, None) == fb.BFS_EINVAL
     assert lib.bfs_graph_info(None, None, None, None, None, None) == fb.BFS_EINVAL
     assert lib.bfs_last_run_launch_timing(None, 0, None, None) == fb.BFS_EINVAL
+    # the allocation-free search refuses sizes beyond its fixed scratch, and
+    # missing pointers, before any device work
+    assert lib.bfs_run_noalloc(fb.NOALLOC_MAX_N + 1, ctypes.c_void_p(1), ctypes.c_void_p(1), 0,
+                               ctypes.c_void_p(1), None, None, None) == fb.BFS_EINVAL
+    assert "limit" in fb.bfs_last_error()
+    assert lib.bfs_run_noalloc(0, ctypes.c_void_p(1), ctypes.c_void_p(1), 0,
+                               ctypes.c_void_p(1), None, None, None) == fb.BFS_EINVAL
+    assert lib.bfs_run_noalloc(10, None, ctypes.c_void_p(1), 0, ctypes.c_void_p(1), None, None,
+                               None) == fb.BFS_EINVAL
+    assert lib.bfs_run_noalloc(10, ctypes.c_void_p(1), ctypes.c_void_p(1), 0, None, None, None,
+                               None) == fb.BFS_EINVAL
+    assert lib.bfs_run_noalloc(10, ctypes.c_void_p(1), ctypes.c_void_p(1), 10, ctypes.c_void_p(1), None,
+                               None, None) == fb.BFS_EINVAL
+    assert "source 10" in fb.bfs_last_error()
     lib.bfs_graph_destroy(None)   # no-op
 
 
