@@ -79,6 +79,24 @@ def component_edges(deg, dist, symmetric=True):
     return total // 2 if symmetric else total
 
 
+def host_cpu():
+    """The host's CPU model name and core counts (for the CPU baseline)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 0
+    return {"cpu_model": model, "nproc": usable, "cpu_count": os.cpu_count() or 0}
+
+
 def copy_calibration(nbytes):
     """A plain device copy of known size, for scaling PMC byte counters."""
     import torch
@@ -237,10 +255,12 @@ def main():
                 ok = ok and bool((gpu_dist[s] == ref[0]).all())
             if spent >= args.cpu_seconds:
                 break
+        host = host_cpu()
         cpu = {"value": cedges / spent / 1e9, "unit": "GTEPS", "cores": 1, "kind": "oracle",
                "sample": f"{cnt} of the {len(sources)} sources of the same graph, serial FIFO BFS "
-                         f"(gcc -O2), {spent:.1f} s",
-               "ms_per_bfs": spent / cnt * 1e3}
+                         f"(gcc -O2) on one core of {host['nproc']} ({host['cpu_model']}), {spent:.1f} s",
+               "ms_per_bfs": spent / cnt * 1e3, "host_cpu_model": host["cpu_model"],
+               "host_nproc": host["nproc"]}
         parity_sample = {"sources_compared": sum(1 for s in sources[:cnt] if gpu_dist.get(s) is not None),
                          "dist_equal": ok}
 

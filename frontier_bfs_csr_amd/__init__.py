@@ -32,7 +32,8 @@ SMALL_GRAPH_N = 3584
 EXPORTS = ("bfs_graph_create", "bfs_run", "bfs_graph_destroy", "bfs_last_error",
            "bfs_set_policy", "bfs_last_run_stats", "bfs_set_timing", "bfs_last_run_timing",
            "bfs_graph_info", "bfs_set_switch", "bfs_last_run_kernel_timing", "bfs_walk_level", "bfs_set_primitives",
-           "bfs_sssp", "bfs_last_run_launch_timing", "bfs_run_noalloc")
+           "bfs_sssp", "bfs_last_run_launch_timing", "bfs_run_noalloc", "bfs_debug_enqueue_counts",
+           "bfs_last_error_code")
 
 _lib = None
 
@@ -43,52 +44,73 @@ class BfsError(RuntimeError):
         self.code = code
 
 
+# the enqueue-counting debug build (validator V5 of the tests)
+LIB_V5_PATH = os.path.join(_PKG, "libfrontier_bfs_v5.so")
+_lib_v5 = None
+
+
 def load():
     """Load the built library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
-                               "(python -c 'import __graft_entry__ as g; g.build()')")
-        lib = ctypes.CDLL(LIB_PATH)
-        P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-        lib.bfs_graph_create.argtypes = [i32, P, P]
-        lib.bfs_graph_create.restype = P
-        lib.bfs_run.argtypes = [P, i32, P, P, P, P]
-        lib.bfs_run.restype = i32
-        lib.bfs_graph_destroy.argtypes = [P]
-        lib.bfs_graph_destroy.restype = None
-        lib.bfs_last_error.argtypes = []
-        lib.bfs_last_error.restype = ctypes.c_char_p
-        lib.bfs_set_policy.argtypes = [P, i32, i32, i32]
-        lib.bfs_set_policy.restype = i32
-        lib.bfs_set_switch.argtypes = [P, i32, i32]
-        lib.bfs_set_switch.restype = i32
-        lib.bfs_last_run_stats.argtypes = [P, i32, P, P]
-        lib.bfs_last_run_stats.restype = i32
-        lib.bfs_graph_info.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i32),
-                                       ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
-        lib.bfs_graph_info.restype = i32
-        lib.bfs_set_timing.argtypes = [P, i32]
-        lib.bfs_set_timing.restype = i32
-        lib.bfs_last_run_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float),
-                                            ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
-        lib.bfs_last_run_timing.restype = i32
-        lib.bfs_last_run_kernel_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32),
-                                                   ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
-        lib.bfs_last_run_kernel_timing.restype = i32
-        lib.bfs_run_noalloc.argtypes = [i32, P, P, i32, P, P, P, P]
-        lib.bfs_run_noalloc.restype = i32
-        lib.bfs_last_run_launch_timing.argtypes = [P, i32, P, P]
-        lib.bfs_last_run_launch_timing.restype = i32
-        lib.bfs_walk_level.argtypes = [P, P, i32, i32, i32, P, P]
-        lib.bfs_walk_level.restype = i32
-        lib.bfs_set_primitives.argtypes = [P, i32, i32]
-        lib.bfs_set_primitives.restype = i32
-        lib.bfs_sssp.argtypes = [P, i32, P, ctypes.c_uint32, P, P, P]
-        lib.bfs_sssp.restype = i32
-        _lib = lib
+        _lib = _open(LIB_PATH)
     return _lib
+
+
+def load_v5():
+    """Load the enqueue-counting debug build (tests only)."""
+    global _lib_v5
+    if _lib_v5 is None:
+        _lib_v5 = _open(LIB_V5_PATH)
+    return _lib_v5
+
+
+def _open(path):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.bfs_graph_create.argtypes = [i32, P, P]
+    lib.bfs_graph_create.restype = P
+    lib.bfs_run.argtypes = [P, i32, P, P, P, P]
+    lib.bfs_run.restype = i32
+    lib.bfs_graph_destroy.argtypes = [P]
+    lib.bfs_graph_destroy.restype = None
+    lib.bfs_last_error.argtypes = []
+    lib.bfs_last_error.restype = ctypes.c_char_p
+    lib.bfs_last_error_code.argtypes = []
+    lib.bfs_last_error_code.restype = i32
+    lib.bfs_set_policy.argtypes = [P, i32, i32, i32]
+    lib.bfs_set_policy.restype = i32
+    lib.bfs_set_switch.argtypes = [P, i32, i32]
+    lib.bfs_set_switch.restype = i32
+    lib.bfs_last_run_stats.argtypes = [P, i32, P, P]
+    lib.bfs_last_run_stats.restype = i32
+    lib.bfs_graph_info.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                   ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.bfs_graph_info.restype = i32
+    lib.bfs_set_timing.argtypes = [P, i32]
+    lib.bfs_set_timing.restype = i32
+    lib.bfs_last_run_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float),
+                                        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    lib.bfs_last_run_timing.restype = i32
+    lib.bfs_last_run_kernel_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32),
+                                               ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    lib.bfs_last_run_kernel_timing.restype = i32
+    lib.bfs_debug_enqueue_counts.argtypes = [P, P]
+    lib.bfs_debug_enqueue_counts.restype = i32
+    lib.bfs_run_noalloc.argtypes = [i32, P, P, i32, P, P, P, P]
+    lib.bfs_run_noalloc.restype = i32
+    lib.bfs_last_run_launch_timing.argtypes = [P, i32, P, P]
+    lib.bfs_last_run_launch_timing.restype = i32
+    lib.bfs_walk_level.argtypes = [P, P, i32, i32, i32, P, P]
+    lib.bfs_walk_level.restype = i32
+    lib.bfs_set_primitives.argtypes = [P, i32, i32]
+    lib.bfs_set_primitives.restype = i32
+    lib.bfs_sssp.argtypes = [P, i32, P, ctypes.c_uint32, P, P, P]
+    lib.bfs_sssp.restype = i32
+    return lib
 
 
 def bfs_last_error() -> str:
@@ -153,7 +175,7 @@ def bfs_graph_create(n, row_ptr, col_idx):
     ci = _dev_i32(col_idx, "col_idx")
     h = load().bfs_graph_create(int(n), rp, ci)
     if not h:
-        raise BfsError(BFS_EINVAL, bfs_last_error())
+        raise BfsError(load().bfs_last_error_code() or BFS_EINVAL, bfs_last_error())
     _handle_sizes[h] = (int(n), bfs_graph_info(h)["m"])
     return h
 

@@ -10,6 +10,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfrontier_bfs.so")
+# the same library built with per-vertex enqueue counting (validator V5 of the
+# tests); never the one the product path loads
+LIB_V5 = os.path.join(PKG, "libfrontier_bfs_v5.so")
 SOURCES = ["bfs_device.hip", "bfs_small.hip", "bfs_walk.hip", "bfs_variants.hip", "bfs_sssp.hip", "bfs_api.hip"]
 
 HIPCC_FLAGS = [
@@ -27,16 +30,23 @@ def hipcc():
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC,
+def _build_one(out: str, extra, verbose: bool) -> str:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC,
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """The library, then its enqueue-counting debug build (both in-tree)."""
+    _build_one(LIB, [], verbose)
+    _build_one(LIB_V5, ["-DFBFS_COUNT_ENQUEUES"], verbose)
     return LIB
 
 

@@ -20,6 +20,7 @@ using namespace fbfs;
 namespace {
 
 thread_local std::string g_err;
+thread_local int32_t g_err_code = 0;
 
 void set_error(const char *fmt, ...) {
     char buf[512];
@@ -28,6 +29,16 @@ void set_error(const char *fmt, ...) {
     vsnprintf(buf, sizeof(buf), fmt, ap);
     va_end(ap);
     g_err = buf;
+}
+
+// bfs_last_error text for an error word the kernels recorded
+void set_device_error(int32_t err, int32_t info, uint32_t barrier_ticks) {
+    if (err == ERR_BARRIER_TIMEOUT)
+        set_error("small-frontier barrier wait exceeded its limit (%u ticks)", barrier_ticks);
+    else if (err == ERR_BAD_VERTEX)
+        set_error("vertex id %d outside [0, n) met in the graph (changed after it was checked?)", info);
+    else
+        set_error("device reported internal error %d (info %d)", err, info);
 }
 
 struct HostCtl {
@@ -63,6 +74,7 @@ struct bfs_graph {
     int64_t *st_fdeg = nullptr;
     int32_t st_cap = 0;
     HostCtl *host_ctl = nullptr;   // pinned
+    int32_t *enq = nullptr;        // debug builds: per-vertex enqueue counts of the last run
     GraphFacts *facts = nullptr;   // device, create only
     int32_t pol_dir = BFS_DIR_AUTO, pol_adv = BFS_ADV_AUTO, pol_loop = BFS_LOOP_DEVICE;
     int32_t pol_claim = BFS_CLAIM_BITMAP, pol_compact = BFS_COMPACT_DEFAULT;
@@ -99,12 +111,13 @@ struct bfs_graph {
 
 namespace {
 
+// a failed HIP call returns `code`, or BFS_ENOMEM when the device ran out of memory
 #define HIP_TRY(expr, code)                                                              \
     do {                                                                                 \
         hipError_t e_ = (expr);                                                          \
         if (e_ != hipSuccess) {                                                          \
             set_error("%s failed: %s", #expr, hipGetErrorString(e_));                   \
-            return code;                                                                 \
+            return e_ == hipErrorOutOfMemory ? BFS_ENOMEM : (code);                      \
         }                                                                                \
     } while (0)
 
@@ -116,7 +129,7 @@ hipError_t dalloc(T **p, size_t count) {
 
 void free_all(bfs_graph *g) {
     void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->cf, g->pnb, g->snb, g->deg8, g->in_row_ptr, g->in_col, g->q0, g->q1, g->t0, g->t1,
-                    g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts};
+                    g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts, g->enq};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     void *vptrs[] = {g->va, g->vb, g->vs, g->vo, g->vt, g->vctl};
@@ -178,11 +191,21 @@ int alloc_workspace(bfs_graph *g) {
     };
     for (auto &x : r) {
         if (x.e != hipSuccess) {
+            // a failed allocation leaves HIP's last-error state set: clear it,
+            // or the next launch check (this handle's or another's) reads it
+            (void)hipGetLastError();
             set_error("allocating the %s for n=%d m=%d failed: %s", x.what, g->n, g->m,
                       hipGetErrorString(x.e));
             return x.e == hipErrorOutOfMemory ? BFS_ENOMEM : BFS_EHIP;
         }
     }
+#ifdef FBFS_COUNT_ENQUEUES
+    if (dalloc(&g->enq, n) != hipSuccess) {
+        (void)hipGetLastError();
+        set_error("allocating the enqueue counts for n=%d failed", g->n);
+        return BFS_ENOMEM;
+    }
+#endif
     HIP_TRY(hipMemset(g->ctr, 0, (size_t)NSLOTS * NCTR * CTR_STRIDE * sizeof(unsigned long long)),
             BFS_EHIP);
     HIP_TRY(hipMemset(g->ctl, 0, sizeof(Ctl)), BFS_EHIP);
@@ -209,7 +232,11 @@ int validate_and_classify(bfs_graph *g) {
         set_error("col_idx must be a device pointer when row_ptr[n] = %d > 0", g->m);
         return BFS_EINVAL;
     }
-    HIP_TRY(dalloc(&g->facts, 1), BFS_ENOMEM);
+    if (dalloc(&g->facts, 1) != hipSuccess) {
+        (void)hipGetLastError();
+        set_error("allocating the graph facts failed");
+        return BFS_ENOMEM;
+    }
     GraphFacts h;
     std::memset(&h, 0, sizeof(h));
     h.bad_row = ~0ull;
@@ -534,19 +561,25 @@ extern "C" {
 
 const char *bfs_last_error(void) { return g_err.c_str(); }
 
+int32_t bfs_last_error_code(void) { return g_err_code; }
+
 bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *col_idx) {
     g_err.clear();
+    g_err_code = 0;
     if (n < 1) {
         set_error("n = %d: need at least one vertex", n);
+        g_err_code = BFS_EINVAL;
         return nullptr;
     }
     if (!row_ptr) {
         set_error("row_ptr must be a device pointer (got NULL)");
+        g_err_code = BFS_EINVAL;
         return nullptr;
     }
     bfs_graph *g = new (std::nothrow) bfs_graph();
     if (!g) {
         set_error("host allocation failed");
+        g_err_code = BFS_ENOMEM;
         return nullptr;
     }
     g->n = n;
@@ -554,6 +587,7 @@ bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *co
     g->col_idx = col_idx;
     if (hipGetDevice(&g->device) != hipSuccess) {
         set_error("no HIP device");
+        g_err_code = BFS_EHIP;
         delete g;
         return nullptr;
     }
@@ -588,6 +622,7 @@ bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *co
         g->grid_bu = cus * level_kernel_blocks_per_cu(true);
     }
     if (rc != 0) {
+        g_err_code = rc;
         free_all(g);
         delete g;
         return nullptr;
@@ -729,6 +764,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.max_deg = g->max_degree;
     P.beta = g->beta;
     P.barrier_ticks = g->barrier_ticks;
+    P.enq = g->enq;
 
     if (g->pol_compact != BFS_COMPACT_DEFAULT) return run_variant(g, P, stream);
     const bool timing = g->timing != 0;
@@ -745,6 +781,10 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
         if (timing) HIP_TRY(hipEventRecord(g->events[1], stream), BFS_EHIP);
         HIP_TRY(hipMemcpyAsync(g->host_ctl, g->ctl, sizeof(HostCtl), hipMemcpyDeviceToHost, stream), BFS_EHIP);
         HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+        if (g->host_ctl->err) {
+            set_device_error(g->host_ctl->err, g->host_ctl->err_info, g->barrier_ticks);
+            return BFS_EDEVICE;
+        }
         const int32_t L = g->host_ctl->L;
         g->last_L = L;
         if (timing) {
@@ -823,10 +863,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
         const HostCtl &h = *g->host_ctl;
         if (h.err) {
             g->plan.clear();
-            if (h.err == ERR_BARRIER_TIMEOUT)
-                set_error("small-frontier barrier wait exceeded its limit (%u ticks)", g->barrier_ticks);
-            else
-                set_error("device reported internal error %d (info %d)", h.err, h.err_info);
+            set_device_error(h.err, h.err_info, g->barrier_ticks);
             return BFS_EDEVICE;
         }
         if (h.done) {
@@ -997,6 +1034,10 @@ int32_t bfs_run_noalloc(int32_t n, const int32_t *row_ptr, const int32_t *col_id
         HIP_TRY(launch_one(P, stream), BFS_EHIP);
         HIP_TRY(hipMemcpyAsync(hc, P.ctl, sizeof(hc), hipMemcpyDeviceToHost, stream), BFS_EHIP);
         HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
+        if (hc[2]) {
+            set_device_error(hc[2], hc[3], P.barrier_ticks);
+            return BFS_EDEVICE;
+        }
         return hc[1];
     }
     HIP_TRY(launch_init(P, d->grid, stream), BFS_EHIP);
@@ -1015,10 +1056,7 @@ int32_t bfs_run_noalloc(int32_t n, const int32_t *row_ptr, const int32_t *col_id
         HIP_TRY(hipMemcpyAsync(hc, P.ctl, sizeof(hc), hipMemcpyDeviceToHost, stream), BFS_EHIP);
         HIP_TRY(hipStreamSynchronize(stream), BFS_EHIP);
         if (hc[2]) {
-            if (hc[2] == ERR_BARRIER_TIMEOUT)
-                set_error("small-frontier barrier wait exceeded its limit");
-            else
-                set_error("device reported internal error %d (info %d)", hc[2], hc[3]);
+            set_device_error(hc[2], hc[3], P.barrier_ticks);
             return BFS_EDEVICE;
         }
         if (hc[0]) return hc[1];
@@ -1228,6 +1266,21 @@ int32_t bfs_last_run_kernel_timing(const bfs_graph *g, float *td_ms, int32_t *td
     if (bu_ms) *bu_ms = g->last_kind_ms[1];
     if (bu_launches) *bu_launches = g->last_kind_launches[1];
     return 0;
+}
+
+int32_t bfs_debug_enqueue_counts(const bfs_graph *g, int32_t *counts_out) {
+    if (!g || !counts_out) {
+        set_error("NULL graph handle or output");
+        return BFS_EINVAL;
+    }
+#ifdef FBFS_COUNT_ENQUEUES
+    HIP_TRY(hipSetDevice(g->device), BFS_EHIP);
+    HIP_TRY(hipMemcpy(counts_out, g->enq, sizeof(int32_t) * (size_t)g->n, hipMemcpyDeviceToDevice), BFS_EHIP);
+    return 0;
+#else
+    set_error("this build does not count enqueues (build with -DFBFS_COUNT_ENQUEUES)");
+    return BFS_EINVAL;
+#endif
 }
 
 int32_t bfs_last_run_launch_timing(const bfs_graph *g, int32_t cap, float *ms, uint8_t *ran) {

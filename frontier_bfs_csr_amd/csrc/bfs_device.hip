@@ -207,6 +207,7 @@ __device__ __forceinline__ int list_of(int len) {
 // buffer is full (the expansion loops flush often enough that this is rare).
 __device__ __forceinline__ void emit_single(Ctx &c, int v, int beg, int len) {
     const Params &P = *c.P;
+    FBFS_ENQ(P, v);
     c.fcnt += 1;
     c.fdeg += len;
     c.sh->spilled = 1;
@@ -258,15 +259,23 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
     constexpr int CB = N;
     const Params &P = *c.P;
     bool tryq[CB];
+    // an id outside [0, n) (a graph changed after its checks) is reported,
+    // never used as an index
+    bool okq[CB];
+#pragma unroll
+    for (int q = 0; q < CB; ++q) {
+        okq[q] = ok[q] && (uint32_t)v[q] < (uint32_t)P.n;
+        if (ok[q] && !okq[q]) set_err(P, ERR_BAD_VERTEX, v[q]);
+    }
     if (c.sh->vfilter) {
         uint32_t w[CB];
 #pragma unroll
-        for (int q = 0; q < CB; ++q) w[q] = ok[q] ? P.visited[v[q] >> 5] : ~0u;
+        for (int q = 0; q < CB; ++q) w[q] = okq[q] ? P.visited[v[q] >> 5] : ~0u;
 #pragma unroll
-        for (int q = 0; q < CB; ++q) tryq[q] = ok[q] && !((w[q] >> (v[q] & 31)) & 1u);
+        for (int q = 0; q < CB; ++q) tryq[q] = okq[q] && !((w[q] >> (v[q] & 31)) & 1u);
     } else {
 #pragma unroll
-        for (int q = 0; q < CB; ++q) tryq[q] = ok[q];
+        for (int q = 0; q < CB; ++q) tryq[q] = okq[q];
     }
     uint32_t old[CB];
 #pragma unroll
@@ -295,6 +304,7 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
     if (c.noq) {
 #pragma unroll
         for (int q = 0; q < CB; ++q) {
+            if (win[q]) FBFS_ENQ(P, v[q]);
             c.fcnt += win[q] ? 1 : 0;
             c.fdeg += win[q] ? len[q] - beg[q] : 0;
         }
@@ -381,6 +391,7 @@ __device__ __forceinline__ void flush(Ctx &c) {
         const int beg = sh.sbeg[i];
         const int len = sh.slen[i];
         const int l = list_of(len);
+        FBFS_ENQ(P, v);   // every staged vertex joins the tally above once
         sh.tstart[i] = (int32_t)(ex2 >> 32);
         sh.toff[i] = (int32_t)(ex2 & 0xffffffffull);
         if (l == L_SMALL) {
@@ -720,7 +731,14 @@ __device__ __forceinline__ int probe_first(const BuLds &sh, const uint32_t *cbm,
 // frontier tally counts out-degrees, which differ on a directed graph).
 __device__ __forceinline__ void bu_found(BuCtx &c, int wbase, int v, int u, int d) {
     const Params &P = *c.P;
+    // v comes from this wavefront's own words [wbase, wbase + 64): anything
+    // else is reported, never stored
+    if ((uint32_t)v >= (uint32_t)P.n || (v >> 6) - wbase < 0 || (v >> 6) - wbase >= WAVE) {
+        set_err(P, ERR_BAD_VERTEX, v);
+        return;
+    }
     if (!P.symmetric) d = P.row_ptr[v + 1] - P.row_ptr[v];
+    FBFS_ENQ(P, v);
     __builtin_nontemporal_store(c.level + 1, P.dist + v);   // streaming, as in the word pass
     if (P.parent) __builtin_nontemporal_store(u, P.parent + v);
     atomicOr(&c.sh->bu_fm[wave_id()][(v >> 6) - wbase], 1ull << (v & 63));
@@ -953,8 +971,9 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
 #pragma unroll
             for (int q = 0; q < FW; ++q) {
                 const int par = h1[q] ? f[q] : ((f2[q] >= 0 && ((w[q] >> (f2[q] & 31)) & 1u)) ? f2[q] : -1);
-                const bool hitq = par >= 0;
+                const bool hitq = par >= 0 && v[q] < P.n;   // padding bits past n are set visited
                 if (hitq) {
+                    FBFS_ENQ(P, v[q]);
                     // outputs are never read back: streaming stores keep them
                     // out of the caches the pass reads through
                     __builtin_nontemporal_store(c.level + 1, P.dist + v[q]);
@@ -1039,6 +1058,10 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
     uint64_t *b0 = reinterpret_cast<uint64_t *>(P.fbm0);
     uint64_t *b1 = reinterpret_cast<uint64_t *>(P.fbm1);
     for (int i = tid; i < 3 * CF_WORDS; i += nth) P.cf[i] = 0u;
+#ifdef FBFS_COUNT_ENQUEUES
+    if (P.enq)
+        for (int i = tid; i < P.n; i += nth) P.enq[i] = 0;
+#endif
     for (int wp = tid; wp < P.nwp; wp += nth) {
         const uint64_t sbit = (wp == (s >> 6)) ? (1ull << (s & 63)) : 0ull;
         vis64[wp] = init64[wp] | sbit;

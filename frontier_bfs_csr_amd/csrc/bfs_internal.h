@@ -100,6 +100,7 @@ constexpr int ERR_QUEUE_OVERFLOW = 1;
 constexpr int ERR_TILE_OVERFLOW = 2;
 constexpr int ERR_TSTART_OVERFLOW = 3;
 constexpr int ERR_BARRIER_TIMEOUT = 4;
+constexpr int ERR_BAD_VERTEX = 5;        // a vertex id outside [0, n) met before a store (info: the id)
 
 // small-frontier mode: a top-down level whose frontier has at most SMALL_F
 // vertices and SMALL_E edges runs on the first SMALL_G workgroups only, and
@@ -170,7 +171,22 @@ struct Params {
                               // frontier of a level l with l % 3 == j
     int32_t cf_sh, cf_words;  // vertices per coarse bit (log2); words in use per map
     uint32_t barrier_ticks;   // small-mode barrier wait limit (100 MHz ticks)
+    int32_t *enq;             // debug builds (FBFS_COUNT_ENQUEUES): n per-vertex counts of
+                              // writes into a next frontier, else null
 };
+
+// Debug builds count, per vertex, every write of it into a next frontier (a
+// queue segment, a bitmap-only winner, a bottom-up find), so that a test can
+// check each reached vertex joins exactly one frontier once: duplicates in
+// the frontier leave dist right and are invisible to a dist check.
+#ifdef FBFS_COUNT_ENQUEUES
+#define FBFS_ENQ(P, v)                                  \
+    do {                                                \
+        if ((P).enq) atomicAdd((P).enq + (v), 1);       \
+    } while (0)
+#else
+#define FBFS_ENQ(P, v) ((void)0)
+#endif
 
 // Workspace capacities (segments or entries per stripe region) for a graph of
 // n vertices and m CSR entries; the handle's workspace and the fixed scratch

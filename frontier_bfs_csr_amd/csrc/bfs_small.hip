@@ -42,9 +42,16 @@ __global__ __launch_bounds__(ONE_BLOCK) void bfs_one_kernel(Params P) {
     for (int i = tid; i < n; i += ONE_BLOCK) {
         P.dist[i] = (i == s) ? 0 : -1;
         if (P.parent) P.parent[i] = (i == s) ? s : -1;
+#ifdef FBFS_COUNT_ENQUEUES
+        if (P.enq) P.enq[i] = 0;
+#endif
     }
     for (int w = tid; w < ONE_N / 32; w += ONE_BLOCK) sh.vis[w] = (w == (s >> 5)) ? (1u << (s & 31)) : 0u;
-    if (tid == 0) sh.q[0][0] = s;
+    if (tid == 0) {
+        sh.q[0][0] = s;
+        P.ctl->err = 0;
+        P.ctl->err_info = 0;
+    }
     __syncthreads();
     int F = 1, cur = 0, k = 0;
     while (F > 0 && k < n) {
@@ -110,10 +117,15 @@ __global__ __launch_bounds__(ONE_BLOCK) void bfs_one_kernel(Params P) {
 #pragma unroll
             for (int q = 0; q < ONE_CB; ++q) {
                 if (u[q] < 0) continue;
+                if (u[q] >= n) {   // a graph changed after its checks: reported, never stored
+                    if (P.ctl->err == 0) { P.ctl->err = ERR_BAD_VERTEX; P.ctl->err_info = u[q]; }
+                    continue;
+                }
                 const uint32_t bit = 1u << (u[q] & 31);
                 if (atomicOr(&sh.vis[u[q] >> 5], bit) & bit) continue;
                 P.dist[u[q]] = k + 1;
                 if (P.parent) P.parent[u[q]] = sh.q[cur][o[q]];
+                FBFS_ENQ(P, u[q]);
                 sh.q[nxt][atomicAdd(&sh.ncount, 1)] = u[q];
             }
         }
@@ -125,8 +137,6 @@ __global__ __launch_bounds__(ONE_BLOCK) void bfs_one_kernel(Params P) {
     if (tid == 0) {
         P.ctl->L = k;
         P.ctl->done = 1;
-        P.ctl->err = 0;
-        P.ctl->err_info = 0;
     }
 }
 

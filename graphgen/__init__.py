@@ -366,9 +366,13 @@ def grid_damaged(w=4096, h=4096, delete_frac=0.05, seed=4):
 
 
 # Truncated power-law expected degrees for the small Chung-Lu workload,
-# calibrated once (deterministic search on seed 1) so that the kept component
-# has median degree ~3, mean ~9 and max ~1,255.
-CHUNG_LU_PARAMS = {"n0": 3485, "gamma": 2.1, "w_hi": 2500.0, "i_scale": 1.0, "w_lo": 1.0}
+# calibrated once by a deterministic grid search on seed 1 over (n0, w_hi,
+# i_scale) so that the kept component has about the word graph's 3,485
+# vertices and ~31k CSR entries, median degree ~3, mean ~9 and max ~1,255:
+# n0 = 3,740 generated vertices leave a component of 3,482 vertices and
+# 30,418 entries (median 3, mean 8.74, max 1,275).  The word graph is itself
+# one large component with a few strays (its search reaches 3,434 of 3,485).
+CHUNG_LU_PARAMS = {"n0": 3740, "gamma": 2.1, "w_hi": 2550.0, "i_scale": 1.1, "w_lo": 1.0}
 
 
 def chung_lu_weights(n0, gamma, w_hi, i_scale, w_lo):

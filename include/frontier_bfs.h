@@ -101,11 +101,31 @@ int32_t bfs_run_noalloc(int32_t n, const int32_t *row_ptr, const int32_t *col_id
                         int32_t *dist_out, int32_t *parent_out, int32_t *level_sizes_out,
                         hipStream_t stream);
 
-/* Frees the workspace.  NULL is a no-op.  Synchronises the device first. */
+/*
+ * Frees the handle's workspace (the counterpart of the frees at the end of
+ * bfs.cu's main in the Day 38 program, which releases the device graph and
+ * the search's buffers once the runs are done).  The caller's row_ptr,
+ * col_idx and output arrays are not touched.  NULL is a no-op.  Synchronises
+ * the device first, so work still queued on the handle finishes.
+ */
 void bfs_graph_destroy(bfs_graph *g);
 
-/* Thread-local description of the last failure on this thread ("" if none). */
+/*
+ * Thread-local description of the last failure on this thread ("" if none).
+ * It names the first bad index where there is one: the Day 38 program's
+ * loadGraph rejects a graph file at its first bad line, and its CUDA_CHECK
+ * reports a failed call with the runtime's error text; here both come back
+ * as text and a return code instead of an exit.
+ */
 const char *bfs_last_error(void);
+
+/*
+ * The BFS_E* code behind the last NULL that bfs_graph_create returned on this
+ * thread (BFS_EINVAL: invalid graph or argument; BFS_ENOMEM: the workspace
+ * did not fit; BFS_EHIP: a HIP call failed); 0 after a successful create.
+ * Same sources as bfs_last_error.
+ */
+int32_t bfs_last_error_code(void);
 
 /* ---- measurement and test hooks (results never depend on them) --------- */
 
@@ -168,7 +188,12 @@ int32_t bfs_set_switch(bfs_graph *g, int32_t alpha, int32_t beta);
 
 /*
  * Per-level record of the last bfs_run on this handle, for the byte model and
- * tests.  For k < min(L, cap): dir[k] = 0 for a top-down level, 1 for a
+ * tests: the per-level table of the "Day 38 - Graph traversal on a GPU" page
+ * (section "What a level-synchronous search actually launches": frontier
+ * size and edges to walk per level), with the direction each level ran in
+ * (PMPP ch.15 notes, section 15.7: push or pull per level).  The frontier
+ * sizes themselves are level_sizes_out of bfs_run.
+ * For k < min(L, cap): dir[k] = 0 for a top-down level, 1 for a
  * bottom-up level; frontier_edges[k] = sum of degrees of level k's vertices.
  * Either array may be NULL.  Host memory.  Returns L of that run (0 if none
  * yet), or a negative code.
@@ -219,6 +244,21 @@ int32_t bfs_last_run_kernel_timing(const bfs_graph *g, float *td_ms, int32_t *td
  * paths and the non-default compactions record no launches (count 0).
  */
 int32_t bfs_last_run_launch_timing(const bfs_graph *g, int32_t cap, float *ms, uint8_t *ran);
+
+/*
+ * Validator V5 of a debug build: copies to counts_out (device, n entries) how
+ * many times each vertex was written into a next frontier during the last
+ * bfs_run on this handle (a queue segment, a bitmap-only winner of a wide
+ * top-down level, a bottom-up find); the source, the initial frontier, reads
+ * 0.  On a correct search every other reached vertex reads exactly 1 and
+ * every unreached vertex 0: a frontier with duplicates ("Day 38 - Graph
+ * traversal on a GPU", Pitfalls; Chapter 22, section 22.1, where a naive
+ * claim discovers a vertex twice) still gives the right dist, so only a count
+ * shows it.  Runs of the default direction-optimising path only (not the
+ * non-default compactions).  Returns 0; BFS_EINVAL for a NULL argument or a
+ * library built without -DFBFS_COUNT_ENQUEUES (the normal build).
+ */
+int32_t bfs_debug_enqueue_counts(const bfs_graph *g, int32_t *counts_out);
 
 /*
  * Claim and compaction primitives of the top-down level (Gunrock reading

@@ -111,3 +111,35 @@ def check_graph(g, sources=None, policies=None, label="", ref_cache=None):
                 want_fe = np.bincount(ref[0][ref[0] >= 0], weights=deg[ref[0] >= 0],
                                       minlength=L).astype(np.int64)
                 assert (fe == want_fe).all(), f"{label}: frontier edge sums"
+
+
+def check_sources_parallel(g, sources, policy="auto", chunk=8, workers=8, label=""):
+    """dist, L and level sizes bit-exact, parents valid, for many sources of a
+    large graph under one policy: the oracle's searches and the checks run on
+    host threads (the oracle is C and releases the interpreter lock), the GPU
+    searches one after another, `chunk` sources at a time."""
+    from concurrent.futures import ThreadPoolExecutor
+    import frontier_bfs_csr_amd as fb
+    rp, ci = to_dev(g)
+    d, a, lp = POLICIES[policy]
+    sources = [int(s) for s in sources]
+    with fb.BfsGraph(rp, ci) as bg, ThreadPoolExecutor(workers) as pool:
+        bg.set_policy(d, a, lp)
+        for c0 in range(0, len(sources), chunk):
+            part = sources[c0:c0 + chunk]
+            refs = list(pool.map(lambda s: oracle.bfs(g.row_ptr, g.col_idx, s), part))
+            outs = []
+            for s in part:
+                print(f"[gpu] {label or g.name} n={g.n} m={g.m} source={s} policy={policy}",
+                      file=sys.stderr, flush=True)
+                outs.append(run_hip(bg, g.n, s))
+
+            def chk(i):
+                s, ref = part[i], refs[i]
+                L, dist, parent, sizes = outs[i]
+                oracle.assert_bfs_ok(g.row_ptr, g.col_idx, s, ref, dist, parent, L, sizes[:L],
+                                     symmetric=g.symmetric, label=f"{label or g.name} s={s} {policy}")
+                assert (sizes[L:] == -7).all(), f"{label}: level sizes written beyond L"
+                return True
+            assert all(pool.map(chk, range(len(part))))
+    return len(sources)

@@ -48,3 +48,9 @@ def test_component_edges():
     # directed: the reached vertices' out-edges, each counted once
     assert bench.component_edges(np.array([2, 0, 1]), np.array([0, 1, -1]), symmetric=False) == 2
     assert bench.component_edges(deg, np.full(4, -1), symmetric=True) == 0
+
+
+def test_host_cpu_fields():
+    h = bench.host_cpu()
+    assert isinstance(h["cpu_model"], str) and h["cpu_model"]
+    assert h["nproc"] >= 1 and h["cpu_count"] >= h["nproc"]

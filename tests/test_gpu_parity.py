@@ -7,7 +7,7 @@ import pytest
 
 import graphgen as gg
 import oracle
-from gpu_util import check_graph, run_hip, sorted_rows_copy, to_dev
+from gpu_util import check_graph, check_sources_parallel, run_hip, sorted_rows_copy, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -69,15 +69,20 @@ def test_c1_workload():
     check_graph(g, sources=list(g.sources) + [0, g.n - 1])
 
 
-def test_c2_workload_sampled():
+def test_c2_workload_all_sources():
+    """R-MAT scale 20: all 64 sources under the default policy, every policy
+    on the first four."""
     g = gg.c2_rmat20(nsrc=64)
+    assert check_sources_parallel(g, g.sources) == 64
     check_graph(g, sources=g.sources[:4])
-    check_graph(g, sources=g.sources[4:12], policies=["auto"])
 
 
-def test_c3_workload_sampled():
+def test_c3_workload_all_sources():
+    """Erdos-Renyi, 4M vertices: all 64 sources under the default policy; the
+    binned and edge-balanced push advances and pull on two."""
     g = gg.c3_er(nsrc=64)
-    check_graph(g, sources=g.sources[:2], policies=["auto", "push_binned", "push_edge"])
+    assert check_sources_parallel(g, g.sources) == 64
+    check_graph(g, sources=g.sources[:2], policies=["push_binned", "push_edge", "pull"])
 
 
 def test_c4_workload():
@@ -88,10 +93,11 @@ def test_c4_workload():
 
 def test_c5_workload_sampled():
     """R-MAT scale 24 at full size, in the benchmark's configuration (auto
-    policy, parents and level sizes written), on a sample of its sources."""
+    policy, parents and level sizes written), on the first 16 of its 64
+    sources; the other policies on two more."""
     g = gg.c5_rmat24(nsrc=64)
-    check_graph(g, sources=g.sources[:2], policies=["auto"])
-    check_graph(g, sources=g.sources[2:3], policies=["push_binned", "pull"])
+    assert check_sources_parallel(g, g.sources[:16]) == 16
+    check_graph(g, sources=g.sources[16:18], policies=["push_binned", "push_edge", "pull", "auto_chain"])
 
 
 @pytest.mark.parametrize("alpha,beta", [(1, 1), (1, 10**6), (10**6, 1), (10**6, 10**6), (4, 64)])
@@ -160,7 +166,18 @@ def test_timing_hooks():
             assert kt["td"][1] - kt["bu"][1] in (0, 1), kt   # they alternate, top-down first
             assert abs(kt["td"][0] + kt["bu"][0] - level_ms) <= 1e-3 * max(1.0, level_ms)
             _, dirs, _ = bg.stats()
-            assert (kt["bu"][0] > 0) == bool((dirs == 1).any()) or kt["bu"][0] > 0
+            ms, ran = bg.launch_timing()
+            assert ms.shape[0] == launches
+            assert abs(float(ms.sum()) - level_ms) <= 1e-3 * max(1.0, level_ms)
+            # every bottom-up level ran in a bottom-up launch of its own, which
+            # recorded it; one more bottom-up record when such a launch found
+            # the empty frontier
+            nbu = int((dirs == 1).sum())
+            assert int((ran == 2).sum()) in (nbu, nbu + 1), (pol, dirs, ran)
+            assert kt["bu"][1] >= nbu
+            if pol[2] == 2:   # one level per launch: a top-down record per top-down level
+                ntd = int((dirs == 0).sum())
+                assert int((ran == 1).sum()) in (ntd, ntd + 1), (pol, dirs, ran)
             assert init_ms > 0 and level_ms > 0
             bg.set_timing(False)
 
