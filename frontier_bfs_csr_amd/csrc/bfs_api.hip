@@ -60,6 +60,8 @@ struct bfs_graph {
     uint32_t *visited = nullptr, *vis_init = nullptr, *fbm0 = nullptr, *fbm1 = nullptr;
     uint32_t *cf = nullptr;        // 3 coarse frontier maps
     int32_t *pnb = nullptr;        // in-neighbour of highest out-degree of each vertex
+    int4 *sreg = nullptr;          // small-frontier regions
+    unsigned long long *sslot = nullptr;   // small-frontier words
     int32_t *snb = nullptr;        // ... and of second highest
     uint8_t *deg8 = nullptr;       // in-degrees in a byte (255: 255 or more)
     int32_t *in_row_ptr = nullptr, *in_col = nullptr;   // transpose (directed graphs)
@@ -129,7 +131,7 @@ hipError_t dalloc(T **p, size_t count) {
 
 void free_all(bfs_graph *g) {
     void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->cf, g->pnb, g->snb, g->deg8, g->in_row_ptr, g->in_col, g->q0, g->q1, g->t0, g->t1,
-                    g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts, g->enq};
+                    g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts, g->enq, g->sreg, g->sslot};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     void *vptrs[] = {g->va, g->vb, g->vs, g->vo, g->vt, g->vctl};
@@ -184,6 +186,8 @@ int alloc_workspace(bfs_graph *g) {
         {dalloc(&g->t1, (size_t)STRIPES * g->tcap), "tile queue"},
         {dalloc(&g->ts0, (size_t)NLISTS * STRIPES * g->tscap), "tile start table"},
         {dalloc(&g->ts1, (size_t)NLISTS * STRIPES * g->tscap), "tile start table"},
+        {dalloc(&g->sreg, (size_t)2 * SMALL_G * SREG_CAP), "small-frontier regions"},
+        {dalloc(&g->sslot, (size_t)2 * SMALL_G), "small-frontier words"},
         {dalloc(&g->ctr, (size_t)NSLOTS * NCTR * CTR_STRIDE), "counters"},
         {dalloc(&g->ctl, 1), "control block"},
         {dalloc(&g->st_dir, (size_t)g->st_cap), "level stats"},
@@ -508,7 +512,9 @@ constexpr int64_t NA_T0 = NA_Q1 + na_round(STRIPES * queue_cap(NA_N) * (int64_t)
 constexpr int64_t NA_T1 = NA_T0 + na_round(STRIPES * tile_cap(NA_M) * (int64_t)sizeof(Seg));
 constexpr int64_t NA_TS0 = NA_T1 + na_round(STRIPES * tile_cap(NA_M) * (int64_t)sizeof(Seg));
 constexpr int64_t NA_TS1 = NA_TS0 + na_round((int64_t)NLISTS * STRIPES * tstart_cap(NA_M) * 4);
-constexpr int64_t NA_STDIR = NA_TS1 + na_round((int64_t)NLISTS * STRIPES * tstart_cap(NA_M) * 4);
+constexpr int64_t NA_SREG = NA_TS1 + na_round((int64_t)NLISTS * STRIPES * tstart_cap(NA_M) * 4);
+constexpr int64_t NA_SSLOT = NA_SREG + na_round((int64_t)2 * SMALL_G * SREG_CAP * 16);
+constexpr int64_t NA_STDIR = NA_SSLOT + na_round((int64_t)2 * SMALL_G * 8);
 constexpr int64_t NA_STFDEG = NA_STDIR + na_round(stats_cap(NA_N));
 constexpr int64_t NA_BYTES = NA_STFDEG + na_round(stats_cap(NA_N) * 8);
 
@@ -765,6 +771,8 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.beta = g->beta;
     P.barrier_ticks = g->barrier_ticks;
     P.enq = g->enq;
+    P.sreg = g->sreg;
+    P.sslot = g->sslot;
 
     if (g->pol_compact != BFS_COMPACT_DEFAULT) return run_variant(g, P, stream);
     const bool timing = g->timing != 0;
@@ -1008,6 +1016,8 @@ int32_t bfs_run_noalloc(int32_t n, const int32_t *row_ptr, const int32_t *col_id
     P.tscap = tstart_cap(m);
     P.ctr = reinterpret_cast<unsigned long long *>(base + NA_CTR);
     P.ctl = reinterpret_cast<Ctl *>(base + NA_CTL);
+    P.sreg = reinterpret_cast<int4 *>(base + NA_SREG);
+    P.sslot = reinterpret_cast<unsigned long long *>(base + NA_SSLOT);
     P.st_dir = reinterpret_cast<int8_t *>(base + NA_STDIR);
     P.st_fdeg = reinterpret_cast<int64_t *>(base + NA_STFDEG);
     P.st_cap = (int32_t)stats_cap(n);

@@ -91,6 +91,8 @@ struct LevelCommon {
     int32_t mode;                     // 0 exit, 1 finish, 2 run
     int32_t dir, input_bm, wbits, wcf, clear_bm, adv_eb, small, use_cf, cf_clear, noq;
     int32_t fsize;
+    int32_t prev_wcf;                 // the level before set the coarse map of this one
+    int64_t prev_fdeg;                // the level before's frontier edges
     int64_t fdeg, reached_before, edges_before;
     int32_t lcount[NLISTS * STRIPES];  // segments per (list, stripe)
     int32_t ledges[NLISTS * STRIPES];  // edges per (list, stripe)
@@ -113,6 +115,13 @@ struct TdLds : LevelCommon {
     int32_t nbig;
     int32_t fl_cnt[WAVES], fl_more[WAVES];   // from-bitmap lists: count, words left
     int32_t vfilter;                  // claims first load the visited words
+    // small-frontier mode
+    int32_t rcnt;                     // this workgroup's winners in its region
+    int32_t rbig;                     // ... one of them has at least T_WG edges
+    unsigned long long redges;        // ... and their edges
+    int32_t spre[SMALL_G + 1];        // exclusive prefix of the workgroups' winners
+    int32_t s_total, s_err, s_big;    // winners of all workgroups; an error was recorded; a big one
+    unsigned long long s_edges;       // their edges (saturating per workgroup at 2^24 - 1)
 };
 
 // ... and the bottom-up kernel's, per wavefront; kept small so that several
@@ -145,6 +154,8 @@ struct CtxT {
     int32_t noq;            // no queue: winners are tallied per thread, not staged
     Seg *nq, *nt;           // queues of level k+1
     int32_t *nts;
+    int4 *region;           // small-frontier mode: winners go to this region (else staged)
+    int32_t converting;     // the flush converts a region already counted (enqueue counts)
     // per-thread tallies of new frontier vertices
     int32_t fcnt;
     int64_t fdeg;
@@ -243,6 +254,29 @@ __device__ __forceinline__ void stage(Ctx &c, bool win, int v, int beg, int len)
     if (spill) emit_single(c, v, beg, len);
 }
 
+// Small-frontier mode: a winner (adjacency [beg, beg+len)) goes straight to
+// this workgroup's region (wave-aggregated LDS atomic for its place); the
+// region's count and edges are kept in LDS.
+__device__ __forceinline__ void stage_region(Ctx &c, bool win, int v, int beg, int len) {
+    const uint64_t m = __ballot(win);
+    if (m == 0) return;
+    const int leader = __ffsll((unsigned long long)m) - 1;
+    int base = 0;
+    if (lane_id() == leader) base = atomicAdd(&c.sh->rcnt, __popcll(m));
+    base = readlane_i(base, leader);
+    if (win) {
+        const int slot = base + mbcnt64(m);
+        atomicAdd(&c.sh->redges, (unsigned long long)(uint32_t)len);
+        if (len >= T_WG) c.sh->rbig = 1;
+        if (slot < SREG_CAP) {
+            c.region[slot] = make_int4(v, beg, len, 0);
+            FBFS_ENQ(*c.P, v);
+        } else {
+            set_err(*c.P, ERR_QUEUE_OVERFLOW, slot);
+        }
+    }
+}
+
 // Claim up to N targets (v[q] valid where ok[q], reached from u[q]) for
 // level k+1: one atomicOr per target on the visited bitmap decides its single
 // winner.  On wide levels (vfilter) a plain load of the visited words first
@@ -308,6 +342,11 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
             c.fcnt += win[q] ? 1 : 0;
             c.fdeg += win[q] ? len[q] - beg[q] : 0;
         }
+        return;
+    }
+    if (c.region) {
+#pragma unroll
+        for (int q = 0; q < CB; ++q) stage_region(c, win[q], v[q], beg[q], len[q] - beg[q]);
         return;
     }
 #pragma unroll
@@ -391,7 +430,7 @@ __device__ __forceinline__ void flush(Ctx &c) {
         const int beg = sh.sbeg[i];
         const int len = sh.slen[i];
         const int l = list_of(len);
-        FBFS_ENQ(P, v);   // every staged vertex joins the tally above once
+        if (!c.converting) FBFS_ENQ(P, v);   // every staged vertex joins the tally above once
         sh.tstart[i] = (int32_t)(ex2 >> 32);
         sh.toff[i] = (int32_t)(ex2 & 0xffffffffull);
         if (l == L_SMALL) {
@@ -1058,6 +1097,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
     uint64_t *b0 = reinterpret_cast<uint64_t *>(P.fbm0);
     uint64_t *b1 = reinterpret_cast<uint64_t *>(P.fbm1);
     for (int i = tid; i < 3 * CF_WORDS; i += nth) P.cf[i] = 0u;
+    for (int i = tid; i < 2 * SMALL_G; i += nth) P.sslot[i] = 0ull;
 #ifdef FBFS_COUNT_ENQUEUES
     if (P.enq)
         for (int i = tid; i < P.n; i += nth) P.enq[i] = 0;
@@ -1076,7 +1116,6 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
             P.ctl->done = 0; P.ctl->L = 0; P.ctl->err = 0; P.ctl->err_info = 0;
             for (int i = 0; i < RAN_CAP; ++i) P.ctl->ran[i] = 0;
             P.ctl->lvl[0] = 0; P.ctl->lvl[1] = 0;
-            P.ctl->bar_count = 0ull;
             for (int k = 0; k < NSLOTS; ++k) {
                 P.ctl->slot[k].dir = 0; P.ctl->slot[k].wbits = 0; P.ctl->slot[k].wcf = 0;
                 P.ctl->slot[k].input_bm = 0; P.ctl->slot[k].fsize = 0; P.ctl->slot[k].noq = 0;
@@ -1088,6 +1127,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
             Ctx c;
             c.P = &P; c.sh = nullptr; c.level = -1; c.wg = 0; c.G = 1; c.stripe = 0; c.nslot = 0; c.wbits = 0;
             c.nbm = nullptr; c.ncf = nullptr; c.wcf = 0; c.noq = 0; c.nq = P.q0; c.nt = P.t0; c.nts = P.ts0; c.fcnt = 0; c.fdeg = 0;
+            c.region = nullptr; c.converting = 0;
             const int beg = P.row_ptr[s];
             const int len = P.row_ptr[s + 1] - beg;
             const int l = list_of(len);
@@ -1140,6 +1180,8 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
     }
     if (lane == 0) {
         sh.fsize = (int32_t)fsize; sh.fdeg = fdeg;
+        sh.prev_wcf = prev.wcf;
+        sh.prev_fdeg = (k > 0) ? edges_before - prev.edges_before : 0;
         sh.small = 0;
         sh.use_cf = 0;
         sh.noq = 0;
@@ -1200,60 +1242,39 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
     }
 }
 
-// Barrier among the G workgroups of the small-frontier mode (all resident:
-// the others exit at once).  The arrival count only grows: arrivals
-// [jG, (j+1)G) make up the j-th barrier of the search, since no workgroup can
-// arrive at barrier j+1 before barrier j is complete, so the count before a
-// workgroup's own arrival names its barrier and the barrier opens when the
-// count reaches (j+1)G -- the last arrival opens it with its own atomic, and
-// no second word has to be written and read.  Release before arriving,
-// acquire after leaving, both at device scope, so queues, bitmaps and
-// counters written before it are seen after it.  The wait is bounded: past
-// the limit it records ERR_BARRIER_TIMEOUT and returns, and every workgroup
-// then leaves its loop.
-__device__ __forceinline__ void small_barrier(const Params &P, int G) {
+// This workgroup's per-thread tallies of new frontier vertices (and their
+// edges) into one striped atomic of the next level's vertex counters.
+template <class S>
+__device__ __forceinline__ void add_tallies(CtxT<S> &c) {
+    auto &sh = *c.sh;
+    const int lane = lane_id();
+    // a workgroup's vertices and their edges number below 2^31: 32-bit scans
+    const int64_t wc = (uint32_t)readlane_i((int)wave_incl_scan_u32((uint32_t)c.fcnt), WAVE - 1);
+    const int64_t wd = (uint32_t)readlane_i((int)wave_incl_scan_u32((uint32_t)c.fdeg), WAVE - 1);
+    __syncthreads();
+    if (lane == 0) { sh.scan_tmp[0][wave_id()] = (uint64_t)wc; sh.scan_tmp[1][wave_id()] = (uint64_t)wd; }
     __syncthreads();
     if (threadIdx.x == 0) {
-        // one release before arriving and one acquire after the barrier
-        // opens; the arrival and the polls are relaxed device-scope atomics
-        // (coherent, so a poll sees the last arrival without a fence of its own)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const unsigned long long before =
-            __hip_atomic_fetch_add(&P.ctl->bar_count, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned long long open_at = (before / (unsigned long long)G + 1ull) * (unsigned long long)G;
-        if (before + 1ull < open_at) {
-            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-            while (__hip_atomic_load(&P.ctl->bar_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < open_at) {
-                __builtin_amdgcn_s_sleep(2);
-                if (__builtin_amdgcn_s_memrealtime() - t0 > P.barrier_ticks) {
-                    atomicCAS(&P.ctl->err, 0, ERR_BARRIER_TIMEOUT);
-                    break;
-                }
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        uint64_t tc = 0, td = 0;
+        for (int w = 0; w < WAVES; ++w) { tc += sh.scan_tmp[0][w]; td += sh.scan_tmp[1][w]; }
+        if (tc) atomicAdd(ctr_at(*c.P, c.nslot, VC_BASE + c.stripe), (unsigned long long)((tc << 32) | td));
     }
-    __syncthreads();
 }
 
-// One level on the G workgroups taking part (this one is number wg); BU
-// selects the direction's code (the decision in sh must agree).
-template <bool BU, class S>
-__device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg, int G) {
-    const int lane = lane_id();
-    const int slot = k % NSLOTS;
-    if constexpr (!BU) {
-        if (threadIdx.x == 0) {
-            sh.cnt = 0;
-            sh.spilled = 0;
-            sh.nbig = 0;
-            // a visited-word load before each claim pays on levels with many
-            // edges (it spares the atomics of targets already reached)
-            sh.vfilter = sh.fdeg >= VFILTER_EDGES;
-        }
-    }
-    // unit prefix tables: one lane per (list, stripe) and a wavefront scan
-    // (a serial loop here waits out one LDS round trip per entry)
+// Will a small level's winners make a small frontier again?  The next
+// frontier's edges are predicted as this level's edges times their growth
+// since the level before: a level that grows out of the small-frontier mode
+// writes the queue lists at once and ends the launch, instead of its
+// workgroups publishing regions and converting them afterwards.
+__device__ __forceinline__ bool grows_out(int64_t fdeg, int64_t fprev) {
+    const double g = (double)fdeg / (double)(fprev > 0 ? fprev : 1);
+    return (double)fdeg * (g > 1.0 ? g : 1.0) > (double)SMALL_E;
+}
+
+// Unit prefix tables of a level read from the queue lists: one lane per
+// (list, stripe) and a wavefront scan (a serial loop here waits out one LDS
+// round trip per entry).  The caller synchronises before using them.
+__device__ __forceinline__ void unit_prefix(LevelCommon &sh) {
     if (threadIdx.x < WAVE) {
         const int r = threadIdx.x;
         int units = 0;
@@ -1268,6 +1289,28 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
         if (r < NLISTS * STRIPES) sh.uprefix[r] = incl - units;
         if (r == NLISTS * STRIPES - 1) sh.uprefix[NLISTS * STRIPES] = incl;
     }
+}
+
+// One level on the G workgroups taking part (this one is number wg); BU
+// selects the direction's code (the decision in sh must agree).
+template <bool BU, class S>
+__device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg, int G, bool to_region = false) {
+    const int lane = lane_id();
+    const int slot = k % NSLOTS;
+    if constexpr (!BU) {
+        if (threadIdx.x == 0) {
+            sh.cnt = 0;
+            sh.spilled = 0;
+            sh.nbig = 0;
+            sh.rcnt = 0;
+            sh.rbig = 0;
+            sh.redges = 0ull;
+            // a visited-word load before each claim pays on levels with many
+            // edges (it spares the atomics of targets already reached)
+            sh.vfilter = sh.fdeg >= VFILTER_EDGES;
+        }
+    }
+    unit_prefix(sh);
     // bookkeeping of level k by workgroup 0
     if (wg == 0) {
         if (threadIdx.x == 0) {
@@ -1297,6 +1340,9 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
     c.wbits = sh.wbits;
     c.wcf = sh.wcf;
     c.noq = sh.noq;
+    // the small-frontier mode's first level: winners to this workgroup's region
+    c.region = to_region ? P.sreg + ((size_t)((k + 1) & 1) * SMALL_G + wg) * SREG_CAP : nullptr;
+    c.converting = 0;
     const int cur = k & 1;
     uint32_t *cbm = cur ? P.fbm1 : P.fbm0;
     uint32_t *obm = cur ? P.fbm0 : P.fbm1;
@@ -1332,16 +1378,260 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
     if constexpr (!BU) {
         if (!sh.spilled && !sh.noq) return;
     }
-    // a workgroup's vertices and their edges number below 2^31: 32-bit scans
-    const int64_t wc = (uint32_t)readlane_i((int)wave_incl_scan_u32((uint32_t)c.fcnt), WAVE - 1);
-    const int64_t wd = (uint32_t)readlane_i((int)wave_incl_scan_u32((uint32_t)c.fdeg), WAVE - 1);
-    __syncthreads();
-    if (lane == 0) { sh.scan_tmp[0][wave_id()] = (uint64_t)wc; sh.scan_tmp[1][wave_id()] = (uint64_t)wd; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint64_t tc = 0, td = 0;
-        for (int w = 0; w < WAVES; ++w) { tc += sh.scan_tmp[0][w]; td += sh.scan_tmp[1][w]; }
-        if (tc) atomicAdd(ctr_at(P, c.nslot, VC_BASE + c.stripe), (unsigned long long)((tc << 32) | td));
+    add_tallies(c);
+}
+
+// Small-frontier mode: top-down levels k, k+1, ... on the first G
+// workgroups while they stay small (at most SMALL_F vertices and SMALL_E
+// edges) and top-down, so that a long thin search needs few launches.  Per
+// level, each workgroup appends the vertices it wins to its own region (no
+// shared reservation), then publishes one 64-bit word {level, count, edges}
+// after a release; every workgroup waits for all G words of the level with
+// an acquire.  Those words are the barrier, and they also give the next
+// level's size and work split: each workgroup takes an equal share of the
+// frontier's entries, located from the prefix of the counts, and expands them
+// lane, wavefront or workgroup per entry by degree.  Level k itself reads
+// the queue lists the launch started from.  When the next level is not small
+// (or pulls), each workgroup converts its region into that level's queue
+// lists and counters with the usual flush, and the next launch takes over.
+// The wait for the words is bounded: past the limit the search ends with
+// ERR_BARRIER_TIMEOUT.  Returns the level the next launch starts at, or -1
+// when this launch found the empty frontier or an error was recorded.
+// word layout: bits 40-63 level + 1 (24 bits), 25-39 winners (at most
+// SMALL_E), 24 a winner has at least T_WG edges, 0-23 their edges
+// (saturating at 2^24 - 1, far above SMALL_E)
+constexpr uint32_t SW_SEQ_MASK = 0xffffffu;
+constexpr unsigned long long SW_EDGE_MAX = 0xffffffull;
+
+__device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int launch, int G) {
+    const int wg = blockIdx.x;
+    const int lane = lane_id();
+    // level k has run (run_level, its winners in the regions); the level
+    // state as decide() left it, kept in sh from level to level
+    for (;;) {
+        const int cur = k & 1;
+        const int fsize = sh.fsize, wbits = sh.wbits, wcf = sh.wcf;
+        const int64_t fdeg = sh.fdeg;
+        // publish this workgroup's winners of level k+1
+        const uint32_t want = (uint32_t)(k + 1) & SW_SEQ_MASK;
+        unsigned long long *words = P.sslot + (size_t)((k + 1) & 1) * SMALL_G;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned long long cnt = (unsigned long long)min(sh.rcnt, SREG_CAP);
+            const unsigned long long ed = sh.redges < SW_EDGE_MAX ? sh.redges : SW_EDGE_MAX;
+            const unsigned long long big = sh.rbig ? 1ull : 0ull;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __hip_atomic_store(words + wg, ((unsigned long long)want << 40) | (cnt << 25) | (big << 24) | ed,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // wait for every workgroup's word: lane w polls workgroup w's
+        if (threadIdx.x < WAVE) {
+            const bool mine = lane < G;
+            unsigned long long word = 0ull;
+            bool late = false;
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            for (;;) {
+                if (mine) word = __hip_atomic_load(words + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const bool ok = !mine || (uint32_t)(word >> 40) == want;
+                if (__ballot(!ok) == 0ull) break;
+                __builtin_amdgcn_s_sleep(1);
+                if (__builtin_amdgcn_s_memrealtime() - t0 > P.barrier_ticks) {
+                    late = true;
+                    break;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            const int cnt = mine ? (int)((word >> 25) & 0x7fffull) : 0;
+            const bool anybig = __ballot(mine && ((word >> 24) & 1ull)) != 0ull;
+            const uint32_t ed = mine ? (uint32_t)(word & SW_EDGE_MAX) : 0u;   // G * 2^24 < 2^32
+            const int incl = wave_incl_scan_i32(cnt);
+            const uint32_t eincl = wave_incl_scan_u32(ed);
+            // cross-lane reads in uniform control flow: inside a branch on
+            // the lane, the scans' last steps may be left to that lane only
+            const int total = readlane_i(incl, WAVE - 1);
+            const uint32_t etotal = (uint32_t)readlane_i((int)eincl, WAVE - 1);
+            if (mine) sh.spre[lane] = incl - cnt;
+            if (lane == 0) {
+                if (late) atomicCAS(&P.ctl->err, 0, ERR_BARRIER_TIMEOUT);
+                sh.spre[G] = total;
+                sh.s_total = total;
+                sh.s_edges = etotal;
+                sh.s_big = anybig;
+                sh.s_err = late || __hip_atomic_load(&P.ctl->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+            }
+        }
+        __syncthreads();
+        if (sh.s_err) return -1;
+        const int F1 = sh.s_total;
+        const int64_t E1 = (int64_t)sh.s_edges;
+        const int64_t reached_before = sh.reached_before + fsize;
+        const int64_t edges_before = sh.edges_before + fdeg;
+        if (F1 == 0) {
+            if (wg == 0 && threadIdx.x == 0) {
+                P.ctl->L = k + 1;
+                P.ctl->done = 1;
+                if (launch < RAN_CAP) P.ctl->ran[launch] = 1;
+            }
+            return -1;
+        }
+        // the direction of level k+1, as decide() takes it after a top-down
+        // level (edges saturate only above SMALL_E, where the next launch
+        // decides again from the exact counters)
+        const int64_t m_u = (int64_t)P.m - edges_before - E1;
+        const bool want_pull = P.pol_dir == BFS_DIR_PULL || (P.pol_dir == BFS_DIR_AUTO && E1 * P.alpha > m_u);
+        const bool pull = want_pull && P.can_pull && wbits;   // level k set the next bitmap
+        Ctx c;
+        c.P = &P; c.sh = &sh; c.level = k; c.wg = wg; c.G = G; c.stripe = wg % STRIPES;
+        c.nslot = (k + 1) % NSLOTS; c.wbits = wbits; c.wcf = wcf; c.noq = 0;
+        c.nbm = cur ? P.fbm0 : P.fbm1;
+        c.ncf = P.cf + (size_t)((k + 1) % 3) * CF_WORDS;
+        c.nq = cur ? P.q0 : P.q1; c.nt = cur ? P.t0 : P.t1; c.nts = cur ? P.ts0 : P.ts1;
+        c.fcnt = 0; c.fdeg = 0;
+        // a vertex of T_WG or more edges in the next frontier: the regions
+        // are dealt out by entries, which would leave its list to one
+        // workgroup, so the next launch takes the level, edge-balanced
+        if (pull || !P.small_mode || F1 > SMALL_F || E1 > SMALL_E || sh.s_big) {
+            // level k+1's frontier into its queue lists and counters
+            c.region = nullptr;
+            c.converting = 1;
+            const int4 *rg = P.sreg + ((size_t)((k + 1) & 1) * SMALL_G + wg) * SREG_CAP;
+            const int total = min(sh.rcnt, SREG_CAP);
+            for (int b0 = 0; b0 < total; b0 += CAP) {
+                const int nb = min(CAP, total - b0);
+                for (int i = threadIdx.x; i < nb; i += BLOCK) {
+                    const int4 e = rg[b0 + i];
+                    sh.buf[i] = e.x; sh.sbeg[i] = e.y; sh.slen[i] = e.z;
+                }
+                if (threadIdx.x == 0) sh.cnt = nb;
+                flush(c);   // begins with a barrier
+            }
+            return k + 1;
+        }
+        // level k+1: small and top-down; its winners go to the regions, or
+        // to the queue lists when they are predicted not to be small (then
+        // the launch ends after it)
+        const bool to_queue = grows_out(E1, fdeg);
+        const int64_t m_left = (int64_t)P.m - edges_before - E1;
+        const bool may_pull = (double)P.max_deg * (double)E1 * (double)(P.alpha + 1) > (double)m_left;
+        const int wbits1 = (P.can_pull && P.pol_dir == BFS_DIR_AUTO && may_pull) ? 1 : 0;
+        const int clear_bm = wbits;    // level k's bits are level k+1's frontier bitmap
+        const int cf_clear = sh.prev_wcf;   // level k-1 wrote the coarse map of level k+3
+        const int wcf1 = (wbits1 && (E1 << P.cf_sh) <= 2 * (int64_t)P.n) ? 1 : 0;
+        ++k;
+        const int nc = k & 1;
+        uint32_t *cbm = nc ? P.fbm1 : P.fbm0;
+        // bookkeeping of level k by workgroup 0 (as a full-grid level's)
+        if (wg == 0) {
+            if (threadIdx.x == 0) {
+                const int slot = k % NSLOTS;
+                if (P.level_sizes) P.level_sizes[k] = F1;
+                if (k < P.st_cap) { P.st_dir[k] = (int8_t)DIR_TD; P.st_fdeg[k] = E1; }
+                P.ctl->slot[slot].dir = DIR_TD;
+                P.ctl->slot[slot].wbits = wbits1;
+                P.ctl->slot[slot].wcf = wcf1;
+                P.ctl->slot[slot].input_bm = 0;
+                P.ctl->slot[slot].fsize = F1;
+                P.ctl->slot[slot].noq = 0;
+                P.ctl->slot[(k + 1) % NSLOTS].reached_before = reached_before + F1;
+                P.ctl->slot[(k + 1) % NSLOTS].edges_before = edges_before + E1;
+            }
+            if (threadIdx.x < NCTR) *ctr_at(P, (k + 2) % NSLOTS, threadIdx.x) = 0ull;
+        }
+        if (cf_clear) {
+            // the coarse map of level k+2: level k-2 wrote it, level k-1 read it
+            uint32_t *z = P.cf + (size_t)((k + 2) % 3) * CF_WORDS;
+            for (int i = wg * BLOCK + (int)threadIdx.x; i < P.cf_words; i += G * BLOCK) z[i] = 0u;
+        }
+        __syncthreads();   // every thread has read the state of level k-1
+        if (threadIdx.x == 0) {
+            sh.prev_wcf = wcf;
+            sh.wcf = wcf1;
+            sh.wbits = wbits1;
+            sh.fsize = F1;
+            sh.prev_fdeg = fdeg;
+            sh.fdeg = E1;
+            sh.reached_before = reached_before;
+            sh.edges_before = edges_before;
+            sh.nbig = 0; sh.cnt = 0; sh.spilled = 0;
+            sh.rcnt = 0; sh.rbig = 0; sh.redges = 0ull;
+        }
+        __syncthreads();
+        c.level = k;
+        c.nslot = (k + 1) % NSLOTS;
+        c.wbits = wbits1;
+        c.wcf = wcf1;
+        c.nbm = nc ? P.fbm0 : P.fbm1;
+        c.ncf = P.cf + (size_t)((k + 1) % 3) * CF_WORDS;
+        c.nq = nc ? P.q0 : P.q1; c.nt = nc ? P.t0 : P.t1; c.nts = nc ? P.ts0 : P.ts1;
+        c.region = to_queue ? nullptr : P.sreg + ((size_t)((k + 1) & 1) * SMALL_G + wg) * SREG_CAP;
+        c.converting = 0;
+        // this workgroup's share of level k's entries, from the regions; the
+        // share's edges are dealt out over the whole workgroup (an exclusive
+        // scan of the entries' degrees in LDS, the owner of each edge by
+        // binary search), as in the edge-balanced advance
+        const int4 *rin = P.sreg + (size_t)nc * SMALL_G * SREG_CAP;
+        int32_t *s_off = sh.work;
+        int32_t *s_v = sh.work + (EB_TE + 1);
+        int32_t *s_beg = sh.work + 2 * (EB_TE + 1);
+        const int per = (F1 + G - 1) / G;
+        const int lo = min(F1, wg * per), hi = min(F1, lo + per);
+        for (int i0 = lo; i0 < hi; i0 += BLOCK) {
+            const int nloc = min(BLOCK, hi - i0);
+            const int t = (int)threadIdx.x;
+            int v = 0, beg = 0, len = 0;
+            if (t < nloc) {
+                const int i = i0 + t;
+                int a = 0, b = G;   // the region holding entry i: last a with spre[a] <= i
+                while (b - a > 1) {
+                    const int mid = (a + b) >> 1;
+                    if (sh.spre[mid] <= i) a = mid; else b = mid;
+                }
+                const int4 e = rin[(size_t)a * SREG_CAP + (i - sh.spre[a])];
+                v = e.x; beg = e.y; len = e.z;
+                if (clear_bm) cbm[v >> 5] = 0u;
+            }
+            const int incl = wave_incl_scan_i32(len);
+            const int wsum = readlane_i(incl, WAVE - 1);
+            if (lane == 0) sh.scan_tmp[0][wave_id()] = (uint64_t)(uint32_t)wsum;
+            __syncthreads();
+            int base = 0, Ew = 0;
+            for (int w = 0; w < WAVES; ++w) {
+                const int x = (int)sh.scan_tmp[0][w];
+                if (w < wave_id()) base += x;
+                Ew += x;
+            }
+            if (t < nloc) { s_off[t] = base + incl - len; s_v[t] = v; s_beg[t] = beg; }
+            __syncthreads();
+            // STEP_CLAIMS claims per step, then a flush check: the staging
+            // buffer of a level into the queue lists never overfills
+            constexpr int NQ = STEP_CLAIMS / BLOCK;
+            for (int e0 = 0; e0 < Ew; e0 += NQ * BLOCK) {
+                int tv[NQ], ow[NQ];
+                bool ok[NQ];
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const int e = e0 + q * BLOCK + t;
+                    ok[q] = e < Ew;
+                    int lo2 = 0, hi2 = nloc;   // last j with s_off[j] <= e (skips degree-0 entries)
+                    while (hi2 - lo2 > 1) {
+                        const int mid = (lo2 + hi2) >> 1;
+                        if (s_off[mid] <= e) lo2 = mid; else hi2 = mid;
+                    }
+                    ow[q] = s_v[lo2];
+                    tv[q] = ok[q] ? P.col_idx[s_beg[lo2] + (e - s_off[lo2])] : 0;
+                }
+                claim_batch(c, tv, ok, ow);
+                __syncthreads();
+                maybe_flush(c);
+            }
+            __syncthreads();   // s_off and scan_tmp are reused
+        }
+        if (wg == 0 && threadIdx.x == 0 && launch < RAN_CAP) P.ctl->ran[launch] = 1;
+        if (to_queue) {
+            if (sh.cnt > 0) flush(c);
+            if (sh.spilled) add_tallies(c);
+            return k + 1;
+        }
     }
 }
 
@@ -1372,39 +1662,45 @@ __device__ __forceinline__ void set_next_level(const Params &P, int launch, int 
 // Top-down launch: runs the level it stands at on the whole grid when that
 // level is top-down, or, when the level is small, runs levels on the first
 // SMALL_G workgroups until one is not small (or is bottom-up); a bottom-up
-// level is passed on to the next launch.  One decision point serves every
-// level of the launch.
+// level is passed on to the next launch.
 __global__ __launch_bounds__(BLOCK, 4) void bfs_td_kernel(Params P, int32_t launch) {
     __shared__ TdLds sh;
-    int k = P.ctl->lvl[launch & 1];
-    int G = 0;   // 0 until the first level is decided
-    for (;;) {
-        if (threadIdx.x < WAVE) decide(P, sh, k);
-        __syncthreads();
-        if (sh.mode == 0) return;    // over, or an error was recorded
-        if (sh.mode == 1) {
-            if (blockIdx.x == 0 && threadIdx.x == 0) {
-                P.ctl->L = k;
-                P.ctl->done = 1;
-                if (launch < RAN_CAP) P.ctl->ran[launch] = 1;
-            }
+    const int k = P.ctl->lvl[launch & 1];
+    if (threadIdx.x < WAVE) decide(P, sh, k);
+    __syncthreads();
+    if (sh.mode == 0) return;    // over, or an error was recorded
+    if (sh.mode == 1) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            P.ctl->L = k;
+            P.ctl->done = 1;
+            if (launch < RAN_CAP) P.ctl->ran[launch] = 1;
+        }
+        return;
+    }
+    if (sh.dir == DIR_BU) {      // for the bottom-up launch
+        set_next_level(P, launch, k);
+        return;
+    }
+    if (sh.small) {
+        // the first SMALL_G workgroups; the first level writes the regions
+        // unless its winners are predicted not to be small (no growth is
+        // seen at the source level, which always writes the queue lists)
+        if (blockIdx.x >= SMALL_G) return;
+        const int G = min((int)gridDim.x, SMALL_G);
+        const bool to_queue = k == 0 || grows_out(sh.fdeg, sh.prev_fdeg);
+        run_level<false>(P, sh, k, blockIdx.x, G, !to_queue);
+        if (blockIdx.x == 0 && threadIdx.x == 0 && launch < RAN_CAP) P.ctl->ran[launch] = 1;
+        if (to_queue) {
+            set_next_level(P, launch, k + 1);
             return;
         }
-        if (G == 0) {
-            if (sh.dir == DIR_BU) break;   // for the bottom-up launch
-            if (sh.small && blockIdx.x >= SMALL_G) return;
-            G = sh.small ? min((int)gridDim.x, SMALL_G) : (int)gridDim.x;
-        } else if (!sh.small) {
-            break;                         // not small, or bottom-up
-        }
-        const bool small = sh.small;
-        run_level<false>(P, sh, k, blockIdx.x, G);
-        if (blockIdx.x == 0 && threadIdx.x == 0 && launch < RAN_CAP) P.ctl->ran[launch] = 1;
-        ++k;
-        if (!small) break;
-        small_barrier(P, G);
+        const int kn = run_small(P, sh, k, launch, G);
+        if (kn >= 0) set_next_level(P, launch, kn);
+        return;
     }
-    set_next_level(P, launch, k);
+    run_level<false>(P, sh, k, blockIdx.x, (int)gridDim.x);
+    if (blockIdx.x == 0 && threadIdx.x == 0 && launch < RAN_CAP) P.ctl->ran[launch] = 1;
+    set_next_level(P, launch, k + 1);
 }
 
 // Bottom-up launch: runs the level it stands at when that level is

@@ -90,9 +90,6 @@ struct Ctl {
     int32_t lvl[2];       // level the launch with index i starts at: lvl[i & 1]
     int32_t pad0[2];
     SlotInfo slot[NSLOTS];
-    // arrivals at the barrier of the small-frontier mode (only grows within a
-    // search), alone in its 128 bytes
-    alignas(128) unsigned long long bar_count;
     alignas(128) uint32_t pad1;
 };
 
@@ -110,6 +107,12 @@ constexpr int ERR_BAD_VERTEX = 5;        // a vertex id outside [0, n) met befor
 constexpr int SMALL_G = 32;
 constexpr int SMALL_F = SMALL_G * BLOCK;
 constexpr int SMALL_E = SMALL_F;
+// In that mode each workgroup appends the vertices it wins to a region of
+// its own (entries {v, beg, len}: a workgroup's winners are at most the
+// level's edges, so SMALL_E entries always fit), one set of regions per level
+// parity, and publishes {level, count, edges} in one 64-bit word; the words
+// of all workgroups are the barrier and the next level's work split at once.
+constexpr int SREG_CAP = SMALL_E;
 
 // Inclusive prefix sum over the 64 lanes of a wavefront (all lanes active)
 // with DPP moves, register to register: shifts right by 1, 2, 4 and 8 lanes
@@ -171,6 +174,8 @@ struct Params {
                               // frontier of a level l with l % 3 == j
     int32_t cf_sh, cf_words;  // vertices per coarse bit (log2); words in use per map
     uint32_t barrier_ticks;   // small-mode barrier wait limit (100 MHz ticks)
+    int4 *sreg;               // small-frontier regions: 2 parities x SMALL_G x SREG_CAP entries
+    unsigned long long *sslot;   // small-frontier words: 2 parities x SMALL_G
     int32_t *enq;             // debug builds (FBFS_COUNT_ENQUEUES): n per-vertex counts of
                               // writes into a next frontier, else null
 };
