@@ -20,6 +20,10 @@ HIPCC_FLAGS = [
     # packed fp32 instructions stay off (none of this code needs them)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # atomics on one address with per-lane values (the small-frontier
+    # staging's LDS counter, reached from divergent code) are combined per
+    # wavefront by a DPP scan instead of a loop over the active lanes
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=DPP",
 ]
 
 

@@ -69,7 +69,10 @@ struct bfs_graph {
     int32_t cf_sh = 0, cf_words = 0;
     Seg *q0 = nullptr, *q1 = nullptr, *t0 = nullptr, *t1 = nullptr;
     int32_t *ts0 = nullptr, *ts1 = nullptr;
-    int64_t qcap = 0, tcap = 0, tscap = 0;
+    int64_t tcap = 0, tscap = 0;
+    unsigned long long *qtab = nullptr;   // queue chunk tables
+    int32_t *wscr = nullptr;              // walk scratch (binned, merge), grown on demand
+    int64_t wscr_ints = 0;
     unsigned long long *ctr = nullptr;
     Ctl *ctl = nullptr;
     int8_t *st_dir = nullptr;
@@ -131,7 +134,8 @@ hipError_t dalloc(T **p, size_t count) {
 
 void free_all(bfs_graph *g) {
     void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->cf, g->pnb, g->snb, g->deg8, g->in_row_ptr, g->in_col, g->q0, g->q1, g->t0, g->t1,
-                    g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts, g->enq, g->sreg, g->sslot};
+                    g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts, g->enq, g->sreg, g->sslot,
+                    g->qtab, g->wscr};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     void *vptrs[] = {g->va, g->vb, g->vs, g->vo, g->vt, g->vctl};
@@ -160,7 +164,6 @@ hipError_t ensure_events(bfs_graph *g, size_t count) {
 int alloc_workspace(bfs_graph *g) {
     const int64_t n = g->n, m = g->m;
     const int64_t nwp = (n + 63) / 64;
-    g->qcap = queue_cap(n);
     g->tcap = tile_cap(m);
     g->tscap = tstart_cap(m);
     g->st_cap = (int32_t)stats_cap(n);
@@ -180,8 +183,9 @@ int alloc_workspace(bfs_graph *g) {
         {dalloc(&g->pnb, n), "probe-neighbour index"},
         {dalloc(&g->snb, n), "probe-neighbour index"},
         {dalloc(&g->deg8, n), "byte degrees"},
-        {dalloc(&g->q0, (size_t)STRIPES * g->qcap), "frontier queue"},
-        {dalloc(&g->q1, (size_t)STRIPES * g->qcap), "frontier queue"},
+        {dalloc(&g->q0, (size_t)queue_segs(n)), "frontier queue"},
+        {dalloc(&g->q1, (size_t)queue_segs(n)), "frontier queue"},
+        {dalloc(&g->qtab, (size_t)queue_tab(n)), "queue chunk tables"},
         {dalloc(&g->t0, (size_t)STRIPES * g->tcap), "tile queue"},
         {dalloc(&g->t1, (size_t)STRIPES * g->tcap), "tile queue"},
         {dalloc(&g->ts0, (size_t)NLISTS * STRIPES * g->tscap), "tile start table"},
@@ -507,8 +511,9 @@ constexpr int64_t NA_PNB = NA_CF + na_round(3 * (int64_t)CF_WORDS * 4);
 constexpr int64_t NA_SNB = NA_PNB + na_round(NA_N * 4);
 constexpr int64_t NA_DEG8 = NA_SNB + na_round(NA_N * 4);
 constexpr int64_t NA_Q0 = NA_DEG8 + na_round(NA_N);
-constexpr int64_t NA_Q1 = NA_Q0 + na_round(STRIPES * queue_cap(NA_N) * (int64_t)sizeof(Seg));
-constexpr int64_t NA_T0 = NA_Q1 + na_round(STRIPES * queue_cap(NA_N) * (int64_t)sizeof(Seg));
+constexpr int64_t NA_Q1 = NA_Q0 + na_round(queue_segs(NA_N) * (int64_t)sizeof(Seg));
+constexpr int64_t NA_QTAB = NA_Q1 + na_round(queue_segs(NA_N) * (int64_t)sizeof(Seg));
+constexpr int64_t NA_T0 = NA_QTAB + na_round(queue_tab(NA_N) * 8);
 constexpr int64_t NA_T1 = NA_T0 + na_round(STRIPES * tile_cap(NA_M) * (int64_t)sizeof(Seg));
 constexpr int64_t NA_TS0 = NA_T1 + na_round(STRIPES * tile_cap(NA_M) * (int64_t)sizeof(Seg));
 constexpr int64_t NA_TS1 = NA_TS0 + na_round((int64_t)NLISTS * STRIPES * tstart_cap(NA_M) * 4);
@@ -752,7 +757,9 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.t1 = g->t1;
     P.ts0 = g->ts0;
     P.ts1 = g->ts1;
-    P.qcap = g->qcap;
+    P.qk_sh = qk_shift(g->n);
+    P.qpool = (int32_t)queue_pool(g->n);
+    P.qtab = g->qtab;
     P.tcap = g->tcap;
     P.tscap = g->tscap;
     P.ctr = g->ctr;
@@ -1011,7 +1018,9 @@ int32_t bfs_run_noalloc(int32_t n, const int32_t *row_ptr, const int32_t *col_id
     P.t1 = reinterpret_cast<Seg *>(base + NA_T1);
     P.ts0 = reinterpret_cast<int32_t *>(base + NA_TS0);
     P.ts1 = reinterpret_cast<int32_t *>(base + NA_TS1);
-    P.qcap = queue_cap(n);
+    P.qk_sh = qk_shift(n);
+    P.qpool = (int32_t)queue_pool(n);
+    P.qtab = reinterpret_cast<unsigned long long *>(base + NA_QTAB);
     P.tcap = tile_cap(m);
     P.tscap = tstart_cap(m);
     P.ctr = reinterpret_cast<unsigned long long *>(base + NA_CTR);
@@ -1097,14 +1106,25 @@ int32_t bfs_walk_level(bfs_graph *g, const int32_t *vertices, int32_t count, int
         set_error("vertices and out must be device pointers");
         return BFS_EINVAL;
     }
-    // the merge mapping's scratch lives in the first frontier queue
-    // (STRIPES * qcap segments of 16 bytes)
-    const int64_t scratch_ints = (int64_t)STRIPES * g->qcap * (int64_t)(sizeof(Seg) / sizeof(int32_t));
-    if ((int64_t)count > 8 * (int64_t)g->n || walk_scratch_ints(count) > scratch_ints) {
+    if ((int64_t)count > 8 * (int64_t)g->n) {
         set_error("count %d is above the walk's limit of 8n = %lld", count, 8LL * g->n);
         return BFS_EINVAL;
     }
     HIP_TRY(hipSetDevice(g->device), BFS_EHIP);
+    // the binned and merge mappings' scratch: a buffer of the handle, grown on demand
+    if ((mapping == BFS_WALK_BINNED || mapping == BFS_WALK_MERGE) && walk_scratch_ints(count) > g->wscr_ints) {
+        HIP_TRY(hipDeviceSynchronize(), BFS_EHIP);   // a walk still running may use the old one
+        if (g->wscr) (void)hipFree(g->wscr);
+        g->wscr = nullptr;
+        g->wscr_ints = 0;
+        if (dalloc(&g->wscr, (size_t)walk_scratch_ints(count)) != hipSuccess) {
+            (void)hipGetLastError();
+            g->wscr = nullptr;
+            set_error("allocating the walk scratch for count %d failed", count);
+            return BFS_ENOMEM;
+        }
+        g->wscr_ints = walk_scratch_ints(count);
+    }
     Params P;
     std::memset(&P, 0, sizeof(P));
     P.row_ptr = g->row_ptr;
@@ -1119,7 +1139,7 @@ int32_t bfs_walk_level(bfs_graph *g, const int32_t *vertices, int32_t count, int
         HIP_TRY(ensure_events(g, 2), BFS_EHIP);
         HIP_TRY(hipEventRecord(g->events[0], stream), BFS_EHIP);
     }
-    HIP_TRY(launch_walk(P, vertices, count, mapping, repeats, out, reinterpret_cast<int32_t *>(g->q0), bad,
+    HIP_TRY(launch_walk(P, vertices, count, mapping, repeats, out, g->wscr, bad,
                         g->grid, stream),
             BFS_EHIP);
     if (timing) HIP_TRY(hipEventRecord(g->events[1], stream), BFS_EHIP);

@@ -110,17 +110,21 @@ struct TdLds : LevelCommon {
     int32_t tstart[CAP], toff[CAP];   // flush: piece start / edge offset of each staged slot
     int32_t ntiles;
     unsigned long long list_base[NLISTS];
+    int32_t qsplit[2], qd[2][2];      // flush: per list, the first index of its second chunk and
+                                      // storage - index for either chunk (QD_NONE: missing)
+    int32_t qbad;                     // a queue chunk of the level's input is missing (error recorded)
     int32_t cnt;                      // staged count (may exceed CAP: overflow spilled)
     int32_t spilled;                  // some lane appended directly this level (its tallies are per thread)
     int32_t nbig;
     int32_t fl_cnt[WAVES], fl_more[WAVES];   // from-bitmap lists: count, words left
     int32_t vfilter;                  // claims first load the visited words
     // small-frontier mode
-    int32_t rcnt;                     // this workgroup's winners in its region
+    unsigned long long rpack;         // this workgroup's winners in its region (bits 40-63) and
+                                      // their edges (bits 0-39, each winner's at most SMALL_E + 1)
     int32_t rbig;                     // ... one of them has at least T_WG edges
-    unsigned long long redges;        // ... and their edges
     int32_t spre[SMALL_G + 1];        // exclusive prefix of the workgroups' winners
     int32_t s_total, s_err, s_big;    // winners of all workgroups; an error was recorded; a big one
+    int32_t s_own;                    // each workgroup expands its own winners (kept in buf, sbeg, slen)
     unsigned long long s_edges;       // their edges (saturating per workgroup at 2^24 - 1)
 };
 
@@ -165,29 +169,110 @@ using BuCtx = CtxT<BuLds>;
 
 // --------------------------------------------------------- emission --------
 
-// Where segment `idx` of list `l`, stripe `s` lives.
-__device__ __forceinline__ Seg *seg_slot(const Params &P, Seg *q, Seg *t, int l, int s, int64_t idx) {
-    if (l == L_SMALL) return q + (size_t)s * P.qcap + idx;
-    if (l == L_MID) return q + (size_t)s * P.qcap + (P.qcap - 1 - idx);
-    return t + (size_t)s * P.tcap + idx;
-}
-
 __device__ __forceinline__ void set_err(const Params &P, int code, int info) {
     atomicCAS(&P.ctl->err, 0, code);
     P.ctl->err_info = info;
 }
 
+constexpr int32_t QD_NONE = (int32_t)0x80000000;
+
+// Table entry of chunk j >= 1 of region (list l < L_TILE, stripe s) in the
+// chunk table of level slot `slot`.
+__device__ __forceinline__ unsigned long long *qtab_at(const Params &P, int slot, int l, int s, int64_t j) {
+    return P.qtab + (((size_t)slot * 2 + l) * STRIPES + s) * P.qpool + (size_t)(j - 1);
+}
+
+// Where segment `idx` of list l, stripe s of the queue of level k (tables of
+// slot k % NSLOTS, tag k + 1) lives; null (the error recorded) when a chunk
+// table entry is missing or out of range.
+__device__ __forceinline__ Seg *seg_slot(const Params &P, Seg *q, Seg *t, int l, int s, int64_t idx, int k) {
+    if (l == L_TILE) return t + (size_t)s * P.tcap + idx;
+    const int64_t j = idx >> P.qk_sh;
+    const int64_t off = idx & ((1LL << P.qk_sh) - 1);
+    if (__builtin_expect(j == 0, 1)) return q + ((size_t)(l * STRIPES + s) << P.qk_sh) + off;
+    if (j > P.qpool) { set_err(P, ERR_QUEUE_OVERFLOW, l); return nullptr; }
+    const unsigned long long e = *qtab_at(P, k % NSLOTS, l, s, j);
+    const uint32_t id = (uint32_t)e;
+    if ((uint32_t)(e >> 32) != (uint32_t)(k + 1) || id >= (uint32_t)P.qpool) {
+        set_err(P, ERR_QUEUE_OVERFLOW, l);
+        return nullptr;
+    }
+    return q + ((size_t)(2 * STRIPES + id) << P.qk_sh) + off;
+}
+
+// Start (a segment offset into the queue being written) of chunk j of this
+// workgroup's region of list l < L_TILE in the queue of level c.level + 1,
+// for a reservation of segments from index b on: chunk 0 is fixed; a chunk
+// whose first segment lies in the reservation is taken from the pool here
+// and recorded (tagged c.level + 2) in the level's table; any other chunk was
+// taken by the earlier reservation holding its first segment, whose entry
+// is awaited (bounded).  -1, the error recorded, when the pool or the wait
+// runs out.
+// The pool chunk behind table entry e (tag: the writing level's): taken from
+// the pool counter and recorded (take), or awaited until recorded (bounded
+// by `ticks`).  -1 when the pool is used up or the wait runs out, the error
+// recorded in ctl.  Lanes of one wavefront may need the same chunk, one
+// taking it and others awaiting it, so every lane that takes a chunk has
+// recorded it before any lane starts to wait (an if / else here could run
+// the waiting side first, with the taking lane masked off).  Kept out of
+// line: the expansion loops inline the queue writes in many places, and this
+// rare path would weigh on all of them.
+__device__ __noinline__ int32_t queue_chunk_slow(unsigned long long *e, unsigned long long *pool, uint32_t tag,
+                                                 int32_t qpool, bool take, uint32_t ticks, Ctl *ctl) {
+    uint32_t id = 0xffffffffu;
+    int code = ERR_QUEUE_OVERFLOW;
+    if (take) {
+        id = (uint32_t)atomicAdd(pool, 1ull);
+        if (id < (uint32_t)qpool)
+            __hip_atomic_store(e, ((unsigned long long)tag << 32) | id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // keeps the records ahead of the waits
+    if (!take) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (;;) {
+            const unsigned long long x = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((uint32_t)(x >> 32) == tag) {
+                id = (uint32_t)x;
+                break;
+            }
+            if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) {
+                code = ERR_BARRIER_TIMEOUT;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    if (id >= (uint32_t)qpool) {
+        atomicCAS(&ctl->err, 0, code);
+        return -1;
+    }
+    return (int32_t)id;
+}
+
+__device__ __forceinline__ int64_t queue_chunk(const Ctx &c, int l, int64_t j, int64_t b) {
+    const Params &P = *c.P;
+    if (__builtin_expect(j == 0, 1)) return (int64_t)(l * STRIPES + c.stripe) << P.qk_sh;
+    if (j > P.qpool) { set_err(P, ERR_QUEUE_OVERFLOW, l); return -1; }
+    const int32_t id = queue_chunk_slow(qtab_at(P, c.nslot, l, c.stripe, j), ctr_at(P, c.nslot, QPOOL_CTR),
+                                        (uint32_t)(c.level + 2), P.qpool, (j << P.qk_sh) >= b,
+                                        P.barrier_ticks, P.ctl);
+    return id < 0 ? -1 : (int64_t)(2 * STRIPES + id) << P.qk_sh;
+}
+
 // Writes one segment (vertex v, adjacency piece [pb, pb+pl), edge offset po)
-// at index si of list l and records the edge-balanced tiles whose first edge
+// at index si of list l (stored at dst; null: its chunk is missing, the error
+// already recorded) and records the edge-balanced tiles whose first edge
 // falls inside it.
 __device__ __forceinline__ void write_piece(const Ctx &c, int l, int64_t si, int v, int pb, int pl,
-                                            int64_t po) {
+                                            int64_t po, Seg *dst) {
     const Params &P = *c.P;
-    const int64_t cap = (l == L_TILE) ? P.tcap : P.qcap;
+    // a region of the queue holds at most n segments (one per vertex)
+    const int64_t cap = (l == L_TILE) ? P.tcap : (int64_t)P.n;
     if (si >= cap) { set_err(P, l == L_TILE ? ERR_TILE_OVERFLOW : ERR_QUEUE_OVERFLOW, (int)l); return; }
+    if (!dst) return;
     Seg sg;
     sg.v = v; sg.beg = pb; sg.len = pl; sg.off = (int32_t)po;
-    *seg_slot(P, c.nq, c.nt, l, c.stripe, si) = sg;
+    *dst = sg;
     int32_t *ts = c.nts + (size_t)(l * STRIPES + c.stripe) * P.tscap;
     int64_t t0 = (po + EB_TE - 1) / EB_TE;
     const int64_t t1 = (po + pl - 1) / EB_TE;
@@ -202,11 +287,22 @@ __device__ __forceinline__ void write_piece(const Ctx &c, int l, int64_t si, int
 // offset `eoff` of list l.
 __device__ __forceinline__ void write_vertex_segments(const Ctx &c, int l, int v, int beg, int len,
                                                       int64_t idx, int64_t eoff) {
-    const int nseg = (l == L_TILE) ? (len + TILE - 1) / TILE : 1;
+    const Params &P = *c.P;
+    if (l != L_TILE) {
+        // one segment: its chunk, for a reservation of this index alone
+        Seg *dst = nullptr;
+        if (idx < (int64_t)P.n) {
+            const int64_t cb = queue_chunk(c, l, idx >> P.qk_sh, idx);
+            if (cb >= 0) dst = c.nq + cb + (idx & ((1LL << P.qk_sh) - 1));
+        }
+        write_piece(c, l, idx, v, beg, len, eoff, dst);
+        return;
+    }
+    const int nseg = (len + TILE - 1) / TILE;
     for (int j = 0; j < nseg; ++j) {
-        const int pb = (l == L_TILE) ? beg + j * TILE : beg;
-        const int pl = (l == L_TILE) ? min(TILE, len - j * TILE) : len;
-        write_piece(c, l, idx + j, v, pb, pl, eoff + (int64_t)j * TILE);
+        const int64_t si = idx + j;
+        write_piece(c, l, si, v, beg + j * TILE, min(TILE, len - j * TILE), eoff + (int64_t)j * TILE,
+                    si < P.tcap ? c.nt + (size_t)c.stripe * P.tcap + si : nullptr);
     }
 }
 
@@ -255,22 +351,32 @@ __device__ __forceinline__ void stage(Ctx &c, bool win, int v, int beg, int len)
 }
 
 // Small-frontier mode: a winner (adjacency [beg, beg+len)) goes straight to
-// this workgroup's region (wave-aggregated LDS atomic for its place); the
-// region's count and edges are kept in LDS.
+// this workgroup's region; one LDS atomic per winner on the packed (count,
+// edges) word gives its place and the edge offset of its list (per lane:
+// callers may be in divergent control flow).  The first OWN_CAP winners are
+// also kept in LDS (vertex, adjacency start, edge offset), in the half of
+// buf / sbeg / toff that belongs to their level's parity, for the next
+// level's own-mode expansion.
+constexpr int OWN_CAP = CAP / 2;
+constexpr unsigned long long RP_EDGES = (1ull << 40) - 1;
+
 __device__ __forceinline__ void stage_region(Ctx &c, bool win, int v, int beg, int len) {
-    const uint64_t m = __ballot(win);
-    if (m == 0) return;
-    const int leader = __ffsll((unsigned long long)m) - 1;
-    int base = 0;
-    if (lane_id() == leader) base = atomicAdd(&c.sh->rcnt, __popcll(m));
-    base = readlane_i(base, leader);
     if (win) {
-        const int slot = base + mbcnt64(m);
-        atomicAdd(&c.sh->redges, (unsigned long long)(uint32_t)len);
+        // each degree counts at most SMALL_E + 1: the sum only needs to be
+        // exact up to SMALL_E (the published edges saturate above it)
+        const unsigned long long old =
+            atomicAdd(&c.sh->rpack, (1ull << 40) | (unsigned long long)min(len, SMALL_E + 1));
+        const int slot = (int)(old >> 40);
         if (len >= T_WG) c.sh->rbig = 1;
         if (slot < SREG_CAP) {
             c.region[slot] = make_int4(v, beg, len, 0);
             FBFS_ENQ(*c.P, v);
+            if (slot < OWN_CAP) {
+                const int o = ((c.level + 1) & 1) * OWN_CAP + slot;
+                c.sh->buf[o] = v;
+                c.sh->sbeg[o] = beg;
+                c.sh->toff[o] = (int32_t)(old & RP_EDGES);   // exact while the level's edges are few
+            }
         } else {
             set_err(*c.P, ERR_QUEUE_OVERFLOW, slot);
         }
@@ -317,11 +423,23 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
         old[q] = tryq[q] ? atomicOr(P.visited + (v[q] >> 5), 1u << (v[q] & 31)) : ~0u;
     bool win[CB];
     int beg[CB], len[CB];
+    if (c.region) {
+        // small levels wait on each round trip: the adjacency bounds of every
+        // candidate are read beside its claim, not after it
 #pragma unroll
-    for (int q = 0; q < CB; ++q) {
-        win[q] = tryq[q] && !((old[q] >> (v[q] & 31)) & 1u);
-        beg[q] = win[q] ? P.row_ptr[v[q]] : 0;
-        len[q] = win[q] ? P.row_ptr[v[q] + 1] : 0;
+        for (int q = 0; q < CB; ++q) {
+            beg[q] = tryq[q] ? P.row_ptr[v[q]] : 0;
+            len[q] = tryq[q] ? P.row_ptr[v[q] + 1] : 0;
+        }
+#pragma unroll
+        for (int q = 0; q < CB; ++q) win[q] = tryq[q] && !((old[q] >> (v[q] & 31)) & 1u);
+    } else {
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            win[q] = tryq[q] && !((old[q] >> (v[q] & 31)) & 1u);
+            beg[q] = win[q] ? P.row_ptr[v[q]] : 0;
+            len[q] = win[q] ? P.row_ptr[v[q] + 1] : 0;
+        }
     }
 #pragma unroll
     for (int q = 0; q < CB; ++q) {
@@ -409,8 +527,24 @@ __device__ __forceinline__ void flush(Ctx &c) {
         const int l = threadIdx.x;
         uint64_t all = 0;
         for (int w = 0; w < WAVES; ++w) all += sh.scan_tmp[l][w];
-        if (all != 0)
-            sh.list_base[l] = atomicAdd(ctr_at(P, c.nslot, l * STRIPES + c.stripe), (unsigned long long)all);
+        if (all != 0) {
+            const unsigned long long base =
+                atomicAdd(ctr_at(P, c.nslot, l * STRIPES + c.stripe), (unsigned long long)all);
+            sh.list_base[l] = base;
+            if (l != L_TILE) {
+                // the chunks holding this flush's segments [b, b + cnt) of list l
+                // (cnt <= min(CAP, n) <= 2^qk_sh: at most two), as the
+                // difference storage - index for the indexes below and from
+                // the second chunk's first one
+                const int64_t b = (int64_t)(base >> 32), e = b + (int64_t)(all >> 32) - 1;
+                const int64_t j0 = b >> P.qk_sh, j1 = e >> P.qk_sh;
+                const int64_t c0 = (b < (int64_t)P.n) ? queue_chunk(c, l, j0, b) : -1;
+                const int64_t c1 = (j1 == j0) ? c0 : ((e < (int64_t)P.n) ? queue_chunk(c, l, j1, b) : -1);
+                sh.qsplit[l] = (int32_t)((j0 + 1) << P.qk_sh);
+                sh.qd[l][0] = (c0 >= 0) ? (int32_t)(c0 - (j0 << P.qk_sh)) : QD_NONE;
+                sh.qd[l][1] = (c1 >= 0) ? (int32_t)(c1 - (j1 << P.qk_sh)) : QD_NONE;
+            }
+        }
         if (l == L_TILE) sh.ntiles = (int32_t)(all >> 32);
     } else if (threadIdx.x == NLISTS) {
         // the flushed vertices and their edges go straight into the level
@@ -425,6 +559,13 @@ __device__ __forceinline__ void flush(Ctx &c) {
     // vertices: record where their pieces start, then the whole workgroup
     // writes the pieces (a hub can have hundreds)
     const uint64_t b0 = sh.list_base[L_SMALL], b1 = sh.list_base[L_MID];
+    // where segment si of the small (mid) list of this flush is stored
+    const int32_t sp0 = sh.qsplit[L_SMALL], d00 = sh.qd[L_SMALL][0], d01 = sh.qd[L_SMALL][1];
+    const int32_t sp1 = sh.qsplit[L_MID], d10 = sh.qd[L_MID][0], d11 = sh.qd[L_MID][1];
+    auto qdst = [&](int64_t si, int32_t sp, int32_t da, int32_t db) -> Seg * {
+        const int32_t d = (si < sp) ? da : db;
+        return d != QD_NONE ? c.nq + (si + d) : nullptr;
+    };
     for (int i = i0; i < min(i0 + EPT, cnt); ++i) {
         const int v = sh.buf[i];
         const int beg = sh.sbeg[i];
@@ -434,12 +575,14 @@ __device__ __forceinline__ void flush(Ctx &c) {
         sh.tstart[i] = (int32_t)(ex2 >> 32);
         sh.toff[i] = (int32_t)(ex2 & 0xffffffffull);
         if (l == L_SMALL) {
-            write_piece(c, l, (int64_t)((b0 >> 32) + (ex0 >> 32)), v, beg, len,
-                        (int64_t)((b0 & 0xffffffffull) + (ex0 & 0xffffffffull)));
+            const int64_t si = (int64_t)((b0 >> 32) + (ex0 >> 32));
+            write_piece(c, l, si, v, beg, len, (int64_t)((b0 & 0xffffffffull) + (ex0 & 0xffffffffull)),
+                        qdst(si, sp0, d00, d01));
             ex0 += (1ull << 32) | (uint32_t)len;
         } else if (l == L_MID) {
-            write_piece(c, l, (int64_t)((b1 >> 32) + (ex1 >> 32)), v, beg, len,
-                        (int64_t)((b1 & 0xffffffffull) + (ex1 & 0xffffffffull)));
+            const int64_t si = (int64_t)((b1 >> 32) + (ex1 >> 32));
+            write_piece(c, l, si, v, beg, len, (int64_t)((b1 & 0xffffffffull) + (ex1 & 0xffffffffull)),
+                        qdst(si, sp1, d10, d11));
             ex1 += (1ull << 32) | (uint32_t)len;
         } else if (l == L_TILE) {
             ex2 += ((uint64_t)((len + TILE - 1) / TILE) << 32) | (uint32_t)len;
@@ -462,8 +605,10 @@ __device__ __forceinline__ void flush(Ctx &c) {
             const int beg = sh.sbeg[lo];
             const int len = sh.slen[lo];
             const int pcs = gt - sh.tstart[lo];
-            write_piece(c, L_TILE, tbase + gt, v, beg + pcs * TILE, min(TILE, len - pcs * TILE),
-                        ebase + sh.toff[lo] + (int64_t)pcs * TILE);
+            const int64_t si = tbase + gt;
+            write_piece(c, L_TILE, si, v, beg + pcs * TILE, min(TILE, len - pcs * TILE),
+                        ebase + sh.toff[lo] + (int64_t)pcs * TILE,
+                        si < P.tcap ? c.nt + (size_t)c.stripe * P.tcap + si : nullptr);
         }
     }
     __syncthreads();
@@ -544,10 +689,13 @@ __device__ __forceinline__ void td_binned(Ctx &c, const Seg *cq, const Seg *ct, 
         }
         int v = 0, beg = 0, len = 0;
         if (si >= 0 && si < nseg) {
-            const Seg sg = *seg_slot(P, const_cast<Seg *>(cq), const_cast<Seg *>(ct), l, s, si);
-            v = sg.v; beg = sg.beg; len = sg.len;
-            has = true;
-            if (c.sh->clear_bm) cbm[v >> 5] = 0u;
+            const Seg *sp = seg_slot(P, const_cast<Seg *>(cq), const_cast<Seg *>(ct), l, s, si, c.level);
+            if (sp) {
+                const Seg sg = *sp;
+                v = sg.v; beg = sg.beg; len = sg.len;
+                has = true;
+                if (c.sh->clear_bm) cbm[v >> 5] = 0u;
+            }
         }
         expand_segments(c, has, v, beg, len);
         maybe_flush(c);
@@ -592,11 +740,17 @@ __device__ __forceinline__ void td_edge_balanced(Ctx &c, const Seg *cq, const Se
             ns = max(1, min(ns, EB_TE + 1));
         }
         for (int j = threadIdx.x; j < ns; j += BLOCK) {
-            const Seg sg = *seg_slot(P, const_cast<Seg *>(cq), const_cast<Seg *>(ct), l, s, i0 + j);
-            s_off[j] = sg.off; s_v[j] = sg.v; s_beg[j] = sg.beg;
-            if (sh.clear_bm) cbm[sg.v >> 5] = 0u;
+            const Seg *sp = seg_slot(P, const_cast<Seg *>(cq), const_cast<Seg *>(ct), l, s, i0 + j, c.level);
+            if (sp) {
+                const Seg sg = *sp;
+                s_off[j] = sg.off; s_v[j] = sg.v; s_beg[j] = sg.beg;
+                if (sh.clear_bm) cbm[sg.v >> 5] = 0u;
+            } else {
+                sh.qbad = 1;   // a missing chunk (error recorded): the tile is skipped
+            }
         }
         __syncthreads();
+        if (sh.qbad) continue;   // uniform: every thread reads it after the barrier
         static_assert(EB_TE % BLOCK == 0 && EB_TE <= STEP_CLAIMS, "one step per tile");
         constexpr int NB = EB_TE / BLOCK;
         {
@@ -1097,6 +1251,8 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
     uint64_t *b0 = reinterpret_cast<uint64_t *>(P.fbm0);
     uint64_t *b1 = reinterpret_cast<uint64_t *>(P.fbm1);
     for (int i = tid; i < 3 * CF_WORDS; i += nth) P.cf[i] = 0u;
+    // queue chunk tables: entries of an earlier search must not match a tag
+    for (int64_t i = tid; i < (int64_t)NSLOTS * 2 * STRIPES * P.qpool; i += nth) P.qtab[i] = 0ull;
     for (int i = tid; i < 2 * SMALL_G; i += nth) P.sslot[i] = 0ull;
 #ifdef FBFS_COUNT_ENQUEUES
     if (P.enq)
@@ -1167,7 +1323,7 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
             edges_before = P.ctl->slot[slot].edges_before;
         }
     }
-    const bool is_vc = lane >= VC_BASE && lane < NCTR;
+    const bool is_vc = lane >= VC_BASE && lane < VC_BASE + STRIPES;
     // |F| <= n and deg(F) <= m, both below 2^31: 32-bit sums, read from the
     // last lane of the scans
     const int64_t fsize = (uint32_t)readlane_i(
@@ -1302,9 +1458,9 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
             sh.cnt = 0;
             sh.spilled = 0;
             sh.nbig = 0;
-            sh.rcnt = 0;
+            sh.rpack = 0ull;
             sh.rbig = 0;
-            sh.redges = 0ull;
+            sh.qbad = 0;
             // a visited-word load before each claim pays on levels with many
             // edges (it spares the atomics of targets already reached)
             sh.vfilter = sh.fdeg >= VFILTER_EDGES;
@@ -1417,8 +1573,8 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
         unsigned long long *words = P.sslot + (size_t)((k + 1) & 1) * SMALL_G;
         __syncthreads();
         if (threadIdx.x == 0) {
-            const unsigned long long cnt = (unsigned long long)min(sh.rcnt, SREG_CAP);
-            const unsigned long long ed = sh.redges < SW_EDGE_MAX ? sh.redges : SW_EDGE_MAX;
+            const unsigned long long cnt = min(sh.rpack >> 40, (unsigned long long)SREG_CAP);
+            const unsigned long long ed = min(sh.rpack & RP_EDGES, SW_EDGE_MAX);
             const unsigned long long big = sh.rbig ? 1ull : 0ull;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             __hip_atomic_store(words + wg, ((unsigned long long)want << 40) | (cnt << 25) | (big << 24) | ed,
@@ -1428,10 +1584,13 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
         if (threadIdx.x < WAVE) {
             const bool mine = lane < G;
             unsigned long long word = 0ull;
+            int errv = 0;
             bool late = false;
             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
             for (;;) {
+                // lane G reads the error word beside the others' words (G <= SMALL_G < WAVE)
                 if (mine) word = __hip_atomic_load(words + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else if (lane == G) errv = __hip_atomic_load(&P.ctl->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const bool ok = !mine || (uint32_t)(word >> 40) == want;
                 if (__ballot(!ok) == 0ull) break;
                 __builtin_amdgcn_s_sleep(1);
@@ -1444,6 +1603,9 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
             const int cnt = mine ? (int)((word >> 25) & 0x7fffull) : 0;
             const bool anybig = __ballot(mine && ((word >> 24) & 1ull)) != 0ull;
             const uint32_t ed = mine ? (uint32_t)(word & SW_EDGE_MAX) : 0u;   // G * 2^24 < 2^32
+            // every workgroup's winners fit one claim step: each expands its own
+            const bool own = __ballot(mine && (cnt > OWN_CAP || ed > (uint32_t)STEP_CLAIMS)) == 0ull;
+            const bool err_seen = readlane_i(errv, G) != 0;
             const int incl = wave_incl_scan_i32(cnt);
             const uint32_t eincl = wave_incl_scan_u32(ed);
             // cross-lane reads in uniform control flow: inside a branch on
@@ -1457,7 +1619,8 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
                 sh.s_total = total;
                 sh.s_edges = etotal;
                 sh.s_big = anybig;
-                sh.s_err = late || __hip_atomic_load(&P.ctl->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+                sh.s_own = own;
+                sh.s_err = late || err_seen;
             }
         }
         __syncthreads();
@@ -1495,7 +1658,7 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
             c.region = nullptr;
             c.converting = 1;
             const int4 *rg = P.sreg + ((size_t)((k + 1) & 1) * SMALL_G + wg) * SREG_CAP;
-            const int total = min(sh.rcnt, SREG_CAP);
+            const int total = (int)min(sh.rpack >> 40, (unsigned long long)SREG_CAP);
             for (int b0 = 0; b0 < total; b0 += CAP) {
                 const int nb = min(CAP, total - b0);
                 for (int i = threadIdx.x; i < nb; i += BLOCK) {
@@ -1542,6 +1705,13 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
             uint32_t *z = P.cf + (size_t)((k + 2) % 3) * CF_WORDS;
             for (int i = wg * BLOCK + (int)threadIdx.x; i < P.cf_words; i += G * BLOCK) z[i] = 0u;
         }
+        // own mode: this workgroup's winners of level k, in LDS (at most
+        // OWN_CAP of them, with at most STEP_CLAIMS edges); not when this
+        // level's winners go to the queue lists, whose LDS staging would
+        // overwrite them
+        const bool own = sh.s_own && !to_queue;
+        const int own_cnt = (int)min(sh.rpack >> 40, (unsigned long long)OWN_CAP);
+        const int own_edges = (int)min(sh.rpack & RP_EDGES, (unsigned long long)STEP_CLAIMS);
         __syncthreads();   // every thread has read the state of level k-1
         if (threadIdx.x == 0) {
             sh.prev_wcf = wcf;
@@ -1553,7 +1723,7 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
             sh.reached_before = reached_before;
             sh.edges_before = edges_before;
             sh.nbig = 0; sh.cnt = 0; sh.spilled = 0;
-            sh.rcnt = 0; sh.rbig = 0; sh.redges = 0ull;
+            sh.rpack = 0ull; sh.rbig = 0;
         }
         __syncthreads();
         c.level = k;
@@ -1565,46 +1735,13 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
         c.nq = nc ? P.q0 : P.q1; c.nt = nc ? P.t0 : P.t1; c.nts = nc ? P.ts0 : P.ts1;
         c.region = to_queue ? nullptr : P.sreg + ((size_t)((k + 1) & 1) * SMALL_G + wg) * SREG_CAP;
         c.converting = 0;
-        // this workgroup's share of level k's entries, from the regions; the
-        // share's edges are dealt out over the whole workgroup (an exclusive
-        // scan of the entries' degrees in LDS, the owner of each edge by
-        // binary search), as in the edge-balanced advance
-        const int4 *rin = P.sreg + (size_t)nc * SMALL_G * SREG_CAP;
-        int32_t *s_off = sh.work;
-        int32_t *s_v = sh.work + (EB_TE + 1);
-        int32_t *s_beg = sh.work + 2 * (EB_TE + 1);
-        const int per = (F1 + G - 1) / G;
-        const int lo = min(F1, wg * per), hi = min(F1, lo + per);
-        for (int i0 = lo; i0 < hi; i0 += BLOCK) {
-            const int nloc = min(BLOCK, hi - i0);
-            const int t = (int)threadIdx.x;
-            int v = 0, beg = 0, len = 0;
-            if (t < nloc) {
-                const int i = i0 + t;
-                int a = 0, b = G;   // the region holding entry i: last a with spre[a] <= i
-                while (b - a > 1) {
-                    const int mid = (a + b) >> 1;
-                    if (sh.spre[mid] <= i) a = mid; else b = mid;
-                }
-                const int4 e = rin[(size_t)a * SREG_CAP + (i - sh.spre[a])];
-                v = e.x; beg = e.y; len = e.z;
-                if (clear_bm) cbm[v >> 5] = 0u;
-            }
-            const int incl = wave_incl_scan_i32(len);
-            const int wsum = readlane_i(incl, WAVE - 1);
-            if (lane == 0) sh.scan_tmp[0][wave_id()] = (uint64_t)(uint32_t)wsum;
-            __syncthreads();
-            int base = 0, Ew = 0;
-            for (int w = 0; w < WAVES; ++w) {
-                const int x = (int)sh.scan_tmp[0][w];
-                if (w < wave_id()) base += x;
-                Ew += x;
-            }
-            if (t < nloc) { s_off[t] = base + incl - len; s_v[t] = v; s_beg[t] = beg; }
-            __syncthreads();
-            // STEP_CLAIMS claims per step, then a flush check: the staging
-            // buffer of a level into the queue lists never overfills
+        // STEP_CLAIMS claims per step over the edges [0, Ew) of entries
+        // [0, nloc) (vertex ev[j], adjacency start eb[j], edge offset eo[j],
+        // ascending), each step followed by a flush check: the staging buffer
+        // of a level into the queue lists never overfills
+        auto claim_steps = [&](const int32_t *eo, const int32_t *ev, const int32_t *eb, int nloc, int Ew) {
             constexpr int NQ = STEP_CLAIMS / BLOCK;
+            const int t = (int)threadIdx.x;
             for (int e0 = 0; e0 < Ew; e0 += NQ * BLOCK) {
                 int tv[NQ], ow[NQ];
                 bool ok[NQ];
@@ -1612,19 +1749,69 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
                 for (int q = 0; q < NQ; ++q) {
                     const int e = e0 + q * BLOCK + t;
                     ok[q] = e < Ew;
-                    int lo2 = 0, hi2 = nloc;   // last j with s_off[j] <= e (skips degree-0 entries)
+                    int lo2 = 0, hi2 = nloc;   // last j with eo[j] <= e (skips degree-0 entries)
                     while (hi2 - lo2 > 1) {
                         const int mid = (lo2 + hi2) >> 1;
-                        if (s_off[mid] <= e) lo2 = mid; else hi2 = mid;
+                        if (eo[mid] <= e) lo2 = mid; else hi2 = mid;
                     }
-                    ow[q] = s_v[lo2];
-                    tv[q] = ok[q] ? P.col_idx[s_beg[lo2] + (e - s_off[lo2])] : 0;
+                    ow[q] = ev[lo2];
+                    tv[q] = ok[q] ? P.col_idx[eb[lo2] + (e - eo[lo2])] : 0;
                 }
                 claim_batch(c, tv, ok, ow);
                 __syncthreads();
                 maybe_flush(c);
             }
-            __syncthreads();   // s_off and scan_tmp are reused
+        };
+        if (own) {
+            // own mode: this workgroup's winners of level k, as staged in LDS
+            // with their edge offsets (one step: at most STEP_CLAIMS edges);
+            // level k+1's winners go to the other half
+            const int h = (k & 1) * OWN_CAP;
+            if (clear_bm)
+                for (int i = threadIdx.x; i < own_cnt; i += BLOCK) cbm[sh.buf[h + i] >> 5] = 0u;
+            claim_steps(sh.toff + h, sh.buf + h, sh.sbeg + h, own_cnt, own_edges);
+        } else {
+            // an equal share of all workgroups' entries of level k, from the
+            // regions; the share's edges are dealt out over the whole
+            // workgroup (an exclusive scan of the entries' degrees in LDS,
+            // the owner of each edge by binary search), as in the
+            // edge-balanced advance
+            const int4 *rin = P.sreg + (size_t)nc * SMALL_G * SREG_CAP;
+            int32_t *s_off = sh.work;
+            int32_t *s_v = sh.work + (EB_TE + 1);
+            int32_t *s_beg = sh.work + 2 * (EB_TE + 1);
+            const int per = (F1 + G - 1) / G;
+            const int lo = min(F1, wg * per), hi = min(F1, lo + per);
+            for (int i0 = lo; i0 < hi; i0 += BLOCK) {
+                const int nloc = min(BLOCK, hi - i0);
+                const int t = (int)threadIdx.x;
+                int v = 0, beg = 0, len = 0;
+                if (t < nloc) {
+                    const int i = i0 + t;
+                    int a = 0, b = G;   // the region holding entry i: last a with spre[a] <= i
+                    while (b - a > 1) {
+                        const int mid = (a + b) >> 1;
+                        if (sh.spre[mid] <= i) a = mid; else b = mid;
+                    }
+                    const int4 e = rin[(size_t)a * SREG_CAP + (i - sh.spre[a])];
+                    v = e.x; beg = e.y; len = e.z;
+                    if (clear_bm) cbm[v >> 5] = 0u;
+                }
+                const int incl = wave_incl_scan_i32(len);
+                const int wsum = readlane_i(incl, WAVE - 1);
+                if (lane == 0) sh.scan_tmp[0][wave_id()] = (uint64_t)(uint32_t)wsum;
+                __syncthreads();
+                int base = 0, Ew = 0;
+                for (int w = 0; w < WAVES; ++w) {
+                    const int x = (int)sh.scan_tmp[0][w];
+                    if (w < wave_id()) base += x;
+                    Ew += x;
+                }
+                if (t < nloc) { s_off[t] = base + incl - len; s_v[t] = v; s_beg[t] = beg; }
+                __syncthreads();
+                claim_steps(s_off, s_v, s_beg, nloc, Ew);
+                __syncthreads();   // s_off and scan_tmp are reused
+            }
         }
         if (wg == 0 && threadIdx.x == 0 && launch < RAN_CAP) P.ctl->ran[launch] = 1;
         if (to_queue) {

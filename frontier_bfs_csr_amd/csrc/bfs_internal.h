@@ -48,9 +48,10 @@ constexpr int NLISTS = 3;
 
 // counters of one level slot: NLISTS*STRIPES list counters, then STRIPES
 // vertex counters; each 64-bit counter sits alone in 256 bytes.
-constexpr int NCTR = 32;
+constexpr int NCTR = 33;
 constexpr int CTR_STRIDE = 32;           // in uint64 units
 constexpr int VC_BASE = NLISTS * STRIPES;
+constexpr int QPOOL_CTR = VC_BASE + STRIPES;   // pool chunks handed out for the level's queue
 constexpr int NSLOTS = 4;                // ring of level slots
 
 // direction codes stored per level
@@ -150,11 +151,14 @@ struct Params {
     const int32_t *snb;       // n entries: in-neighbour of second highest out-degree, -1 if none
     const uint8_t *deg8;      // n entries: in-degree, 255 standing for 255 or more
     uint32_t *fbm0, *fbm1;    // frontier bitmaps, 2*nwp words each
-    Seg *q0, *q1;             // STRIPES regions of qcap segments (small from the front,
-                              // mid from the back)
+    Seg *q0, *q1;             // queue storage, queue_segs(n) segments each (chunks of 2^qk_sh)
     Seg *t0, *t1;             // STRIPES regions of tcap tiles
     int32_t *ts0, *ts1;       // edge-balanced tile starts: NLISTS*STRIPES regions of tscap
-    int64_t qcap, tcap, tscap;
+    int64_t tcap, tscap;
+    int32_t qk_sh;            // log2 of the segments per queue chunk
+    int32_t qpool;            // pool chunks per queue
+    unsigned long long *qtab; // chunk tables: NSLOTS x 2 lists x STRIPES x qpool entries,
+                              // entry j-1 = (tag << 32) | pool chunk of chunk j >= 1
     unsigned long long *ctr;  // NSLOTS * NCTR counters, CTR_STRIDE apart
     Ctl *ctl;
     int8_t *st_dir;           // per-level stats, st_cap entries
@@ -196,7 +200,23 @@ struct Params {
 // Workspace capacities (segments or entries per stripe region) for a graph of
 // n vertices and m CSR entries; the handle's workspace and the fixed scratch
 // of the allocation-free entry point both follow them.
-constexpr int64_t queue_cap(int64_t n) { return n; }
+//
+// Queue storage.  A level puts at most n vertices into its queue, but how
+// they split over the 2*STRIPES (small or mid list, stripe) regions is not
+// known ahead, so a region's segments live in chunks of 2^qk_sh: chunk 0 of
+// every region is fixed, and chunk j >= 1 comes from a pool on demand (the
+// reservation holding the chunk's first segment takes it and records it in
+// the level's table).  A region of c segments uses ceil(c / 2^qk_sh) - 1 pool
+// chunks, so the level's regions together use at most n >> qk_sh of them.
+constexpr int QK_MAX_SH = 14;             // chunks of at most 16384 segments
+constexpr int qk_shift(int64_t n) {
+    int s = 0;
+    while ((1LL << s) < n && s < QK_MAX_SH) ++s;
+    return s;
+}
+constexpr int64_t queue_pool(int64_t n) { return (n + (1LL << qk_shift(n)) - 1) >> qk_shift(n); }
+constexpr int64_t queue_segs(int64_t n) { return (2 * STRIPES + queue_pool(n)) << qk_shift(n); }
+constexpr int64_t queue_tab(int64_t n) { return (int64_t)NSLOTS * 2 * STRIPES * queue_pool(n); }
 constexpr int64_t tile_cap(int64_t m) { return m / TILE + m / T_WG + 1; }
 constexpr int64_t tstart_cap(int64_t m) { return m / EB_TE + 2; }
 constexpr int64_t stats_cap(int64_t n) { return (n + 1) < (1 << 22) ? (n + 1) : (1 << 22); }

@@ -88,7 +88,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
  * bad index in bfs_last_error), then searched by the same kernels, the
  * direction switching included when the graph is symmetric with sorted rows
  * (any other graph is searched push-only: dist, L and level sizes do not
- * change).  The workspace (about 20 MB) is one fixed device array per GPU,
+ * change).  The workspace (about 30 MB) is one fixed device array per GPU,
  * created with the library's code object and held until the process ends;
  * nothing is allocated or freed on any call.  Every call on one GPU shares
  * that array and leaves its contents behind, so calls that overlap on one GPU

@@ -33,24 +33,32 @@ def test_workspace_out_of_memory():
     hr, hc = to_dev(h)
     with fb.BfsGraph(hr, hc) as bg:
         run_hip(bg, h.n, 0)
-    g = gg.path_graph(1 << 24)   # a workspace of well over 1 GB
+    g = gg.star_graph(1 << 24)   # a workspace of about 0.8 GB, two levels
     rp, ci = to_dev(g)
     torch.cuda.synchronize()
-    free, _ = torch.cuda.mem_get_info()
-    filler = torch.empty(max(0, free - (1 << 30)), dtype=torch.uint8, device="cuda")
+    # hold device memory in 64 MB pieces until the next piece does not fit,
+    # then give one back: under 128 MB are left
+    pieces = []
     try:
-        print(f"[gpu] out-of-memory create: {filler.numel() >> 20} MB held, n={g.n}", flush=True)
+        while True:
+            try:
+                pieces.append(torch.empty(64 << 20, dtype=torch.uint8, device="cuda"))
+            except torch.OutOfMemoryError:
+                break
+        del pieces[-1:]
+        torch.cuda.synchronize()
+        print(f"[gpu] out-of-memory create: {len(pieces) * 64} MB held, n={g.n}", flush=True)
         with pytest.raises(fb.BfsError) as ei:
             fb.bfs_graph_create(g.n, rp, ci)
         assert ei.value.code == fb.BFS_ENOMEM, str(ei.value)
         assert "failed" in str(ei.value)
     finally:
-        del filler
+        pieces.clear()
         torch.cuda.empty_cache()
     # the partial workspace was released: the same graph now fits
     with fb.BfsGraph(rp, ci) as bg:
         L, dist, _, _ = run_hip(bg, g.n, 0, False, False)
-        assert L == g.n and (dist == np.arange(g.n)).all()
+        assert L == 2 and dist[0] == 0 and (dist[1:] == 1).all()
 
 
 def test_null_dist_on_valid_handle():
