@@ -119,9 +119,10 @@ struct TdLds : LevelCommon {
     int32_t fl_cnt[WAVES], fl_more[WAVES];   // from-bitmap lists: count, words left
     int32_t vfilter;                  // claims first load the visited words
     // small-frontier mode
-    unsigned long long rpack;         // this workgroup's winners in its region (bits 40-63) and
-                                      // their edges (bits 0-39, each winner's at most SMALL_E + 1)
-    int32_t rbig;                     // ... one of them has at least T_WG edges
+    unsigned long long rpack[2];      // this workgroup's winners of a level (by its parity) in
+                                      // its region (bits 40-63) and their edges (bits 0-39, each
+                                      // winner's at most SMALL_E + 1)
+    int32_t rbig[2];                  // ... one of them has at least T_WG edges
     int32_t spre[SMALL_G + 1];        // exclusive prefix of the workgroups' winners
     int32_t s_total, s_err, s_big;    // winners of all workgroups; an error was recorded; a big one
     int32_t s_own;                    // each workgroup expands its own winners (kept in buf, sbeg, slen)
@@ -364,15 +365,16 @@ __device__ __forceinline__ void stage_region(Ctx &c, bool win, int v, int beg, i
     if (win) {
         // each degree counts at most SMALL_E + 1: the sum only needs to be
         // exact up to SMALL_E (the published edges saturate above it)
+        const int par = (c.level + 1) & 1;
         const unsigned long long old =
-            atomicAdd(&c.sh->rpack, (1ull << 40) | (unsigned long long)min(len, SMALL_E + 1));
+            atomicAdd(&c.sh->rpack[par], (1ull << 40) | (unsigned long long)min(len, SMALL_E + 1));
         const int slot = (int)(old >> 40);
-        if (len >= T_WG) c.sh->rbig = 1;
+        if (len >= T_WG) c.sh->rbig[par] = 1;
         if (slot < SREG_CAP) {
             c.region[slot] = make_int4(v, beg, len, 0);
             FBFS_ENQ(*c.P, v);
             if (slot < OWN_CAP) {
-                const int o = ((c.level + 1) & 1) * OWN_CAP + slot;
+                const int o = par * OWN_CAP + slot;
                 c.sh->buf[o] = v;
                 c.sh->sbeg[o] = beg;
                 c.sh->toff[o] = (int32_t)(old & RP_EDGES);   // exact while the level's edges are few
@@ -1458,8 +1460,8 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
             sh.cnt = 0;
             sh.spilled = 0;
             sh.nbig = 0;
-            sh.rpack = 0ull;
-            sh.rbig = 0;
+            sh.rpack[(k + 1) & 1] = 0ull;
+            sh.rbig[(k + 1) & 1] = 0;
             sh.qbad = 0;
             // a visited-word load before each claim pays on levels with many
             // edges (it spares the atomics of targets already reached)
@@ -1563,19 +1565,26 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
     const int wg = blockIdx.x;
     const int lane = lane_id();
     // level k has run (run_level, its winners in the regions); the level
-    // state as decide() left it, kept in sh from level to level
+    // state as decide() left it, carried in registers from level to level
+    // (uniform in the workgroup)
+    int fsize = sh.fsize, wbits = sh.wbits, wcf = sh.wcf, prev_wcf = sh.prev_wcf;
+    int64_t fdeg = sh.fdeg, reached_before0 = sh.reached_before, edges_before0 = sh.edges_before;
     for (;;) {
         const int cur = k & 1;
-        const int fsize = sh.fsize, wbits = sh.wbits, wcf = sh.wcf;
-        const int64_t fdeg = sh.fdeg;
         // publish this workgroup's winners of level k+1
         const uint32_t want = (uint32_t)(k + 1) & SW_SEQ_MASK;
         unsigned long long *words = P.sslot + (size_t)((k + 1) & 1) * SMALL_G;
         __syncthreads();
         if (threadIdx.x == 0) {
-            const unsigned long long cnt = min(sh.rpack >> 40, (unsigned long long)SREG_CAP);
-            const unsigned long long ed = min(sh.rpack & RP_EDGES, SW_EDGE_MAX);
-            const unsigned long long big = sh.rbig ? 1ull : 0ull;
+            const unsigned long long rp = sh.rpack[(k + 1) & 1];
+            const unsigned long long cnt = min(rp >> 40, (unsigned long long)SREG_CAP);
+            const unsigned long long ed = min(rp & RP_EDGES, SW_EDGE_MAX);
+            const unsigned long long big = sh.rbig[(k + 1) & 1] ? 1ull : 0ull;
+            // the counts of level k's winners are read (published, and
+            // taken as own-mode entries) by now: cleared for level k+2's,
+            // which the next expansion stages after the barrier below
+            sh.rpack[k & 1] = 0ull;
+            sh.rbig[k & 1] = 0;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             __hip_atomic_store(words + wg, ((unsigned long long)want << 40) | (cnt << 25) | (big << 24) | ed,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1603,8 +1612,11 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
             const int cnt = mine ? (int)((word >> 25) & 0x7fffull) : 0;
             const bool anybig = __ballot(mine && ((word >> 24) & 1ull)) != 0ull;
             const uint32_t ed = mine ? (uint32_t)(word & SW_EDGE_MAX) : 0u;   // G * 2^24 < 2^32
-            // every workgroup's winners fit one claim step: each expands its own
-            const bool own = __ballot(mine && (cnt > OWN_CAP || ed > (uint32_t)STEP_CLAIMS)) == 0ull;
+            // every workgroup's winners have at most one edge per thread:
+            // each expands its own (a workgroup with two claims per thread
+            // took over 2 us longer on the grid, more than the region read
+            // an equal split costs)
+            const bool own = __ballot(mine && (cnt > OWN_CAP || ed > (uint32_t)BLOCK)) == 0ull;
             const bool err_seen = readlane_i(errv, G) != 0;
             const int incl = wave_incl_scan_i32(cnt);
             const uint32_t eincl = wave_incl_scan_u32(ed);
@@ -1627,8 +1639,8 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
         if (sh.s_err) return -1;
         const int F1 = sh.s_total;
         const int64_t E1 = (int64_t)sh.s_edges;
-        const int64_t reached_before = sh.reached_before + fsize;
-        const int64_t edges_before = sh.edges_before + fdeg;
+        const int64_t reached_before = reached_before0 + fsize;
+        const int64_t edges_before = edges_before0 + fdeg;
         if (F1 == 0) {
             if (wg == 0 && threadIdx.x == 0) {
                 P.ctl->L = k + 1;
@@ -1658,7 +1670,7 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
             c.region = nullptr;
             c.converting = 1;
             const int4 *rg = P.sreg + ((size_t)((k + 1) & 1) * SMALL_G + wg) * SREG_CAP;
-            const int total = (int)min(sh.rpack >> 40, (unsigned long long)SREG_CAP);
+            const int total = (int)min(sh.rpack[(k + 1) & 1] >> 40, (unsigned long long)SREG_CAP);
             for (int b0 = 0; b0 < total; b0 += CAP) {
                 const int nb = min(CAP, total - b0);
                 for (int i = threadIdx.x; i < nb; i += BLOCK) {
@@ -1678,7 +1690,7 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
         const bool may_pull = (double)P.max_deg * (double)E1 * (double)(P.alpha + 1) > (double)m_left;
         const int wbits1 = (P.can_pull && P.pol_dir == BFS_DIR_AUTO && may_pull) ? 1 : 0;
         const int clear_bm = wbits;    // level k's bits are level k+1's frontier bitmap
-        const int cf_clear = sh.prev_wcf;   // level k-1 wrote the coarse map of level k+3
+        const int cf_clear = prev_wcf;   // level k-1 wrote the coarse map of level k+3
         const int wcf1 = (wbits1 && (E1 << P.cf_sh) <= 2 * (int64_t)P.n) ? 1 : 0;
         ++k;
         const int nc = k & 1;
@@ -1706,26 +1718,22 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
             for (int i = wg * BLOCK + (int)threadIdx.x; i < P.cf_words; i += G * BLOCK) z[i] = 0u;
         }
         // own mode: this workgroup's winners of level k, in LDS (at most
-        // OWN_CAP of them, with at most STEP_CLAIMS edges); not when this
+        // OWN_CAP of them, with at most BLOCK edges); not when this
         // level's winners go to the queue lists, whose LDS staging would
         // overwrite them
         const bool own = sh.s_own && !to_queue;
-        const int own_cnt = (int)min(sh.rpack >> 40, (unsigned long long)OWN_CAP);
-        const int own_edges = (int)min(sh.rpack & RP_EDGES, (unsigned long long)STEP_CLAIMS);
-        __syncthreads();   // every thread has read the state of level k-1
-        if (threadIdx.x == 0) {
-            sh.prev_wcf = wcf;
-            sh.wcf = wcf1;
-            sh.wbits = wbits1;
-            sh.fsize = F1;
-            sh.prev_fdeg = fdeg;
-            sh.fdeg = E1;
-            sh.reached_before = reached_before;
-            sh.edges_before = edges_before;
-            sh.nbig = 0; sh.cnt = 0; sh.spilled = 0;
-            sh.rpack = 0ull; sh.rbig = 0;
-        }
-        __syncthreads();
+        const int own_cnt = (int)min(sh.rpack[k & 1] >> 40, (unsigned long long)OWN_CAP);
+        const int own_edges = (int)min(sh.rpack[k & 1] & RP_EDGES, (unsigned long long)STEP_CLAIMS);
+        prev_wcf = wcf;
+        wcf = wcf1;
+        wbits = wbits1;
+        fsize = F1;
+        fdeg = E1;
+        reached_before0 = reached_before;
+        edges_before0 = edges_before;
+        // (the staging count, spill flag and hub list stay 0 in region mode:
+        // only a level that writes the queue lists stages into them, and the
+        // launch ends after it)
         c.level = k;
         c.nslot = (k + 1) % NSLOTS;
         c.wbits = wbits1;
@@ -1758,13 +1766,15 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
                     tv[q] = ok[q] ? P.col_idx[eb[lo2] + (e - eo[lo2])] : 0;
                 }
                 claim_batch(c, tv, ok, ow);
-                __syncthreads();
-                maybe_flush(c);
+                if (!c.region) {   // uniform; region staging never fills the staging buffer
+                    __syncthreads();
+                    maybe_flush(c);
+                }
             }
         };
         if (own) {
             // own mode: this workgroup's winners of level k, as staged in LDS
-            // with their edge offsets (one step: at most STEP_CLAIMS edges);
+            // with their edge offsets (one step: at most BLOCK edges);
             // level k+1's winners go to the other half
             const int h = (k & 1) * OWN_CAP;
             if (clear_bm)
