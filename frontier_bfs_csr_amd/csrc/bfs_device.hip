@@ -538,10 +538,19 @@ __device__ __forceinline__ void flush(Ctx &c) {
                 // (cnt <= min(CAP, n) <= 2^qk_sh: at most two), as the
                 // difference storage - index for the indexes below and from
                 // the second chunk's first one
+                // Chunks whose first segment lies in the range are taken
+                // before any wait for a chunk an earlier reservation holds:
+                // the lists' threads share a wavefront, so a wait ahead of a
+                // take would hold that take back, and two workgroups could
+                // each wait for the other's
                 const int64_t b = (int64_t)(base >> 32), e = b + (int64_t)(all >> 32) - 1;
                 const int64_t j0 = b >> P.qk_sh, j1 = e >> P.qk_sh;
-                const int64_t c0 = (b < (int64_t)P.n) ? queue_chunk(c, l, j0, b) : -1;
-                const int64_t c1 = (j1 == j0) ? c0 : ((e < (int64_t)P.n) ? queue_chunk(c, l, j1, b) : -1);
+                const bool own0 = j0 == 0 || (j0 << P.qk_sh) >= b;
+                int64_t c0 = -1, c1 = -1;
+                if (b < (int64_t)P.n && own0) c0 = queue_chunk(c, l, j0, b);
+                if (j1 != j0 && e < (int64_t)P.n) c1 = queue_chunk(c, l, j1, b);
+                if (b < (int64_t)P.n && !own0) c0 = queue_chunk(c, l, j0, b);
+                if (j1 == j0) c1 = c0;
                 sh.qsplit[l] = (int32_t)((j0 + 1) << P.qk_sh);
                 sh.qd[l][0] = (c0 >= 0) ? (int32_t)(c0 - (j0 << P.qk_sh)) : QD_NONE;
                 sh.qd[l][1] = (c1 >= 0) ? (int32_t)(c1 - (j1 << P.qk_sh)) : QD_NONE;
