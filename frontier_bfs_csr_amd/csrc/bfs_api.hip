@@ -71,6 +71,7 @@ struct bfs_graph {
     int32_t *ts0 = nullptr, *ts1 = nullptr;
     int64_t tcap = 0, tscap = 0;
     unsigned long long *qtab = nullptr;   // queue chunk tables
+    int4 *adj4 = nullptr;                 // inline short adjacencies
     int32_t *wscr = nullptr;              // walk scratch (binned, merge), grown on demand
     int64_t wscr_ints = 0;
     unsigned long long *ctr = nullptr;
@@ -135,7 +136,7 @@ hipError_t dalloc(T **p, size_t count) {
 void free_all(bfs_graph *g) {
     void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->cf, g->pnb, g->snb, g->deg8, g->in_row_ptr, g->in_col, g->q0, g->q1, g->t0, g->t1,
                     g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts, g->enq, g->sreg, g->sslot,
-                    g->qtab, g->wscr};
+                    g->qtab, g->wscr, g->adj4};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     void *vptrs[] = {g->va, g->vb, g->vs, g->vo, g->vt, g->vctl};
@@ -183,6 +184,7 @@ int alloc_workspace(bfs_graph *g) {
         {dalloc(&g->pnb, n), "probe-neighbour index"},
         {dalloc(&g->snb, n), "probe-neighbour index"},
         {dalloc(&g->deg8, n), "byte degrees"},
+        {dalloc(&g->adj4, n), "inline adjacencies"},
         {dalloc(&g->q0, (size_t)queue_segs(n)), "frontier queue"},
         {dalloc(&g->q1, (size_t)queue_segs(n)), "frontier queue"},
         {dalloc(&g->qtab, (size_t)queue_tab(n)), "queue chunk tables"},
@@ -510,7 +512,8 @@ constexpr int64_t NA_CF = NA_FBM1 + na_round(2 * NA_NWP * 4);
 constexpr int64_t NA_PNB = NA_CF + na_round(3 * (int64_t)CF_WORDS * 4);
 constexpr int64_t NA_SNB = NA_PNB + na_round(NA_N * 4);
 constexpr int64_t NA_DEG8 = NA_SNB + na_round(NA_N * 4);
-constexpr int64_t NA_Q0 = NA_DEG8 + na_round(NA_N);
+constexpr int64_t NA_ADJ4 = NA_DEG8 + na_round(NA_N);
+constexpr int64_t NA_Q0 = NA_ADJ4 + na_round(NA_N * 16);
 constexpr int64_t NA_Q1 = NA_Q0 + na_round(queue_segs(NA_N) * (int64_t)sizeof(Seg));
 constexpr int64_t NA_QTAB = NA_Q1 + na_round(queue_segs(NA_N) * (int64_t)sizeof(Seg));
 constexpr int64_t NA_T0 = NA_QTAB + na_round(queue_tab(NA_N) * 8);
@@ -613,6 +616,7 @@ bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *co
         if (e == hipSuccess) e = launch_build_vis_init(g->can_pull ? irp : row_ptr, n, g->can_pull, g->vis_init, 0);
         if (e == hipSuccess && g->can_pull) e = launch_build_probe_nb(row_ptr, irp, icol, n, g->pnb, g->snb, 0);
         if (e == hipSuccess && g->can_pull) e = launch_build_deg8(irp, n, g->deg8, 0);
+        if (e == hipSuccess) e = launch_build_adj4(row_ptr, col_idx, n, g->adj4, 0);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) {
             set_error("building the visited template, in-edges and probe-neighbour index failed: %s",
@@ -743,6 +747,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.pnb = g->pnb;
     P.snb = g->snb;
     P.deg8 = g->deg8;
+    P.adj4 = g->adj4;
     P.in_row_ptr = g->symmetric ? g->row_ptr : g->in_row_ptr;
     P.in_col_idx = g->symmetric ? g->col_idx : g->in_col;
     P.can_pull = g->can_pull;
@@ -1003,6 +1008,7 @@ int32_t bfs_run_noalloc(int32_t n, const int32_t *row_ptr, const int32_t *col_id
     P.pnb = reinterpret_cast<int32_t *>(base + NA_PNB);
     P.snb = reinterpret_cast<int32_t *>(base + NA_SNB);
     P.deg8 = reinterpret_cast<uint8_t *>(base + NA_DEG8);
+    P.adj4 = reinterpret_cast<int4 *>(base + NA_ADJ4);
     P.in_row_ptr = symmetric ? row_ptr : nullptr;
     P.in_col_idx = symmetric ? col_idx : nullptr;
     P.can_pull = symmetric;
@@ -1048,6 +1054,7 @@ int32_t bfs_run_noalloc(int32_t n, const int32_t *row_ptr, const int32_t *col_id
                                       reinterpret_cast<int32_t *>(base + NA_SNB), stream), BFS_EHIP);
         HIP_TRY(launch_build_deg8(row_ptr, n, reinterpret_cast<uint8_t *>(base + NA_DEG8), stream), BFS_EHIP);
     }
+    HIP_TRY(launch_build_adj4(row_ptr, col_idx, n, reinterpret_cast<int4 *>(base + NA_ADJ4), stream), BFS_EHIP);
     int32_t hc[4] = {0, 0, 0, 0};   // done, L, err, err_info
     if (n <= ONE_N) {
         HIP_TRY(launch_one(P, stream), BFS_EHIP);

@@ -44,6 +44,8 @@
 // and written out with one global atomic per workgroup flush per list (PMPP
 // ch.15 notes, section 15.6, privatised queue -- without its overflow drop:
 // a full LDS buffer spills to a direct global append instead).
+#include <type_traits>
+
 #include "bfs_internal.h"
 #include "frontier_bfs.h"
 
@@ -123,6 +125,9 @@ struct TdLds : LevelCommon {
                                       // its region (bits 40-63) and their edges (bits 0-39, each
                                       // winner's at most SMALL_E + 1)
     int32_t rbig[2];                  // ... one of them has at least T_WG edges
+    int32_t inl[2];                   // ... all of them have their targets in itgt / iown
+    int32_t itgt[2][BLOCK];           // own mode: a level's winners' targets by edge offset (those
+    int32_t iown[2][BLOCK];           //   of degree <= ADJ_INLINE within BLOCK edges) and owners
     int32_t spre[SMALL_G + 1];        // exclusive prefix of the workgroups' winners
     int32_t s_total, s_err, s_big;    // winners of all workgroups; an error was recorded; a big one
     int32_t s_own;                    // each workgroup expands its own winners (kept in buf, sbeg, slen)
@@ -359,9 +364,10 @@ __device__ __forceinline__ void stage(Ctx &c, bool win, int v, int beg, int len)
 // buf / sbeg / toff that belongs to their level's parity, for the next
 // level's own-mode expansion.
 constexpr int OWN_CAP = CAP / 2;
+constexpr int ADJ_NONE = (int)0x80000000;   // an inline adjacency record that was not read
 constexpr unsigned long long RP_EDGES = (1ull << 40) - 1;
 
-__device__ __forceinline__ void stage_region(Ctx &c, bool win, int v, int beg, int len) {
+__device__ __forceinline__ void stage_region(Ctx &c, bool win, int v, int beg, int len, int4 a4) {
     if (win) {
         // each degree counts at most SMALL_E + 1: the sum only needs to be
         // exact up to SMALL_E (the published edges saturate above it)
@@ -378,6 +384,18 @@ __device__ __forceinline__ void stage_region(Ctx &c, bool win, int v, int beg, i
                 c.sh->buf[o] = v;
                 c.sh->sbeg[o] = beg;
                 c.sh->toff[o] = (int32_t)(old & RP_EDGES);   // exact while the level's edges are few
+            }
+            // the targets themselves, by edge offset, when the adjacency came
+            // inline and fits the first BLOCK edges
+            const unsigned long long off = old & RP_EDGES;
+            if (a4.x != ADJ_NONE && len <= ADJ_INLINE && off + (unsigned long long)len <= (unsigned long long)BLOCK) {
+                int32_t *tg = c.sh->itgt[par] + off, *ow = c.sh->iown[par] + off;
+                if (len > 0) { tg[0] = a4.x; ow[0] = v; }
+                if (len > 1) { tg[1] = a4.y; ow[1] = v; }
+                if (len > 2) { tg[2] = a4.z; ow[2] = v; }
+                if (len > 3) { tg[3] = a4.w; ow[3] = v; }
+            } else if (len > 0) {
+                c.sh->inl[par] = 0;
             }
         } else {
             set_err(*c.P, ERR_QUEUE_OVERFLOW, slot);
@@ -425,13 +443,19 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
         old[q] = tryq[q] ? atomicOr(P.visited + (v[q] >> 5), 1u << (v[q] & 31)) : ~0u;
     bool win[CB];
     int beg[CB], len[CB];
+    int4 a4[CB];
     if (c.region) {
         // small levels wait on each round trip: the adjacency bounds of every
-        // candidate are read beside its claim, not after it
+        // candidate, and the adjacency itself when it is short, are read
+        // beside its claim, not after it
 #pragma unroll
         for (int q = 0; q < CB; ++q) {
             beg[q] = tryq[q] ? P.row_ptr[v[q]] : 0;
             len[q] = tryq[q] ? P.row_ptr[v[q] + 1] : 0;
+            // (with one claim per lane, as own mode has: more would cost
+            // registers the wider loops spill; ADJ_NONE marks a record not read)
+            if constexpr (CB == 1) a4[q] = tryq[q] ? P.adj4[v[q]] : make_int4(-1, -1, -1, -1);
+            else a4[q] = make_int4(ADJ_NONE, 0, 0, 0);
         }
 #pragma unroll
         for (int q = 0; q < CB; ++q) win[q] = tryq[q] && !((old[q] >> (v[q] & 31)) & 1u);
@@ -466,7 +490,7 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
     }
     if (c.region) {
 #pragma unroll
-        for (int q = 0; q < CB; ++q) stage_region(c, win[q], v[q], beg[q], len[q] - beg[q]);
+        for (int q = 0; q < CB; ++q) stage_region(c, win[q], v[q], beg[q], len[q] - beg[q], a4[q]);
         return;
     }
 #pragma unroll
@@ -1471,6 +1495,7 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
             sh.nbig = 0;
             sh.rpack[(k + 1) & 1] = 0ull;
             sh.rbig[(k + 1) & 1] = 0;
+            sh.inl[(k + 1) & 1] = 1;
             sh.qbad = 0;
             // a visited-word load before each claim pays on levels with many
             // edges (it spares the atomics of targets already reached)
@@ -1594,6 +1619,7 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
             // which the next expansion stages after the barrier below
             sh.rpack[k & 1] = 0ull;
             sh.rbig[k & 1] = 0;
+            sh.inl[k & 1] = 1;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             __hip_atomic_store(words + wg, ((unsigned long long)want << 40) | (cnt << 25) | (big << 24) | ed,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1756,8 +1782,10 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
         // [0, nloc) (vertex ev[j], adjacency start eb[j], edge offset eo[j],
         // ascending), each step followed by a flush check: the staging buffer
         // of a level into the queue lists never overfills
-        auto claim_steps = [&](const int32_t *eo, const int32_t *ev, const int32_t *eb, int nloc, int Ew) {
-            constexpr int NQ = STEP_CLAIMS / BLOCK;
+        // (NQ claims per thread per step: own mode has at most BLOCK edges and
+        // takes one, whose claims also read the winners' inline adjacency)
+        auto claim_steps = [&](auto nq, const int32_t *eo, const int32_t *ev, const int32_t *eb, int nloc, int Ew) {
+            constexpr int NQ = decltype(nq)::value;
             const int t = (int)threadIdx.x;
             for (int e0 = 0; e0 < Ew; e0 += NQ * BLOCK) {
                 int tv[NQ], ow[NQ];
@@ -1788,7 +1816,16 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
             const int h = (k & 1) * OWN_CAP;
             if (clear_bm)
                 for (int i = threadIdx.x; i < own_cnt; i += BLOCK) cbm[sh.buf[h + i] >> 5] = 0u;
-            claim_steps(sh.toff + h, sh.buf + h, sh.sbeg + h, own_cnt, own_edges);
+            if (sh.inl[k & 1]) {
+                // every target is in LDS: edge t of thread t, no adjacency read
+                const int e = (int)threadIdx.x;
+                const bool ok[1] = {e < own_edges};   // own_edges <= BLOCK
+                const int tv[1] = {ok[0] ? sh.itgt[k & 1][e] : 0};
+                const int ow[1] = {ok[0] ? sh.iown[k & 1][e] : 0};
+                claim_batch(c, tv, ok, ow);
+            } else {
+                claim_steps(std::integral_constant<int, 1>{}, sh.toff + h, sh.buf + h, sh.sbeg + h, own_cnt, own_edges);
+            }
         } else {
             // an equal share of all workgroups' entries of level k, from the
             // regions; the share's edges are dealt out over the whole
@@ -1828,7 +1865,7 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
                 }
                 if (t < nloc) { s_off[t] = base + incl - len; s_v[t] = v; s_beg[t] = beg; }
                 __syncthreads();
-                claim_steps(s_off, s_v, s_beg, nloc, Ew);
+                claim_steps(std::integral_constant<int, STEP_CLAIMS / BLOCK>{}, s_off, s_v, s_beg, nloc, Ew);
                 __syncthreads();   // s_off and scan_tmp are reused
             }
         }
@@ -2179,6 +2216,27 @@ __global__ __launch_bounds__(256) void deg8_kernel(const int32_t *in_row_ptr, in
         const int d = in_row_ptr[v + 1] - in_row_ptr[v];
         deg8[v] = (uint8_t)(d < 255 ? d : 255);
     }
+}
+
+__global__ __launch_bounds__(256) void adj4_kernel(const int32_t *row_ptr, const int32_t *col_idx, int32_t n,
+                                                   int4 *adj4) {
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n; v += nth) {
+        const int b = row_ptr[v], d = row_ptr[v + 1] - b;
+        int4 a = make_int4(-1, -1, -1, -1);
+        if (d <= ADJ_INLINE) {
+            if (d > 0) a.x = col_idx[b];
+            if (d > 1) a.y = col_idx[b + 1];
+            if (d > 2) a.z = col_idx[b + 2];
+            if (d > 3) a.w = col_idx[b + 3];
+        }
+        adj4[v] = a;
+    }
+}
+
+hipError_t launch_build_adj4(const int32_t *row_ptr, const int32_t *col_idx, int32_t n, int4 *adj4, hipStream_t s) {
+    hipLaunchKernelGGL(adj4_kernel, dim3(grid_for(n, 256 * 4)), dim3(256), 0, s, row_ptr, col_idx, n, adj4);
+    return hipGetLastError();
 }
 
 hipError_t launch_build_deg8(const int32_t *in_row_ptr, int32_t n, uint8_t *deg8, hipStream_t s) {

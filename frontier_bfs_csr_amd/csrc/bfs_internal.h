@@ -150,6 +150,9 @@ struct Params {
     const int32_t *pnb;       // n entries: in-neighbour of highest out-degree, -1 if none
     const int32_t *snb;       // n entries: in-neighbour of second highest out-degree, -1 if none
     const uint8_t *deg8;      // n entries: in-degree, 255 standing for 255 or more
+    const int4 *adj4;         // n entries: the out-neighbours of a vertex of out-degree at most
+                              // ADJ_INLINE (-1 padded), so a small level reads them beside the
+                              // claim instead of after it; unused for larger degrees
     uint32_t *fbm0, *fbm1;    // frontier bitmaps, 2*nwp words each
     Seg *q0, *q1;             // queue storage, queue_segs(n) segments each (chunks of 2^qk_sh)
     Seg *t0, *t1;             // STRIPES regions of tcap tiles
@@ -253,6 +256,8 @@ hipError_t launch_check_symmetry(const int32_t *row_ptr, const int32_t *col_idx,
 hipError_t launch_build_vis_init(const int32_t *row_ptr, int32_t n, int32_t mark_isolated,
                                  uint32_t *vis_init, hipStream_t s);
 hipError_t launch_build_deg8(const int32_t *in_row_ptr, int32_t n, uint8_t *deg8, hipStream_t s);
+constexpr int ADJ_INLINE = 4;
+hipError_t launch_build_adj4(const int32_t *row_ptr, const int32_t *col_idx, int32_t n, int4 *adj4, hipStream_t s);
 hipError_t launch_build_probe_nb(const int32_t *row_ptr, const int32_t *in_row_ptr, const int32_t *in_col,
                                  int32_t n, int32_t *pnb, int32_t *snb, hipStream_t s);
 // transpose (in-edge CSR) of a CSR: in-degree counts, exclusive scan, scatter
