@@ -1336,6 +1336,12 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
 // Decision for level k, taken by wavefront 0 of every workgroup from the
 // counters the previous level left (identical in every workgroup); the
 // caller synchronises before reading it.
+// A top-down level whose frontier has fewer edges than this never turns to
+// pull: a pull level passes over every vertex, which costs more than pushing
+// a few edges, even when the edges left unexplored are fewer still (the last
+// levels of a long search; on the grid they flipped direction every level).
+__device__ __forceinline__ int64_t pull_floor(const Params &P) { return (int64_t)P.n >> 14; }
+
 __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) {
     const int lane = lane_id();
     const int slot = k % NSLOTS;
@@ -1393,7 +1399,7 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
             } else if (k == 0 || prev.dir == DIR_TD) {
                 // edges still to be explored from unvisited vertices
                 const int64_t m_u = (int64_t)P.m - edges_before - fdeg;
-                want_pull = fdeg * P.alpha > m_u;
+                want_pull = fdeg * P.alpha > m_u && fdeg >= pull_floor(P);
             } else {
                 want_pull = !(fsize * P.beta < (int64_t)P.n && fsize < prev.fsize);
             }
@@ -1688,7 +1694,8 @@ __device__ __forceinline__ int run_small(const Params &P, TdLds &sh, int k, int 
         // level (edges saturate only above SMALL_E, where the next launch
         // decides again from the exact counters)
         const int64_t m_u = (int64_t)P.m - edges_before - E1;
-        const bool want_pull = P.pol_dir == BFS_DIR_PULL || (P.pol_dir == BFS_DIR_AUTO && E1 * P.alpha > m_u);
+        const bool want_pull = P.pol_dir == BFS_DIR_PULL ||
+                               (P.pol_dir == BFS_DIR_AUTO && E1 * P.alpha > m_u && E1 >= pull_floor(P));
         const bool pull = want_pull && P.can_pull && wbits;   // level k set the next bitmap
         Ctx c;
         c.P = &P; c.sh = &sh; c.level = k; c.wg = wg; c.G = G; c.stripe = wg % STRIPES;
