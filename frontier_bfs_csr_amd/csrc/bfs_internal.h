@@ -229,6 +229,7 @@ hipError_t launch_init(const Params &P, int grid, hipStream_t s);
 // Graphs of at most ONE_N vertices are searched by one workgroup with the
 // visited bits and both frontiers in LDS (bfs_small.hip).
 constexpr int ONE_N = 3584;
+constexpr int ONE_M = 40960;           // ... and with the graph itself in LDS when m <= ONE_M
 hipError_t launch_one(const Params &P, hipStream_t s);
 // launch `launch_index` of the level chain: even indexes run the top-down
 // kernel, odd ones the bottom-up kernel
