@@ -92,6 +92,7 @@ struct LevelCommon {
     // decision
     int32_t mode;                     // 0 exit, 1 finish, 2 run
     int32_t dir, input_bm, wbits, wcf, clear_bm, adv_eb, small, use_cf, cf_clear, noq;
+    int32_t dfr;                      // the level before was queue-free: this level writes its frontier's dist
     int32_t fsize;
     int32_t prev_wcf;                 // the level before set the coarse map of this one
     int64_t prev_fdeg;                // the level before's frontier edges
@@ -459,6 +460,23 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
         }
 #pragma unroll
         for (int q = 0; q < CB; ++q) win[q] = tryq[q] && !((old[q] >> (v[q] & 31)) & 1u);
+    } else if (c.noq && P.symmetric) {
+        // a queue-free level needs a winner's degree only for the tallies:
+        // its degree byte (in-degree = out-degree here), and the row
+        // pointers only past 254
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            win[q] = tryq[q] && !((old[q] >> (v[q] & 31)) & 1u);
+            beg[q] = 0;
+            len[q] = win[q] ? (int)P.deg8[v[q]] : 0;
+        }
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            if (len[q] == 255) {
+                beg[q] = P.row_ptr[v[q]];
+                len[q] = P.row_ptr[v[q] + 1];
+            }
+        }
     } else {
 #pragma unroll
         for (int q = 0; q < CB; ++q) {
@@ -466,6 +484,28 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
             beg[q] = win[q] ? P.row_ptr[v[q]] : 0;
             len[q] = win[q] ? P.row_ptr[v[q] + 1] : 0;
         }
+    }
+    if (c.noq) {
+        // a queue-free level: its winners are the next level's frontier
+        // bitmap, and their dist is left to that level, which writes it in
+        // vertex order beside its own (a hub level's winners are spread over
+        // the whole array, and a scattered 4-byte store costs a line).  The
+        // parent, known only here, is a streaming store
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            if (win[q]) {
+                if (P.parent) __builtin_nontemporal_store(u[q], P.parent + v[q]);
+                if (c.wbits) atomicOr(c.nbm + (v[q] >> 5), 1u << (v[q] & 31));
+                if (c.wcf) {
+                    const uint32_t cb = (uint32_t)v[q] >> P.cf_sh;
+                    atomicOr(c.ncf + (cb >> 5), 1u << (cb & 31));
+                }
+                FBFS_ENQ(P, v[q]);
+            }
+            c.fcnt += win[q] ? 1 : 0;
+            c.fdeg += win[q] ? len[q] - beg[q] : 0;
+        }
+        return;
     }
 #pragma unroll
     for (int q = 0; q < CB; ++q) {
@@ -478,15 +518,6 @@ __device__ __forceinline__ void claim_batch(Ctx &c, const int (&v)[N], const boo
                 atomicOr(c.ncf + (cb >> 5), 1u << (cb & 31));
             }
         }
-    }
-    if (c.noq) {
-#pragma unroll
-        for (int q = 0; q < CB; ++q) {
-            if (win[q]) FBFS_ENQ(P, v[q]);
-            c.fcnt += win[q] ? 1 : 0;
-            c.fdeg += win[q] ? len[q] - beg[q] : 0;
-        }
-        return;
     }
     if (c.region) {
 #pragma unroll
@@ -828,6 +859,7 @@ __device__ __forceinline__ void td_from_bitmap(Ctx &c, uint32_t *cbm, uint32_t *
     int32_t *flist = sh.work + wv * FL_WAVE;
     uint64_t *cb64 = reinterpret_cast<uint64_t *>(cbm);
     uint64_t *ob64 = reinterpret_cast<uint64_t *>(obm);
+    const int dfr = sh.dfr;
     const int per = (P.nwp + c.G - 1) / c.G;
     const int start = min(P.nwp, c.wg * per);
     const int end = min(P.nwp, start + per);
@@ -854,6 +886,8 @@ __device__ __forceinline__ void td_from_bitmap(Ctx &c, uint32_t *cbm, uint32_t *
                 const bool in = (wj >> lane) & 1ull;
                 const uint64_t m = __ballot(in);
                 if (in) flist[cnt + mbcnt64(m)] = (w0 + j) * 64 + lane;
+                // the frontier's dist, left by a queue-free level before
+                if (in && dfr && (w0 + j) * 64 + lane < P.n) P.dist[(w0 + j) * 64 + lane] = c.level;
                 cnt += bits;
                 todo &= todo - 1;
             }
@@ -967,7 +1001,9 @@ __device__ __forceinline__ void bu_found(BuCtx &c, int wbase, int v, int u, int 
     }
     if (!P.symmetric) d = P.row_ptr[v + 1] - P.row_ptr[v];
     FBFS_ENQ(P, v);
-    __builtin_nontemporal_store(c.level + 1, P.dist + v);   // streaming, as in the word pass
+    // streaming, as in the word pass; after a queue-free level, dist is
+    // written per word once the wavefront's words are done
+    if (!c.sh->dfr) __builtin_nontemporal_store(c.level + 1, P.dist + v);
     if (P.parent) __builtin_nontemporal_store(u, P.parent + v);
     atomicOr(&c.sh->bu_fm[wave_id()][(v >> 6) - wbase], 1ull << (v & 63));
     c.fcnt += 1;
@@ -1148,6 +1184,8 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
     uint64_t *nbm64 = reinterpret_cast<uint64_t *>(nbm);
     int32_t *lst = sh.bu_lst[wv];
     const int use_cf = sh.use_cf, cf_sh = P.cf_sh;
+    const int dfr = sh.dfr;
+    const uint64_t *cb64 = reinterpret_cast<const uint64_t *>(cbm);
     constexpr int FW = 4;   // words probed together
     for (int cw = ws; cw < we; cw += WAVE) {
         const int nw = min(WAVE, we - cw);
@@ -1203,8 +1241,9 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
                 if (hitq) {
                     FBFS_ENQ(P, v[q]);
                     // outputs are never read back: streaming stores keep them
-                    // out of the caches the pass reads through
-                    __builtin_nontemporal_store(c.level + 1, P.dist + v[q]);
+                    // out of the caches the pass reads through (after a
+                    // queue-free level, dist is written per word at the end)
+                    if (!dfr) __builtin_nontemporal_store(c.level + 1, P.dist + v[q]);
                     if (P.parent) __builtin_nontemporal_store(par, P.parent + v[q]);
                     c.fcnt += 1;
                     c.fdeg += (P.symmetric && dg[q] < 255) ? dg[q] : P.row_ptr[v[q] + 1] - P.row_ptr[v[q]];
@@ -1244,10 +1283,26 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
         }
         wave_lds_sync();
         // the next-bitmap words (every word written) and visited words
+        const uint64_t fm = (lane < nw) ? sh.bu_fm[wv][lane] : 0ull;
         if (lane < nw) {
-            const uint64_t fm = sh.bu_fm[wv][lane];
             nbm64[cw + lane] = fm;
             if (fm) vis64[cw + lane] = myvis | fm;
+        }
+        // after a queue-free level, dist in one store per word with a change:
+        // the vertices found here and this level's frontier, which that
+        // level left (its finds are spread thin, and this level's are most
+        // of the rest: per word, each line is written once)
+        const uint64_t fr = (dfr && lane < nw) ? cb64[cw + lane] : 0ull;
+        for (uint64_t t = __ballot(dfr && (fm | fr) != 0ull); t; t &= t - 1) {
+            const int j = __ffsll((unsigned long long)t) - 1;
+            const uint32_t alo = (uint32_t)readlane_i((int)(uint32_t)fm, j);
+            const uint32_t ahi = (uint32_t)readlane_i((int)(uint32_t)(fm >> 32), j);
+            const uint32_t blo = (uint32_t)readlane_i((int)(uint32_t)fr, j);
+            const uint32_t bhi = (uint32_t)readlane_i((int)(uint32_t)(fr >> 32), j);
+            const bool hit = (((((uint64_t)ahi << 32) | alo) >> lane) & 1ull) != 0;
+            const bool fro = (((((uint64_t)bhi << 32) | blo) >> lane) & 1ull) != 0;
+            const int v = (cw + j) * 64 + lane;
+            if ((hit || fro) && v < P.n) __builtin_nontemporal_store(hit ? c.level + 1 : c.level, P.dist + v);
         }
         wave_lds_sync();
     }
@@ -1382,6 +1437,7 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
         sh.small = 0;
         sh.use_cf = 0;
         sh.noq = 0;
+        sh.dfr = (k > 0 && prev.noq) ? 1 : 0;
         sh.cf_clear = cf_prev2;
         if (done || err) {
             sh.mode = 0;
