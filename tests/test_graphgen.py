@@ -62,11 +62,15 @@ def test_grid_damaged_shape():
 def test_c1_shape_and_source():
     g = gg.c1_chung_lu()
     deg = g.degrees()
-    assert 3000 <= g.n <= 3485
+    # the configuration: about 3,485 vertices (largest component), about 31k
+    # entries, median degree 3, mean about 9, max about 1,255, about 10 levels
+    assert 3400 <= g.n <= 3485
+    assert 29000 <= g.m <= 33000
     assert np.median(deg) == 3
-    assert 7.5 <= deg.mean() <= 10
-    assert 1000 <= deg.max() <= 1500
+    assert 8 <= deg.mean() <= 10
+    assert 1100 <= deg.max() <= 1400
     assert _is_clean_symmetric(g)
+    assert 8 <= oracle.bfs(g.row_ptr, g.col_idx, int(g.sources[0]))[3] <= 12
     # the chosen source has the largest eccentricity, by the oracle over all vertices
     levels, reached = oracle.bfs_many(g.row_ptr, g.col_idx, np.arange(g.n, dtype=np.int32))
     assert (reached == g.n).all()
