@@ -294,7 +294,7 @@ def main():
         "detail": {
             "ms_per_bfs_median": round(float(np.median([p[2] for p in per_step])) * 1e3, 4),
             "gteps_hmean": round(len(step_gteps) / sum(1.0 / x for x in step_gteps), 4),
-            "init_kernel_us_avg": round(init_ms / args.steps * 1e3, 2),
+            "init_finish_us_avg": round(init_ms / args.steps * 1e3, 2),
             "level_kernels_ms_avg": round(level_ms / args.steps, 4),
             "level_launches_avg": round(launches / args.steps, 2),
             "kernels": {v["kernel"]: {"ms_avg": round(v["ms"] / args.steps, 4),

@@ -72,6 +72,7 @@ struct bfs_graph {
     int64_t tcap = 0, tscap = 0;
     unsigned long long *qtab = nullptr;   // queue chunk tables
     int4 *adj4 = nullptr;                 // inline short adjacencies
+    uint64_t *lvbm = nullptr;             // kept per-level found bitmaps (KCAP x nwp words)
     int32_t *wscr = nullptr;              // walk scratch (binned, merge), grown on demand
     int64_t wscr_ints = 0;
     unsigned long long *ctr = nullptr;
@@ -101,6 +102,7 @@ struct bfs_graph {
     SsspCtl *sctl = nullptr, *hsctl = nullptr;
     int32_t alpha = ALPHA, beta = BETA;
     uint32_t barrier_ticks = 200000000u;   // 2 s at 100 MHz
+    int64_t finish_min_n = FINISH_MIN_N;   // kept bitmaps and the finishing pass from this size
     int32_t last_L = 0;
     // timing hook
     int32_t timing = 0;
@@ -136,7 +138,7 @@ hipError_t dalloc(T **p, size_t count) {
 void free_all(bfs_graph *g) {
     void *ptrs[] = {g->visited, g->vis_init, g->fbm0, g->fbm1, g->cf, g->pnb, g->snb, g->deg8, g->in_row_ptr, g->in_col, g->q0, g->q1, g->t0, g->t1,
                     g->ts0, g->ts1, g->ctr, g->ctl, g->st_dir, g->st_fdeg, g->facts, g->enq, g->sreg, g->sslot,
-                    g->qtab, g->wscr, g->adj4};
+                    g->qtab, g->wscr, g->adj4, g->lvbm};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     void *vptrs[] = {g->va, g->vb, g->vs, g->vo, g->vt, g->vctl};
@@ -185,6 +187,7 @@ int alloc_workspace(bfs_graph *g) {
         {dalloc(&g->snb, n), "probe-neighbour index"},
         {dalloc(&g->deg8, n), "byte degrees"},
         {dalloc(&g->adj4, n), "inline adjacencies"},
+        {dalloc(&g->lvbm, n >= g->finish_min_n ? (size_t)KCAP * nwp : 1), "kept level bitmaps"},
         {dalloc(&g->q0, (size_t)queue_segs(n)), "frontier queue"},
         {dalloc(&g->q1, (size_t)queue_segs(n)), "frontier queue"},
         {dalloc(&g->qtab, (size_t)queue_tab(n)), "queue chunk tables"},
@@ -382,7 +385,11 @@ int32_t run_variant(bfs_graph *g, const Params &P, hipStream_t stream) {
         HIP_TRY(ensure_events(g, 3), BFS_EHIP);
         HIP_TRY(hipEventRecord(g->events[0], stream), BFS_EHIP);
     }
-    HIP_TRY(launch_init(P, g->grid, stream), BFS_EHIP);
+    {
+        Params Q = P;
+        Q.fill_dist = 1;   // this path has no finishing pass
+        HIP_TRY(launch_init(Q, g->grid, stream), BFS_EHIP);
+    }
     HIP_TRY(launch_var_seed(g->va, P.source, P.level_sizes, g->vctl, stream), BFS_EHIP);
     if (timing) HIP_TRY(hipEventRecord(g->events[1], stream), BFS_EHIP);
     const int32_t mode = g->pol_compact;
@@ -605,6 +612,12 @@ bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *co
         delete g;
         return nullptr;
     }
+    // tests lower the size from which levels keep bitmaps and a finishing
+    // pass writes dist, to run that path on small graphs
+    if (const char *t = getenv("FBFS_FINISH_MIN_N")) {
+        const long long v = atoll(t);
+        if (v >= 0) g->finish_min_n = v;
+    }
     int rc = validate_and_classify(g);
     if (rc == 0) rc = alloc_workspace(g);
     if (rc == 0) {
@@ -748,6 +761,8 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.snb = g->snb;
     P.deg8 = g->deg8;
     P.adj4 = g->adj4;
+    P.lvbm = g->lvbm;
+    P.fill_dist = (g->n < g->finish_min_n) ? 1 : 0;   // else the finishing pass writes dist
     P.in_row_ptr = g->symmetric ? g->row_ptr : g->in_row_ptr;
     P.in_col_idx = g->symmetric ? g->col_idx : g->in_col;
     P.can_pull = g->can_pull;
@@ -845,7 +860,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     int64_t batch = host_loop ? 1 : (prefix ? prefix : 12);
     bool prev_bu = true;   // so that alternation starts top-down
     std::vector<uint8_t> kinds;
-    float level_ms = 0.f, kind_ms[2] = {0.f, 0.f};
+    float level_ms = 0.f, kind_ms[2] = {0.f, 0.f}, finish_ms = 0.f;
     int32_t kind_launches[2] = {0, 0};
     g->launch_ms.clear();
     g->launch_ran.clear();
@@ -857,7 +872,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
         const int64_t k0 = k;
         kinds.clear();
         if (timing) {
-            HIP_TRY(ensure_events(g, 2 + (size_t)batch + 1), BFS_EHIP);
+            HIP_TRY(ensure_events(g, 2 + (size_t)batch + 2), BFS_EHIP);
             HIP_TRY(hipEventRecord(g->events[2], stream), BFS_EHIP);
         }
         for (int64_t i = 0; i < batch && k <= kmax; ++i, ++k) {
@@ -866,6 +881,12 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
             kinds.push_back(bu ? 1 : 0);
             HIP_TRY(launch_level(P, (int32_t)k, bu, bu ? g->grid_bu : g->grid, stream), BFS_EHIP);   // k = launch index
             if (timing) HIP_TRY(hipEventRecord(g->events[3 + i], stream), BFS_EHIP);
+        }
+        // the finishing pass writes dist once the search is done (it does
+        // nothing after a batch that leaves the search running)
+        if (!P.fill_dist) {
+            HIP_TRY(launch_finish(P, stream), BFS_EHIP);
+            if (timing) HIP_TRY(hipEventRecord(g->events[3 + (k - k0)], stream), BFS_EHIP);
         }
         HIP_TRY(hipMemcpyAsync(g->host_ctl, g->ctl, sizeof(HostCtl), hipMemcpyDeviceToHost, stream),
                 BFS_EHIP);
@@ -878,6 +899,11 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
                 kind_ms[kinds[i]] += ms;
                 kind_launches[kinds[i]] += 1;
                 g->launch_ms.push_back(ms);
+            }
+            if (!P.fill_dist) {
+                float ms = 0.f;
+                HIP_TRY(hipEventElapsedTime(&ms, g->events[2 + (k - k0)], g->events[3 + (k - k0)]), BFS_EHIP);
+                finish_ms += ms;
             }
         }
         const HostCtl &h = *g->host_ctl;
@@ -900,7 +926,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
             if (timing) {
                 float ms = 0.f;
                 HIP_TRY(hipEventElapsedTime(&ms, g->events[0], g->events[1]), BFS_EHIP);
-                g->last_init_ms = ms;
+                g->last_init_ms = ms + finish_ms;   // the init kernel and the finishing pass
                 g->last_level_ms = level_ms;
                 g->last_launches = (int32_t)k;
                 for (int t = 0; t < 2; ++t) {
@@ -1009,6 +1035,10 @@ int32_t bfs_run_noalloc(int32_t n, const int32_t *row_ptr, const int32_t *col_id
     P.snb = reinterpret_cast<int32_t *>(base + NA_SNB);
     P.deg8 = reinterpret_cast<uint8_t *>(base + NA_DEG8);
     P.adj4 = reinterpret_cast<int4 *>(base + NA_ADJ4);
+    // graphs this small keep no level bitmaps: the init kernel fills dist
+    static_assert(NA_N < FINISH_MIN_N, "the allocation-free search has no kept bitmaps");
+    P.lvbm = nullptr;
+    P.fill_dist = 1;
     P.in_row_ptr = symmetric ? row_ptr : nullptr;
     P.in_col_idx = symmetric ? col_idx : nullptr;
     P.can_pull = symmetric;

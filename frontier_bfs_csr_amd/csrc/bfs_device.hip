@@ -93,6 +93,8 @@ struct LevelCommon {
     int32_t mode;                     // 0 exit, 1 finish, 2 run
     int32_t dir, input_bm, wbits, wcf, clear_bm, adv_eb, small, use_cf, cf_clear, noq;
     int32_t dfr;                      // the level before was queue-free: this level writes its frontier's dist
+    int32_t keep_in;                  // ... and this level records its frontier in the kept bitmap instead
+    int32_t keep_out;                 // a bottom-up level recording its finds in the kept bitmap, no dist stores
     int32_t fsize;
     int32_t prev_wcf;                 // the level before set the coarse map of this one
     int64_t prev_fdeg;                // the level before's frontier edges
@@ -860,6 +862,7 @@ __device__ __forceinline__ void td_from_bitmap(Ctx &c, uint32_t *cbm, uint32_t *
     uint64_t *cb64 = reinterpret_cast<uint64_t *>(cbm);
     uint64_t *ob64 = reinterpret_cast<uint64_t *>(obm);
     const int dfr = sh.dfr;
+    uint64_t *lvi = sh.keep_in ? P.lvbm + (size_t)c.level * P.nwp : nullptr;
     const int per = (P.nwp + c.G - 1) / c.G;
     const int start = min(P.nwp, c.wg * per);
     const int end = min(P.nwp, start + per);
@@ -871,6 +874,7 @@ __device__ __forceinline__ void td_from_bitmap(Ctx &c, uint32_t *cbm, uint32_t *
             word = cb64[wp];
             cb64[wp] = 0ull;
             ob64[wp] = 0ull;
+            if (lvi) lvi[wp] = word;   // the frontier a queue-free level left, kept
         }
         uint64_t todo = __ballot(word != 0);
         for (;;) {
@@ -991,7 +995,7 @@ __device__ __forceinline__ int probe_first(const BuLds &sh, const uint32_t *cbm,
 
 // Records that listed vertex v found parent u (d = its in-degree; the
 // frontier tally counts out-degrees, which differ on a directed graph).
-__device__ __forceinline__ void bu_found(BuCtx &c, int wbase, int v, int u, int d) {
+__device__ __forceinline__ void bu_found(BuCtx &c, int wbase, int v, int u, int d, bool dstore) {
     const Params &P = *c.P;
     // v comes from this wavefront's own words [wbase, wbase + 64): anything
     // else is reported, never stored
@@ -1001,9 +1005,9 @@ __device__ __forceinline__ void bu_found(BuCtx &c, int wbase, int v, int u, int 
     }
     if (!P.symmetric) d = P.row_ptr[v + 1] - P.row_ptr[v];
     FBFS_ENQ(P, v);
-    // streaming, as in the word pass; after a queue-free level, dist is
-    // written per word once the wavefront's words are done
-    if (!c.sh->dfr) __builtin_nontemporal_store(c.level + 1, P.dist + v);
+    // streaming, as in the word pass (dstore: dist is neither kept as a
+    // bitmap nor written per word at the end after a queue-free level)
+    if (dstore) __builtin_nontemporal_store(c.level + 1, P.dist + v);
     if (P.parent) __builtin_nontemporal_store(u, P.parent + v);
     atomicOr(&c.sh->bu_fm[wave_id()][(v >> 6) - wbase], 1ull << (v & 63));
     c.fcnt += 1;
@@ -1012,7 +1016,7 @@ __device__ __forceinline__ void bu_found(BuCtx &c, int wbase, int v, int u, int 
 
 // Searches parents for the listed vertices lst[0, cnt) of this wavefront
 // (all inside words [wbase, wbase + 64)).
-__device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, int wbase) {
+__device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, int wbase, bool dstore) {
     const Params &P = *c.P;
     auto &sh = *c.sh;
     const int lane = lane_id();
@@ -1071,7 +1075,7 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
         for (int j = 0; j < R0; ++j) {
             const int i = j * WAVE + lane;
             const bool found = par[j] >= 0;
-            if (found) bu_found(c, wbase, v[j], par[j], en[j] - beg[j]);
+            if (found) bu_found(c, wbase, v[j], par[j], en[j] - beg[j], dstore);
             if (v[j] >= 0) {
                 hit[i] = BU_NOHIT;
                 deg[i] = en[j] - beg[j];
@@ -1158,7 +1162,7 @@ __device__ __forceinline__ void bu_list(BuCtx &c, const uint32_t *cbm, int cnt, 
     for (int j = 0; j < R0; ++j) {
         const int i = j * WAVE + lane;
         const int h = (i < cnt) ? hit[i] : BU_NOHIT;
-        if (h != BU_NOHIT) bu_found(c, wbase, lst[i] & 0x7fffffff, P.in_col_idx[h], deg[i]);
+        if (h != BU_NOHIT) bu_found(c, wbase, lst[i] & 0x7fffffff, P.in_col_idx[h], deg[i], dstore);
     }
 }
 
@@ -1184,8 +1188,12 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
     uint64_t *nbm64 = reinterpret_cast<uint64_t *>(nbm);
     int32_t *lst = sh.bu_lst[wv];
     const int use_cf = sh.use_cf, cf_sh = P.cf_sh;
-    const int dfr = sh.dfr;
+    const int dfr = sh.dfr, keep_out = sh.keep_out;
     const uint64_t *cb64 = reinterpret_cast<const uint64_t *>(cbm);
+    // kept bitmaps: this level's finds (distance level + 1) and its frontier
+    // when a queue-free level left it (distance level)
+    uint64_t *lvo = keep_out ? P.lvbm + (size_t)(c.level + 1) * P.nwp : nullptr;
+    uint64_t *lvi = sh.keep_in ? P.lvbm + (size_t)c.level * P.nwp : nullptr;
     constexpr int FW = 4;   // words probed together
     for (int cw = ws; cw < we; cw += WAVE) {
         const int nw = min(WAVE, we - cw);
@@ -1241,9 +1249,10 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
                 if (hitq) {
                     FBFS_ENQ(P, v[q]);
                     // outputs are never read back: streaming stores keep them
-                    // out of the caches the pass reads through (after a
-                    // queue-free level, dist is written per word at the end)
-                    if (!dfr) __builtin_nontemporal_store(c.level + 1, P.dist + v[q]);
+                    // out of the caches the pass reads through (dist is
+                    // written per word at the end after a queue-free level,
+                    // and not at all when the finds are kept as a bitmap)
+                    if (!dfr && !keep_out) __builtin_nontemporal_store(c.level + 1, P.dist + v[q]);
                     if (P.parent) __builtin_nontemporal_store(par, P.parent + v[q]);
                     c.fcnt += 1;
                     c.fdeg += (P.symmetric && dg[q] < 255) ? dg[q] : P.row_ptr[v[q] + 1] - P.row_ptr[v[q]];
@@ -1269,7 +1278,7 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
             const uint64_t m = __ballot(act);
             if (cnt + __popcll(m) > BU_GSZ) {
                 wave_lds_sync();
-                bu_list(c, cbm, cnt, cw);
+                bu_list(c, cbm, cnt, cw, !dfr && !keep_out);
                 wave_lds_sync();
                 cnt = 0;
             }
@@ -1279,7 +1288,7 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
         }
         if (cnt > 0) {
             wave_lds_sync();
-            bu_list(c, cbm, cnt, cw);
+            bu_list(c, cbm, cnt, cw, !dfr && !keep_out);
         }
         wave_lds_sync();
         // the next-bitmap words (every word written) and visited words
@@ -1288,10 +1297,14 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
             nbm64[cw + lane] = fm;
             if (fm) vis64[cw + lane] = myvis | fm;
         }
-        // after a queue-free level, dist in one store per word with a change:
-        // the vertices found here and this level's frontier, which that
-        // level left (its finds are spread thin, and this level's are most
-        // of the rest: per word, each line is written once)
+        if (lane < nw) {
+            if (lvo) lvo[cw + lane] = fm;
+            if (lvi) lvi[cw + lane] = cb64[cw + lane];
+        }
+        // past KCAP, after a queue-free level, dist in one store per word with
+        // a change: the vertices found here and this level's frontier, which
+        // that level left (its finds are spread thin, and this level's are
+        // most of the rest: per word, each line is written once)
         const uint64_t fr = (dfr && lane < nw) ? cb64[cw + lane] : 0ull;
         for (uint64_t t = __ballot(dfr && (fm | fr) != 0ull); t; t &= t - 1) {
             const int j = __ffsll((unsigned long long)t) - 1;
@@ -1315,26 +1328,32 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
     const int nth = gridDim.x * BLOCK;
     const int s = P.source;
     {
-        // dist and parent: 16-byte streaming stores (no level kernel reads
-        // them, and 8n bytes left in the caches would evict what the levels
-        // read), entry by entry when the caller's arrays are not 16-byte aligned
+        // parent, and dist unless the finishing pass writes it: 16-byte
+        // streaming stores (no level kernel reads them, and 8n bytes left in
+        // the caches would evict what the levels read), entry by entry when
+        // the caller's arrays are not 16-byte aligned.  Without the fill, the
+        // source's dist is the one entry written here
         typedef int v4i __attribute__((ext_vector_type(4)));
-        const bool al = ((reinterpret_cast<uintptr_t>(P.dist) |
+        const int fill = P.fill_dist;
+        const bool al = (((fill ? reinterpret_cast<uintptr_t>(P.dist) : 0) |
                           (P.parent ? reinterpret_cast<uintptr_t>(P.parent) : 0)) & 15) == 0;
-        const int lim = al ? (P.n >> 2) : 0;
+        const int lim = (fill || P.parent) && al ? (P.n >> 2) : 0;
         v4i *d4 = reinterpret_cast<v4i *>(P.dist);
         v4i *p4 = reinterpret_cast<v4i *>(P.parent);
         for (int i = tid; i < lim; i += nth) {
             v4i a = {-1, -1, -1, -1};
             v4i b = a;
             if ((s >> 2) == i) { a[s & 3] = 0; b[s & 3] = s; }
-            __builtin_nontemporal_store(a, d4 + i);
+            if (fill) __builtin_nontemporal_store(a, d4 + i);
             if (P.parent) __builtin_nontemporal_store(b, p4 + i);
         }
-        for (int i = 4 * lim + tid; i < P.n; i += nth) {
-            P.dist[i] = (i == s) ? 0 : -1;
-            if (P.parent) P.parent[i] = (i == s) ? s : -1;
+        if (fill || P.parent) {
+            for (int i = 4 * lim + tid; i < P.n; i += nth) {
+                if (fill) P.dist[i] = (i == s) ? 0 : -1;
+                if (P.parent) P.parent[i] = (i == s) ? s : -1;
+            }
         }
+        if (!fill && tid == 0) P.dist[s] = 0;
     }
     uint64_t *vis64 = reinterpret_cast<uint64_t *>(P.visited);
     const uint64_t *init64 = reinterpret_cast<const uint64_t *>(P.vis_init);
@@ -1362,6 +1381,7 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
             P.ctl->done = 0; P.ctl->L = 0; P.ctl->err = 0; P.ctl->err_info = 0;
             for (int i = 0; i < RAN_CAP; ++i) P.ctl->ran[i] = 0;
             P.ctl->lvl[0] = 0; P.ctl->lvl[1] = 0;
+            P.ctl->kmask = 0u;
             for (int k = 0; k < NSLOTS; ++k) {
                 P.ctl->slot[k].dir = 0; P.ctl->slot[k].wbits = 0; P.ctl->slot[k].wcf = 0;
                 P.ctl->slot[k].input_bm = 0; P.ctl->slot[k].fsize = 0; P.ctl->slot[k].noq = 0;
@@ -1437,7 +1457,11 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
         sh.small = 0;
         sh.use_cf = 0;
         sh.noq = 0;
-        sh.dfr = (k > 0 && prev.noq) ? 1 : 0;
+        // the frontier a queue-free level left: kept as a bitmap below KCAP,
+        // else its dist is written by this level
+        sh.keep_in = (!P.fill_dist && k > 0 && prev.noq && k < KCAP) ? 1 : 0;
+        sh.dfr = (k > 0 && prev.noq && !sh.keep_in) ? 1 : 0;
+        sh.keep_out = 0;
         sh.cf_clear = cf_prev2;
         if (done || err) {
             sh.mode = 0;
@@ -1461,6 +1485,7 @@ __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) 
             }
             const int dir = (want_pull && P.can_pull && has_bm) ? DIR_BU : DIR_TD;
             sh.dir = dir;
+            sh.keep_out = (!P.fill_dist && dir == DIR_BU && k + 1 < KCAP) ? 1 : 0;
             sh.reached_before = reached_before;
             sh.edges_before = edges_before;
             sh.input_bm = (dir == DIR_TD) && !has_queue;
@@ -1576,6 +1601,8 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
             P.ctl->slot[slot].input_bm = sh.input_bm;
             P.ctl->slot[slot].fsize = sh.fsize;
             P.ctl->slot[slot].noq = sh.noq;
+            if (sh.keep_in || sh.keep_out)
+                atomicOr(&P.ctl->kmask, (sh.keep_in ? 1u << k : 0u) | (sh.keep_out ? 1u << (k + 1) : 0u));
             P.ctl->slot[(k + 1) % NSLOTS].reached_before = sh.reached_before + sh.fsize;
             P.ctl->slot[(k + 1) % NSLOTS].edges_before = sh.edges_before + sh.fdeg;
         }
@@ -2122,6 +2149,104 @@ hipError_t launch_facts_reset(GraphFacts *f, hipStream_t s) {
 
 hipError_t launch_init(const Params &P, int grid, hipStream_t s) {
     hipLaunchKernelGGL(bfs_init_kernel, dim3(grid), dim3(BLOCK), 0, s, P);
+    return hipGetLastError();
+}
+
+// The finishing pass, after the level launches: nothing unless the search is
+// done (a search that needs another batch of launches finishes after it).  A
+// lane takes four consecutive vertices (a wavefront, four 64-vertex words),
+// and a wavefront FIN_U such groups at once with all their loads in flight:
+// the distance of the kept bitmap holding a vertex, else -1 for a vertex
+// never reached (not visited, or marked visited from the start for lack of
+// in-edges), else nothing (a level stored it, as the init kernel stored the
+// source's).  A lane whose four vertices all take a value writes them with
+// one 16-byte streaming store (a wavefront, sixteen whole 64-byte lines):
+// 4-byte stores issue four times the lane stores for the same bytes.  Each
+// bitmap is read as the 32-bit half holding the lane's four bits.
+constexpr int FIN_BLOCK = 256;
+constexpr int FIN_U = 4;
+__global__ __launch_bounds__(FIN_BLOCK) void bfs_finish_kernel(Params P) {
+    const Ctl *ctl = P.ctl;
+    if (!ctl->done || ctl->err) return;
+    const uint32_t km = ctl->kmask & ((1u << KCAP) - 1u);
+    const uint32_t *lv32 = reinterpret_cast<const uint32_t *>(P.lvbm);
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    v4i *d4 = reinterpret_cast<v4i *>(P.dist);
+    const bool al = (reinterpret_cast<uintptr_t>(P.dist) & 15) == 0;
+    const int lane = lane_id();
+    const int sh = (lane & 15) * 4;   // this lane's first vertex within its word
+    const int half = sh >> 5;         // the 32-bit half of the word holding it
+    const int bit = sh & 31;
+    const int64_t nquads = ((int64_t)P.nwp + 3) / 4;
+    const int64_t nwaves = (int64_t)gridDim.x * (FIN_BLOCK / WAVE);
+    for (int64_t q0 = ((int64_t)blockIdx.x * (FIN_BLOCK / WAVE) + threadIdx.x / WAVE) * FIN_U; q0 < nquads;
+         q0 += nwaves * FIN_U) {
+        int64_t w[FIN_U];
+        bool ok[FIN_U];
+        uint32_t rn[FIN_U];
+        int d[FIN_U][4];
+#pragma unroll
+        for (int u = 0; u < FIN_U; ++u) {
+            w[u] = (q0 + u) * 4 + (lane >> 4);
+            ok[u] = q0 + u < nquads && w[u] < P.nwp;
+            const size_t x = (size_t)w[u] * 2 + half;
+            rn[u] = ok[u] ? ((P.visited[x] & ~P.vis_init[x]) >> bit) & 15u : 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[u][e] = -1;
+        }
+        // the kept bitmaps, four levels at a time (every load of a round in
+        // flight before any is used)
+        for (uint32_t t = km; t;) {
+            int j[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                j[q] = t ? __ffs((int)t) - 1 : -1;
+                if (t) t &= t - 1;
+            }
+            uint32_t kn[FIN_U][4];
+#pragma unroll
+            for (int u = 0; u < FIN_U; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    kn[u][q] = (ok[u] && j[q] >= 0)
+                                   ? (lv32[((size_t)j[q] * P.nwp + w[u]) * 2 + half] >> bit) & 15u : 0u;
+#pragma unroll
+            for (int u = 0; u < FIN_U; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if ((kn[u][q] >> e) & 1u) d[u][e] = j[q];
+        }
+#pragma unroll
+        for (int u = 0; u < FIN_U; ++u) {
+            if (!ok[u]) continue;
+            const int64_t v0 = w[u] * 64 + sh;
+            bool wr[4];
+            bool all = al;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t v = v0 + e;
+                wr[e] = v < P.n && v != P.source && (d[u][e] >= 0 || !((rn[u] >> e) & 1u));
+                all = all && wr[e];
+            }
+            if (all) {
+                v4i xv = {d[u][0], d[u][1], d[u][2], d[u][3]};
+                __builtin_nontemporal_store(xv, d4 + (v0 >> 2));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (wr[e]) __builtin_nontemporal_store(d[u][e], P.dist + v0 + e);
+            }
+        }
+    }
+}
+
+hipError_t launch_finish(const Params &P, hipStream_t s) {
+    const int64_t quads = ((int64_t)P.nwp + 3) / 4;
+    const int64_t waves = (quads + FIN_U - 1) / FIN_U;
+    const int64_t blocks = (waves + FIN_BLOCK / WAVE - 1) / (FIN_BLOCK / WAVE);
+    hipLaunchKernelGGL(bfs_finish_kernel, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(FIN_BLOCK), 0, s, P);
     return hipGetLastError();
 }
 

@@ -89,10 +89,21 @@ struct Ctl {
     // status words, to order the next search's launches
     uint8_t ran[RAN_CAP];
     int32_t lvl[2];       // level the launch with index i starts at: lvl[i & 1]
-    int32_t pad0[2];
+    uint32_t kmask;       // bit j: level j's found set is in the kept bitmap lvbm[j]
+    int32_t pad0;
     SlotInfo slot[NSLOTS];
     alignas(128) uint32_t pad1;
 };
+
+// Levels below KCAP found from or into a bitmap (bottom-up levels, and the
+// frontier a queue-free top-down level leaves) keep their found set as a
+// bitmap instead of storing dist vertex by vertex; dist is written at the end.
+constexpr int KCAP = 16;
+// ... on graphs of at least FINISH_MIN_N vertices: on smaller ones dist stays
+// in the caches, its scattered stores cost little, and the finishing pass
+// would only add its launch (C2, 2^20 vertices: +10 %; C3, 2^22: +1.5 %;
+// C5, 2^24: -6.5 % per search)
+constexpr int64_t FINISH_MIN_N = 1LL << 23;
 
 constexpr int ERR_QUEUE_OVERFLOW = 1;
 constexpr int ERR_TILE_OVERFLOW = 2;
@@ -153,6 +164,11 @@ struct Params {
     const int4 *adj4;         // n entries: the out-neighbours of a vertex of out-degree at most
                               // ADJ_INLINE (-1 padded), so a small level reads them beside the
                               // claim instead of after it; unused for larger degrees
+    uint64_t *lvbm;           // KCAP bitmaps of nwp words: bitmap j holds the vertices at
+                              // distance j when a level recorded them there (bit j of the
+                              // control block's kmask) instead of storing their dist; the
+                              // finishing pass then writes dist once, in vertex order
+    int32_t fill_dist;        // the init kernel fills dist with -1 (paths without the finishing pass)
     uint32_t *fbm0, *fbm1;    // frontier bitmaps, 2*nwp words each
     Seg *q0, *q1;             // queue storage, queue_segs(n) segments each (chunks of 2^qk_sh)
     Seg *t0, *t1;             // STRIPES regions of tcap tiles
@@ -226,6 +242,9 @@ constexpr int64_t stats_cap(int64_t n) { return (n + 1) < (1 << 22) ? (n + 1) : 
 
 // host-side launch helpers (bfs_device.hip)
 hipError_t launch_init(const Params &P, int grid, hipStream_t s);
+// the finishing pass: once the search is done, dist of every vertex that no
+// level stored directly (kept bitmaps, unreached) in one vertex-order pass
+hipError_t launch_finish(const Params &P, hipStream_t s);
 // Graphs of at most ONE_N vertices are searched by one workgroup with the
 // visited bits and both frontiers in LDS (bfs_small.hip).
 constexpr int ONE_N = 3584;

@@ -158,7 +158,12 @@ int32_t bfs_last_error_code(void);
  *   CHAIN: as DEVICE but at most one level per launch (no small-frontier mode).
  * The small-frontier barrier's wait is bounded (2 s; the environment variable
  * FBFS_BARRIER_TIMEOUT_US, read at bfs_graph_create, overrides it for tests):
- * past it bfs_run returns BFS_EDEVICE instead of waiting forever. */
+ * past it bfs_run returns BFS_EDEVICE instead of waiting forever.
+ * On graphs of at least 2^23 vertices the levels run from or into a bitmap
+ * (bottom-up levels, and the level after a wide top-down level) keep their
+ * found sets as bitmaps, and a finishing launch after each batch writes dist
+ * in vertex order once the search is done; FBFS_FINISH_MIN_N, read at
+ * bfs_graph_create, lowers that size for tests.  Results are the same. */
 #define BFS_LOOP_DEVICE 0
 #define BFS_LOOP_HOST   1
 #define BFS_LOOP_CHAIN  2
@@ -203,14 +208,17 @@ int32_t bfs_last_run_stats(const bfs_graph *g, int32_t cap, int8_t *dir,
 
 /*
  * Timing hook.  When on, bfs_run records HIP events on its stream before and
- * after the initialisation launch and around every batch of level launches.
+ * after the initialisation launch, around every level launch and after the
+ * finishing pass that follows each batch of them.
  * Returns 0 or BFS_EINVAL.
  */
 int32_t bfs_set_timing(bfs_graph *g, int32_t on);
 
 /*
  * Milliseconds of the last timed bfs_run (host memory, any may be NULL):
- * init_ms = the initialisation launch; level_ms = the level launches, each
+ * init_ms = the initialisation launch and the finishing passes (the launch
+ * after each batch of level launches that writes dist from the levels' kept
+ * bitmaps once the search is done); level_ms = the level launches, each
  * timed alone (host waits between batches excluded); level_launches = level
  * launches issued (including the one that found the empty frontier and any
  * that exited at once after it).  Returns 0, or BFS_EINVAL if the last run was
