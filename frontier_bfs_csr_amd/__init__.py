@@ -30,7 +30,7 @@ COMPACT_DEFAULT, COMPACT_ATOMIC, COMPACT_PADDED, COMPACT_FILTER, COMPACT_FLAGS =
 SMALL_GRAPH_N = 3584
 
 EXPORTS = ("bfs_graph_create", "bfs_run", "bfs_graph_destroy", "bfs_last_error",
-           "bfs_set_policy", "bfs_last_run_stats", "bfs_set_timing", "bfs_last_run_timing",
+           "bfs_set_policy", "bfs_last_run_stats", "bfs_last_run_level_flags", "bfs_set_timing", "bfs_last_run_timing",
            "bfs_graph_info", "bfs_set_switch", "bfs_last_run_kernel_timing", "bfs_walk_level", "bfs_set_primitives",
            "bfs_sssp", "bfs_last_run_launch_timing", "bfs_run_noalloc", "bfs_debug_enqueue_counts",
            "bfs_last_error_code")
@@ -87,6 +87,8 @@ def _open(path):
     lib.bfs_set_switch.restype = i32
     lib.bfs_last_run_stats.argtypes = [P, i32, P, P]
     lib.bfs_last_run_stats.restype = i32
+    lib.bfs_last_run_level_flags.argtypes = [P, i32, P]
+    lib.bfs_last_run_level_flags.restype = i32
     lib.bfs_graph_info.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i32),
                                    ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.bfs_graph_info.restype = i32
@@ -273,6 +275,21 @@ def bfs_last_run_stats(g, cap=1 << 22):
     return L, d, fe
 
 
+LF_QUEUE_FREE, LF_FINDS_KEPT, LF_FRONTIER_KEPT, LF_FRONTIER_DIST, LF_FINISHING = 1, 2, 4, 8, 16
+
+
+def bfs_last_run_level_flags(g, cap=1 << 22):
+    """uint8 per level of the last run: LF_* bits, where the level's dist stores went."""
+    L0 = load().bfs_last_run_level_flags(g, 0, None)
+    if L0 < 0:
+        raise BfsError(L0, bfs_last_error())
+    f = np.zeros(min(L0, cap), np.uint8)
+    L = load().bfs_last_run_level_flags(g, f.shape[0], f.ctypes.data_as(ctypes.c_void_p))
+    if L < 0:
+        raise BfsError(L, bfs_last_error())
+    return f
+
+
 def bfs_set_timing(g, on=True):
     rc = load().bfs_set_timing(g, 1 if on else 0)
     if rc < 0:
@@ -353,6 +370,9 @@ class BfsGraph:
 
     def stats(self):
         return bfs_last_run_stats(self.handle)
+
+    def level_flags(self):
+        return bfs_last_run_level_flags(self.handle)
 
     def info(self):
         return bfs_graph_info(self.handle)

@@ -33,8 +33,8 @@ def _load():
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
-        lib.bfs_alg_bytes.argtypes = [ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, ctypes.c_int32,
-                                      ctypes.POINTER(ctypes.c_int64), P]
+        lib.bfs_alg_bytes.argtypes = [ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P, ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_int64), P, ctypes.POINTER(ctypes.c_int64)]
         lib.bfs_alg_bytes.restype = ctypes.c_int32
         _lib = lib
     return _lib
@@ -51,10 +51,12 @@ def transpose(row_ptr, col_idx):
     return in_rp, (key % n).astype(np.int32)
 
 
-def alg_bytes(row_ptr, col_idx, dist, dirs, with_parent=True, in_csr=None):
-    """Returns (init_bytes, level_bytes[L]) for one search.  in_csr = (in_row_ptr,
-    in_col_idx) of a directed graph (see transpose); None: the graph is
-    symmetric and serves as its own."""
+def alg_bytes(row_ptr, col_idx, dist, dirs, with_parent=True, in_csr=None, flags=None):
+    """Returns (init_bytes, level_bytes[L], finish_bytes) for one search.
+    in_csr = (in_row_ptr, in_col_idx) of a directed graph (see transpose);
+    None: the graph is symmetric and serves as its own.  flags: the search's
+    per-level flags (BfsGraph.level_flags(), plus 16 on level 0 when the
+    finishing pass ran); None: every level stores its own dist."""
     lib = _load()
     rp = np.ascontiguousarray(row_ptr, np.int32)
     ci = np.ascontiguousarray(col_idx, np.int32)
@@ -65,10 +67,14 @@ def alg_bytes(row_ptr, col_idx, dist, dirs, with_parent=True, in_csr=None):
     L = dr.shape[0]
     out = np.zeros(L, np.int64)
     init = ctypes.c_int64(0)
+    fin = ctypes.c_int64(0)
     p = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    fl = None if flags is None else np.ascontiguousarray(flags, np.uint8)
+    if fl is not None and fl.shape[0] != L:
+        raise ValueError("flags must hold one entry per level")
     rc = lib.bfs_alg_bytes(rp.shape[0] - 1, p(rp), p(ci), p(irp), p(ici), p(d), L, p(dr),
-                           1 if with_parent else 0,
-                           ctypes.byref(init), p(out))
+                           None if fl is None else p(fl), 1 if with_parent else 0,
+                           ctypes.byref(init), p(out), ctypes.byref(fin))
     if rc != 0:
         raise ValueError(f"bfs_alg_bytes failed ({rc})")
-    return int(init.value), out
+    return int(init.value), out, int(fin.value)

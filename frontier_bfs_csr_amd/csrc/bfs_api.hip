@@ -1305,11 +1305,28 @@ int32_t bfs_last_run_stats(const bfs_graph *g, int32_t cap, int8_t *dir, int64_t
     int64_t cnt = g->last_L;
     if (cnt > cap) cnt = cap;
     if (cnt > g->st_cap) cnt = g->st_cap;
-    if (cnt > 0 && dir)
+    if (cnt > 0 && dir) {
         HIP_TRY(hipMemcpy(dir, g->st_dir, (size_t)cnt, hipMemcpyDeviceToHost), BFS_EHIP);
+        for (int64_t k = 0; k < cnt; ++k) dir[k] &= 1;   // the level flags sit above bit 0
+    }
     if (cnt > 0 && frontier_edges)
         HIP_TRY(hipMemcpy(frontier_edges, g->st_fdeg, (size_t)cnt * sizeof(int64_t), hipMemcpyDeviceToHost),
                 BFS_EHIP);
+    return g->last_L;
+}
+
+int32_t bfs_last_run_level_flags(const bfs_graph *g, int32_t cap, uint8_t *flags) {
+    if (!g || cap < 0) {
+        set_error("NULL graph handle or negative capacity");
+        return BFS_EINVAL;
+    }
+    int64_t cnt = g->last_L;
+    if (cnt > cap) cnt = cap;
+    if (cnt > g->st_cap) cnt = g->st_cap;
+    if (cnt > 0 && flags) {
+        HIP_TRY(hipMemcpy(flags, g->st_dir, (size_t)cnt, hipMemcpyDeviceToHost), BFS_EHIP);
+        for (int64_t k = 0; k < cnt; ++k) flags[k] = (uint8_t)((flags[k] >> 1) & 31);
+    }
     return g->last_L;
 }
 

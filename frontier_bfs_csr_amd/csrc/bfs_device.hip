@@ -1594,7 +1594,13 @@ __device__ __forceinline__ void run_level(const Params &P, S &sh, int k, int wg,
     if (wg == 0) {
         if (threadIdx.x == 0) {
             if (P.level_sizes) P.level_sizes[k] = sh.fsize;
-            if (k < P.st_cap) { P.st_dir[k] = (int8_t)sh.dir; P.st_fdeg[k] = sh.fdeg; }
+            if (k < P.st_cap) {
+                // direction in bit 0; above it where the level's dist stores went
+                // (the level flags of the host interface)
+                const int fl = (sh.noq ? 1 : 0) | (sh.keep_out ? 2 : 0) | (sh.keep_in ? 4 : 0) | (sh.dfr ? 8 : 0);
+                P.st_dir[k] = (int8_t)(sh.dir | (fl << 1));
+                P.st_fdeg[k] = sh.fdeg;
+            }
             P.ctl->slot[slot].dir = sh.dir;
             P.ctl->slot[slot].wbits = sh.wbits;
             P.ctl->slot[slot].wcf = sh.wcf;
@@ -2168,6 +2174,9 @@ constexpr int FIN_U = 4;
 __global__ __launch_bounds__(FIN_BLOCK) void bfs_finish_kernel(Params P) {
     const Ctl *ctl = P.ctl;
     if (!ctl->done || ctl->err) return;
+    // the per-level record says the search ended here (level 0, bit 5:
+    // above the direction bit and the level's own flags)
+    if (blockIdx.x == 0 && threadIdx.x == 0 && P.st_cap > 0) P.st_dir[0] = (int8_t)(P.st_dir[0] | 32);
     const uint32_t km = ctl->kmask & ((1u << KCAP) - 1u);
     const uint32_t *lv32 = reinterpret_cast<const uint32_t *>(P.lvbm);
     typedef int v4i __attribute__((ext_vector_type(4)));

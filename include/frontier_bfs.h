@@ -207,6 +207,33 @@ int32_t bfs_last_run_stats(const bfs_graph *g, int32_t cap, int8_t *dir,
                            int64_t *frontier_edges);
 
 /*
+ * Where each level of the last bfs_run stored its outputs, for the byte model
+ * (the per-level table of the "Day 38 - Graph traversal on a GPU" page,
+ * section "What a level-synchronous search actually launches", extended by
+ * what each launch writes).  For k < min(L, cap), flags[k] ORs:
+ *   BFS_LF_QUEUE_FREE     a wide top-down level: winners go to the next
+ *                         bitmap only, and their dist is left to the next level
+ *   BFS_LF_FINDS_KEPT     the level's finds are kept as a bitmap; the
+ *                         finishing launch writes their dist
+ *   BFS_LF_FRONTIER_KEPT  the level keeps its frontier (left by a queue-free
+ *                         level) as a bitmap for the finishing launch
+ *   BFS_LF_FRONTIER_DIST  the level writes its frontier's dist (left by a
+ *                         queue-free level) beside its own
+ *   BFS_LF_FINISHING      (level 0 only) the search ended with the finishing
+ *                         launch, which wrote dist of every vertex that no
+ *                         level stored; the initialisation wrote none
+ * Levels of the small-frontier mode and of the other search paths read 0.
+ * Host memory, may be NULL.  Returns L of that run (0 if none yet), or a
+ * negative code.
+ */
+#define BFS_LF_QUEUE_FREE     1
+#define BFS_LF_FINDS_KEPT     2
+#define BFS_LF_FRONTIER_KEPT  4
+#define BFS_LF_FRONTIER_DIST  8
+#define BFS_LF_FINISHING      16
+int32_t bfs_last_run_level_flags(const bfs_graph *g, int32_t cap, uint8_t *flags);
+
+/*
  * Timing hook.  When on, bfs_run records HIP events on its stream before and
  * after the initialisation launch, around every level launch and after the
  * finishing pass that follows each batch of them.

@@ -44,6 +44,7 @@ def test_host_side_argument_errors():
     assert lib.bfs_set_primitives(None, 0, 1) == fb.BFS_EINVAL
     assert lib.bfs_sssp(None, 0, None, 1, None, None, None) == fb.BFS_EINVAL
     assert lib.bfs_last_run_stats(None, 0, None, None) == fb.BFS_EINVAL
+    assert lib.bfs_last_run_level_flags(None, 0, None) == fb.BFS_EINVAL
     assert lib.bfs_graph_info(None, None, None, None, None, None) == fb.BFS_EINVAL
     assert lib.bfs_last_run_launch_timing(None, 0, None, None) == fb.BFS_EINVAL
     # the allocation-free search refuses sizes beyond its fixed scratch, and

@@ -65,22 +65,40 @@ def test_finish_directed():
         check_graph(g, sources=[s] + [int(x) for x in g.sources], label="finish directed random")
 
 
-def test_finish_queue_free_wide_levels():
+@pytest.mark.parametrize("finish", [True, False])
+def test_finish_queue_free_wide_levels(finish):
     """A wide top-down level stores no dist; the next level keeps its frontier
-    as a bitmap, whether it pulls (alpha = 40) or expands from the bitmap
-    (alpha = 1 or 4)."""
+    as a bitmap (kept-bitmap path) or writes its dist (default path at this
+    size), whether it pulls (alpha = 40) or expands from the bitmap (alpha = 1
+    or 4).  The level flags record which, and the kept path's bottom-up levels
+    keep their finds."""
     import frontier_bfs_csr_amd as fb
     g = gg.disjoint_union(gg.star_graph(200_001), gg.rmat(16, 16, seed=23, nsrc=1))
     rp, ci = to_dev(g)
-    with finish_from(0), fb.BfsGraph(rp, ci) as bg:
+    seen = 0
+    ctx = finish_from(0) if finish else contextlib.nullcontext()
+    with ctx, fb.BfsGraph(rp, ci) as bg:
         for alpha in (1, 4, 40):
             bg.set_switch(alpha, 48)
             for s in (0, 1, 200_001 + 7):
-                print(f"[gpu] finish queue-free alpha={alpha} source={s}", flush=True)
+                print(f"[gpu] finish={finish} queue-free alpha={alpha} source={s}", flush=True)
                 L, dist, parent, sizes = run_hip(bg, g.n, s)
                 ref = oracle.bfs(g.row_ptr, g.col_idx, s)
                 oracle.assert_bfs_ok(g.row_ptr, g.col_idx, s, ref, dist, parent, L, sizes[:L],
                                      symmetric=True, label=f"finish {g.name} s={s} alpha={alpha}")
+                _, dirs, _ = bg.stats()
+                fl = bg.level_flags()
+                assert ((fl[0] & fb.LF_FINISHING) != 0) == finish, fl
+                for k in range(L):
+                    if dirs[k] == 1 and k + 1 < 16:
+                        assert bool(fl[k] & fb.LF_FINDS_KEPT) == finish, (k, fl)
+                    if dirs[k] == 0:
+                        assert not fl[k] & fb.LF_FINDS_KEPT, (k, fl)
+                    if k > 0 and fl[k - 1] & fb.LF_QUEUE_FREE:
+                        seen += 1
+                        want = fb.LF_FRONTIER_KEPT if finish else fb.LF_FRONTIER_DIST
+                        assert fl[k] & (fb.LF_FRONTIER_KEPT | fb.LF_FRONTIER_DIST) == want, (k, fl)
+    assert seen > 0
 
 
 def test_finish_unaligned_and_optional_outputs():
