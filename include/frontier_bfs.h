@@ -73,7 +73,9 @@ bfs_graph *bfs_graph_create(int32_t n, const int32_t *row_ptr, const int32_t *co
  *                    left untouched.
  *   stream           HIP stream for all work (0 = null stream).
  * Returns L >= 1, the number of non-empty levels (= max dist + 1), or a
- * negative BFS_E* code.  On BFS_EINVAL the outputs are untouched.
+ * negative BFS_E* code.  On BFS_EINVAL the outputs are untouched; after
+ * BFS_EHIP or BFS_EDEVICE their contents are unspecified (on large graphs
+ * dist is completed only by the launch that follows a finished search).
  */
 int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent_out,
                 int32_t *level_sizes_out, hipStream_t stream);
