@@ -838,12 +838,9 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
         }
         return L;
     }
-    if (timing) {
-        HIP_TRY(ensure_events(g, 4), BFS_EHIP);
-        HIP_TRY(hipEventRecord(g->events[0], stream), BFS_EHIP);
-    }
-    HIP_TRY(launch_init(P, g->grid, stream), BFS_EHIP);
-    if (timing) HIP_TRY(hipEventRecord(g->events[1], stream), BFS_EHIP);
+    if (timing) HIP_TRY(ensure_events(g, 4), BFS_EHIP);
+    HIP_TRY(launch_init(P, g->grid, stream, timing ? g->events[0] : nullptr, timing ? g->events[1] : nullptr),
+            BFS_EHIP);
     const bool host_loop = g->pol_loop == BFS_LOOP_HOST;
     int64_t k = 0;
     // Launch kinds: searches on one graph tend to repeat their pattern of
@@ -871,22 +868,24 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     for (;;) {
         const int64_t k0 = k;
         kinds.clear();
-        if (timing) {
-            HIP_TRY(ensure_events(g, 2 + (size_t)batch + 2), BFS_EHIP);
-            HIP_TRY(hipEventRecord(g->events[2], stream), BFS_EHIP);
-        }
+        // timing: launch i of the batch records events 2+2i and 3+2i as its
+        // kernel begins and ends, the finishing pass the next two
+        if (timing) HIP_TRY(ensure_events(g, 2 + 2 * (size_t)batch + 2), BFS_EHIP);
         for (int64_t i = 0; i < batch && k <= kmax; ++i, ++k) {
             const bool bu = k < prefix ? (k < (int64_t)plan.size() && plan[k] == 2) : !prev_bu;
             prev_bu = bu;
             kinds.push_back(bu ? 1 : 0);
-            HIP_TRY(launch_level(P, (int32_t)k, bu, bu ? g->grid_bu : g->grid, stream), BFS_EHIP);   // k = launch index
-            if (timing) HIP_TRY(hipEventRecord(g->events[3 + i], stream), BFS_EHIP);
+            HIP_TRY(launch_level(P, (int32_t)k, bu, bu ? g->grid_bu : g->grid, stream,   // k = launch index
+                                 timing ? g->events[2 + 2 * i] : nullptr, timing ? g->events[3 + 2 * i] : nullptr),
+                    BFS_EHIP);
         }
         // the finishing pass writes dist once the search is done (it does
         // nothing after a batch that leaves the search running)
         if (!P.fill_dist) {
-            HIP_TRY(launch_finish(P, stream), BFS_EHIP);
-            if (timing) HIP_TRY(hipEventRecord(g->events[3 + (k - k0)], stream), BFS_EHIP);
+            const int64_t j = k - k0;
+            HIP_TRY(launch_finish(P, stream, timing ? g->events[2 + 2 * j] : nullptr,
+                                  timing ? g->events[3 + 2 * j] : nullptr),
+                    BFS_EHIP);
         }
         HIP_TRY(hipMemcpyAsync(g->host_ctl, g->ctl, sizeof(HostCtl), hipMemcpyDeviceToHost, stream),
                 BFS_EHIP);
@@ -894,7 +893,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
         if (timing) {
             for (int64_t i = 0; i < k - k0; ++i) {
                 float ms = 0.f;
-                HIP_TRY(hipEventElapsedTime(&ms, g->events[2 + i], g->events[3 + i]), BFS_EHIP);
+                HIP_TRY(hipEventElapsedTime(&ms, g->events[2 + 2 * i], g->events[3 + 2 * i]), BFS_EHIP);
                 level_ms += ms;
                 kind_ms[kinds[i]] += ms;
                 kind_launches[kinds[i]] += 1;
@@ -902,7 +901,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
             }
             if (!P.fill_dist) {
                 float ms = 0.f;
-                HIP_TRY(hipEventElapsedTime(&ms, g->events[2 + (k - k0)], g->events[3 + (k - k0)]), BFS_EHIP);
+                HIP_TRY(hipEventElapsedTime(&ms, g->events[2 + 2 * (k - k0)], g->events[3 + 2 * (k - k0)]), BFS_EHIP);
                 finish_ms += ms;
             }
         }

@@ -46,6 +46,8 @@
 // a full LDS buffer spills to a direct global append instead).
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "bfs_internal.h"
 #include "frontier_bfs.h"
 
@@ -2153,8 +2155,8 @@ hipError_t launch_facts_reset(GraphFacts *f, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_init(const Params &P, int grid, hipStream_t s) {
-    hipLaunchKernelGGL(bfs_init_kernel, dim3(grid), dim3(BLOCK), 0, s, P);
+hipError_t launch_init(const Params &P, int grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+    hipExtLaunchKernelGGL(bfs_init_kernel, dim3(grid), dim3(BLOCK), 0, s, start, stop, 0, P);
     return hipGetLastError();
 }
 
@@ -2251,19 +2253,21 @@ __global__ __launch_bounds__(FIN_BLOCK) void bfs_finish_kernel(Params P) {
     }
 }
 
-hipError_t launch_finish(const Params &P, hipStream_t s) {
+hipError_t launch_finish(const Params &P, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     const int64_t quads = ((int64_t)P.nwp + 3) / 4;
     const int64_t waves = (quads + FIN_U - 1) / FIN_U;
     const int64_t blocks = (waves + FIN_BLOCK / WAVE - 1) / (FIN_BLOCK / WAVE);
-    hipLaunchKernelGGL(bfs_finish_kernel, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(FIN_BLOCK), 0, s, P);
+    hipExtLaunchKernelGGL(bfs_finish_kernel, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(FIN_BLOCK), 0, s,
+                          start, stop, 0, P);
     return hipGetLastError();
 }
 
-hipError_t launch_level(const Params &P, int32_t launch_index, bool bottom_up, int grid, hipStream_t s) {
+hipError_t launch_level(const Params &P, int32_t launch_index, bool bottom_up, int grid, hipStream_t s,
+                        hipEvent_t start, hipEvent_t stop) {
     if (bottom_up)
-        hipLaunchKernelGGL(bfs_bu_kernel, dim3(grid), dim3(BLOCK), 0, s, P, launch_index);
+        hipExtLaunchKernelGGL(bfs_bu_kernel, dim3(grid), dim3(BLOCK), 0, s, start, stop, 0, P, launch_index);
     else
-        hipLaunchKernelGGL(bfs_td_kernel, dim3(grid), dim3(BLOCK), 0, s, P, launch_index);
+        hipExtLaunchKernelGGL(bfs_td_kernel, dim3(grid), dim3(BLOCK), 0, s, start, stop, 0, P, launch_index);
     return hipGetLastError();
 }
 

@@ -241,10 +241,14 @@ constexpr int64_t tstart_cap(int64_t m) { return m / EB_TE + 2; }
 constexpr int64_t stats_cap(int64_t n) { return (n + 1) < (1 << 22) ? (n + 1) : (1 << 22); }
 
 // host-side launch helpers (bfs_device.hip)
-hipError_t launch_init(const Params &P, int grid, hipStream_t s);
+// Launch helpers.  start/stop (may be null): HIP events that the launch
+// itself records when the kernel begins and ends (the timing hook), so a
+// timed interval holds the kernel alone, not the gaps around it.
+hipError_t launch_init(const Params &P, int grid, hipStream_t s, hipEvent_t start = nullptr,
+                       hipEvent_t stop = nullptr);
 // the finishing pass: once the search is done, dist of every vertex that no
 // level stored directly (kept bitmaps, unreached) in one vertex-order pass
-hipError_t launch_finish(const Params &P, hipStream_t s);
+hipError_t launch_finish(const Params &P, hipStream_t s, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Graphs of at most ONE_N vertices are searched by one workgroup with the
 // visited bits and both frontiers in LDS (bfs_small.hip).
 constexpr int ONE_N = 3584;
@@ -252,7 +256,8 @@ constexpr int ONE_M = 40960;           // ... and with the graph itself in LDS w
 hipError_t launch_one(const Params &P, hipStream_t s);
 // launch `launch_index` of the level chain: even indexes run the top-down
 // kernel, odd ones the bottom-up kernel
-hipError_t launch_level(const Params &P, int32_t launch_index, bool bottom_up, int grid, hipStream_t s);
+hipError_t launch_level(const Params &P, int32_t launch_index, bool bottom_up, int grid, hipStream_t s,
+                        hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // resident workgroups per compute unit of the top-down or bottom-up kernel
 int level_kernel_blocks_per_cu(bool bottom_up);
 

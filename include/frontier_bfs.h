@@ -236,9 +236,10 @@ int32_t bfs_last_run_stats(const bfs_graph *g, int32_t cap, int8_t *dir,
 int32_t bfs_last_run_level_flags(const bfs_graph *g, int32_t cap, uint8_t *flags);
 
 /*
- * Timing hook.  When on, bfs_run records HIP events on its stream before and
- * after the initialisation launch, around every level launch and after the
- * finishing pass that follows each batch of them.
+ * Timing hook.  When on, bfs_run's initialisation, level and finishing
+ * launches each record a pair of HIP events as their kernel begins and ends
+ * (the launch records them itself, so an interval holds the kernel and not
+ * the gaps between launches).
  * Returns 0 or BFS_EINVAL.
  */
 int32_t bfs_set_timing(bfs_graph *g, int32_t on);
@@ -259,8 +260,8 @@ int32_t bfs_last_run_timing(const bfs_graph *g, float *init_ms, float *level_ms,
 /*
  * The level launches of the last timed bfs_run split by kernel (host memory,
  * any may be NULL): milliseconds and launches of the top-down kernel and of
- * the bottom-up kernel, each launch timed by HIP events recorded just before
- * and just after it on the run's stream.  The two sums make up level_ms of
+ * the bottom-up kernel, each launch timed by the HIP events it records as its
+ * kernel begins and ends.  The two sums make up level_ms of
  * bfs_last_run_timing.  Returns 0, or BFS_EINVAL if the last run was not timed.
  */
 int32_t bfs_last_run_kernel_timing(const bfs_graph *g, float *td_ms, int32_t *td_launches,
@@ -269,7 +270,7 @@ int32_t bfs_last_run_kernel_timing(const bfs_graph *g, float *td_ms, int32_t *td
 /*
  * The level launches of the last timed bfs_run one by one (host memory, either
  * may be NULL; the first min(cap, count) entries are written): ms[i] = launch
- * i's time between HIP events recorded just before and just after it on the
+ * i's time between the HIP events it records as its kernel begins and ends on the
  * run's stream; ran[i] = the device's record of its work: 1 the top-down
  * kernel ran a level or found the empty frontier, 2 the bottom-up kernel did,
  * 0 it passed its level on or exited at once (launches from index 64 on are
