@@ -1210,7 +1210,15 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
         // every unvisited one in a sparse word
         const bool dense = lane < nw && __popcll(~myvis) >= BU_DENSE;
         uint64_t myrest = dense ? 0ull : ~myvis;
+        // issue priority falls as the wavefront gets through its words (3 and
+        // 2 over the halves of pass 1, 1 and 0 over those of pass 2): a
+        // compute unit otherwise issues for its oldest wavefronts first, and
+        // the workgroups placed last on it end the level well after the others
+        const int nd_it = (__popcll(__ballot(dense)) + FW - 1) / FW;
+        int d_it = 0;
+        __builtin_amdgcn_s_setprio(3);
         for (uint64_t todo = __ballot(dense); todo;) {
+            if (++d_it == nd_it / 2 + 1) __builtin_amdgcn_s_setprio(2);
             int jw[FW], v[FW], f[FW], dg[FW];
             uint32_t w[FW];
 #pragma unroll
@@ -1272,6 +1280,9 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
         // marks those already probed at their probe neighbour)
         int cnt = 0;
         const uint64_t denses = __ballot(dense);
+        const int n2 = readlane_i(wave_incl_scan_i32(__popcll(myrest)), WAVE - 1);
+        int d2 = 0;
+        __builtin_amdgcn_s_setprio(1);
         for (uint64_t tm = __ballot(myrest != 0ull); tm; tm &= tm - 1) {
             const int j = __ffsll((unsigned long long)tm) - 1;
             const uint32_t lo = (uint32_t)readlane_i((int)(uint32_t)myrest, j);
@@ -1282,6 +1293,8 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
                 wave_lds_sync();
                 bu_list(c, cbm, cnt, cw, !dfr && !keep_out);
                 wave_lds_sync();
+                d2 += cnt;
+                if (2 * d2 >= n2) __builtin_amdgcn_s_setprio(0);
                 cnt = 0;
             }
             if (act)
