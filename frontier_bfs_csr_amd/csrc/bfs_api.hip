@@ -388,6 +388,7 @@ int32_t run_variant(bfs_graph *g, const Params &P, hipStream_t stream) {
     {
         Params Q = P;
         Q.fill_dist = 1;   // this path has no finishing pass
+        Q.l0_init = 0;     // ... and seeds level 0 itself
         HIP_TRY(launch_init(Q, g->grid, stream), BFS_EHIP);
     }
     HIP_TRY(launch_var_seed(g->va, P.source, P.level_sizes, g->vctl, stream), BFS_EHIP);
@@ -763,6 +764,7 @@ int32_t bfs_run(bfs_graph *g, int32_t source, int32_t *dist_out, int32_t *parent
     P.adj4 = g->adj4;
     P.lvbm = g->lvbm;
     P.fill_dist = (g->n < g->finish_min_n) ? 1 : 0;   // else the finishing pass writes dist
+    P.l0_init = g->sorted;   // level 0 may run in the init kernel (it needs sorted rows)
     P.in_row_ptr = g->symmetric ? g->row_ptr : g->in_row_ptr;
     P.in_col_idx = g->symmetric ? g->col_idx : g->in_col;
     P.can_pull = g->can_pull;
@@ -1038,6 +1040,7 @@ int32_t bfs_run_noalloc(int32_t n, const int32_t *row_ptr, const int32_t *col_id
     static_assert(NA_N < FINISH_MIN_N, "the allocation-free search has no kept bitmaps");
     P.lvbm = nullptr;
     P.fill_dist = 1;
+    P.l0_init = h.unsorted ? 0 : 1;
     P.in_row_ptr = symmetric ? row_ptr : nullptr;
     P.in_col_idx = symmetric ? col_idx : nullptr;
     P.can_pull = symmetric;

@@ -1338,21 +1338,181 @@ __device__ __forceinline__ void bottom_up(BuCtx &c, const uint32_t *cbm, uint32_
 
 // ---------------------------------------------------------- kernels -------
 
+// A top-down level whose frontier has fewer edges than this never turns to
+// pull: a pull level passes over every vertex, which costs more than pushing
+// a few edges, even when the edges left unexplored are fewer still (the last
+// levels of a long search; on the grid they flipped direction every level).
+__device__ __forceinline__ int64_t pull_floor(const Params &P) { return (int64_t)P.n >> 14; }
+
+// Level 0 in the init kernel: a source of at most L0_MAX entries whose level
+// is top-down.  Its winners are its distinct out-neighbours other than
+// itself, known without a claim when the rows are sorted.  The fill
+// workgroups write everything as for a search from level 0; then each one
+// rewrites, in place, the entries it wrote that level 0 changes (dist and
+// parent of the winners, their visited and next-frontier words, the coarse
+// map of level 1), after a barrier, so those stores land after its own fill
+// stores.  The last workgroup of the grid does no fill: it writes the control
+// block and counters and either the source's queue entry or level 1's queue
+// lists, counters and level 0's record.  The first level launch then starts
+// at level 1, and the search has one launch fewer.
+constexpr int L0_MAX = BLOCK;   // one entry per thread of the control workgroup
+
+struct Level0 {
+    int on;        // level 0 runs here
+    int wb, wcf;   // it sets level 1's frontier bitmap / coarse map
+};
+
+// The decision decide() takes for level 0 (the same in every thread).
+__device__ __forceinline__ Level0 level0_here(const Params &P, int d) {
+    Level0 r{0, 0, 0};
+    if (!P.l0_init || d < 0 || d > L0_MAX || (int64_t)d > (1LL << P.qk_sh) || P.pol_dir == BFS_DIR_PULL)
+        return r;
+    const bool pull = P.pol_dir == BFS_DIR_AUTO && (int64_t)d * P.alpha > (int64_t)P.m - d && d >= pull_floor(P);
+    if (pull && P.can_pull) return r;
+    r.on = 1;
+    const double m_left = (double)((int64_t)P.m - d);
+    r.wb = (P.can_pull && P.pol_dir == BFS_DIR_AUTO &&
+            (double)P.max_deg * (double)d * (double)(P.alpha + 1) > m_left) ? 1 : 0;
+    r.wcf = (r.wb && ((int64_t)d << P.cf_sh) <= 2 * (int64_t)P.n) ? 1 : 0;
+    return r;
+}
+
 __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
-    const int tid = blockIdx.x * BLOCK + threadIdx.x;
-    const int nth = gridDim.x * BLOCK;
+    __shared__ int32_t nsrc[L0_MAX];
+    __shared__ uint64_t l0_tot[3][WAVES];
+    __shared__ int32_t l0_cnt[WAVES];
+    __shared__ int32_t l0_ts[L0_MAX], l0_beg[L0_MAX], l0_len[L0_MAX], l0_eo[L0_MAX];
+    const int G = (int)gridDim.x - 1;   // fill workgroups (the launch adds the control one)
     const int s = P.source;
+    // the source's row bounds: the fill below does not wait for them
+    const int sb = P.row_ptr[s];
+    const int d = P.row_ptr[s + 1] - sb;
+    if ((int)blockIdx.x == G) {
+        const Level0 l0 = level0_here(P, d);
+        // control workgroup: every counter of every slot, the control block,
+        // then level 0's output queue (the source's entry) or level 1's
+        for (int i = threadIdx.x; i < NSLOTS * NCTR; i += BLOCK) P.ctr[(size_t)i * CTR_STRIDE] = 0ull;
+        if (threadIdx.x == 0) {
+            P.ctl->done = 0; P.ctl->L = 0; P.ctl->err = 0; P.ctl->err_info = 0;
+            for (int i = 0; i < RAN_CAP; ++i) P.ctl->ran[i] = 0;
+            P.ctl->lvl[0] = l0.on ? 1 : 0; P.ctl->lvl[1] = 0;
+            P.ctl->kmask = 0u;
+            for (int k = 0; k < NSLOTS; ++k) {
+                P.ctl->slot[k].dir = 0; P.ctl->slot[k].wbits = 0; P.ctl->slot[k].wcf = 0;
+                P.ctl->slot[k].input_bm = 0; P.ctl->slot[k].fsize = 0; P.ctl->slot[k].noq = 0;
+                P.ctl->slot[k].reached_before = 0; P.ctl->slot[k].edges_before = 0;
+            }
+        }
+        if (!l0.on) {
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                Ctx c;
+                c.P = &P; c.sh = nullptr; c.level = -1; c.wg = 0; c.G = 1; c.stripe = 0; c.nslot = 0; c.wbits = 0;
+                c.nbm = nullptr; c.ncf = nullptr; c.wcf = 0; c.noq = 0; c.nq = P.q0; c.nt = P.t0; c.nts = P.ts0;
+                c.fcnt = 0; c.fdeg = 0; c.region = nullptr; c.converting = 0;
+                const int l = list_of(d);
+                if (l >= 0) {
+                    const int nseg = (l == L_TILE) ? (d + TILE - 1) / TILE : 1;
+                    P.ctr[(size_t)(l * STRIPES) * CTR_STRIDE] = ((unsigned long long)nseg << 32) | (unsigned)d;
+                    write_vertex_segments(c, l, s, sb, d, 0, 0);
+                }
+                P.ctr[(size_t)VC_BASE * CTR_STRIDE] = (1ull << 32) | (unsigned)d;
+            }
+            return;
+        }
+        // level 1's queue lists (stripe 0) and counters, and level 0's record,
+        // as run_level and flush leave them: thread t takes entry t of the
+        // row, a winner when it is in [0, n) and neither the source nor the
+        // entry before it (sorted row)
+        const int t = threadIdx.x;
+        if (t < d) nsrc[t] = P.col_idx[sb + t];
+        __syncthreads();
+        const int v = (t < d) ? nsrc[t] : -1;
+        const bool win = t < d && v != s && (t == 0 || nsrc[t - 1] != v) && (uint32_t)v < (uint32_t)P.n;
+        const int beg = win ? P.row_ptr[v] : 0;
+        const int len = win ? P.row_ptr[v + 1] - beg : 0;
+        const int l = win ? list_of(len) : -1;
+        const uint64_t one = (l < 0) ? 0ull
+                             : ((uint64_t)(l == L_TILE ? (len + TILE - 1) / TILE : 1) << 32) | (uint32_t)len;
+        uint64_t in[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            in[q] = wave_incl_scan_u64(l == q ? one : 0ull);
+            if (lane_id() == WAVE - 1) l0_tot[q][wave_id()] = in[q];
+        }
+        const int cin = wave_incl_scan_i32(win ? 1 : 0);
+        if (lane_id() == WAVE - 1) l0_cnt[wave_id()] = cin;
+        __syncthreads();
+        uint64_t ex[3], all[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            ex[q] = in[q] - (l == q ? one : 0ull);
+            all[q] = 0ull;
+            for (int w = 0; w < WAVES; ++w) {
+                if (w < wave_id()) ex[q] += l0_tot[q][w];
+                all[q] += l0_tot[q][w];
+            }
+        }
+        Ctx c;
+        c.P = &P; c.sh = nullptr; c.level = 0; c.wg = 0; c.G = 1; c.stripe = 0; c.nslot = 1; c.wbits = l0.wb;
+        c.nbm = nullptr; c.ncf = nullptr; c.wcf = l0.wcf; c.noq = 0; c.nq = P.q1; c.nt = P.t1; c.nts = P.ts1;
+        c.fcnt = 0; c.fdeg = 0; c.region = nullptr; c.converting = 0;
+        if (win && !P.fill_dist) P.dist[v] = 1;   // (with the fill, its rewrite stores it)
+        if (l == L_SMALL || l == L_MID)
+            write_vertex_segments(c, l, v, beg, len, (int64_t)(ex[l] >> 32), (int64_t)(ex[l] & 0xffffffffull));
+        // hubs: their pieces, written by the whole workgroup (where each
+        // entry's pieces start, then a search for the entry of piece gt)
+        if (t < d) {
+            l0_ts[t] = (int32_t)(ex[L_TILE] >> 32);
+            l0_beg[t] = beg;
+            l0_len[t] = (l == L_TILE) ? len : 0;
+            l0_eo[t] = (int32_t)(ex[L_TILE] & 0xffffffffull);
+        }
+        __syncthreads();
+        const int ntiles = (int)(all[L_TILE] >> 32);
+        for (int gt = t; gt < ntiles; gt += BLOCK) {
+            int lo = 0, hi = d;   // last entry whose pieces start at or before gt
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (l0_ts[mid] <= gt) lo = mid; else hi = mid;
+            }
+            const int pcs = gt - l0_ts[lo];
+            const int64_t si = gt;
+            write_piece(c, L_TILE, si, nsrc[lo], l0_beg[lo] + pcs * TILE, min(TILE, l0_len[lo] - pcs * TILE),
+                        (int64_t)l0_eo[lo] + (int64_t)pcs * TILE, si < P.tcap ? c.nt + si : nullptr);
+        }
+        if (t == 0) {
+            uint64_t winners = 0ull, edges = 0ull;
+            for (int w = 0; w < WAVES; ++w) winners += (uint64_t)l0_cnt[w];
+            for (int q = 0; q < 3; ++q) {
+                *ctr_at(P, 1, q * STRIPES) = all[q];
+                edges += all[q] & 0xffffffffull;
+            }
+            *ctr_at(P, 1, VC_BASE) = (winners << 32) | edges;
+            if (P.level_sizes) P.level_sizes[0] = 1;
+            if (P.st_cap > 0) { P.st_dir[0] = (int8_t)DIR_TD; P.st_fdeg[0] = d; }
+            P.ctl->slot[0].dir = DIR_TD;
+            P.ctl->slot[0].wbits = l0.wb;
+            P.ctl->slot[0].wcf = l0.wcf;
+            P.ctl->slot[0].fsize = 1;
+            P.ctl->slot[1].reached_before = 1;
+            P.ctl->slot[1].edges_before = d;
+        }
+        return;
+    }
+    const int tid = blockIdx.x * BLOCK + threadIdx.x;
+    const int nth = G * BLOCK;
+    // parent, and dist unless the finishing pass writes it: 16-byte
+    // streaming stores (no level kernel reads them, and 8n bytes left in the
+    // caches would evict what the levels read), entry by entry when the
+    // caller's arrays are not 16-byte aligned.  Without the fill, the
+    // source's dist is the one entry written here
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const int fill = P.fill_dist;
+    const bool al = (((fill ? reinterpret_cast<uintptr_t>(P.dist) : 0) |
+                      (P.parent ? reinterpret_cast<uintptr_t>(P.parent) : 0)) & 15) == 0;
+    const int lim = (fill || P.parent) && al ? (P.n >> 2) : 0;
     {
-        // parent, and dist unless the finishing pass writes it: 16-byte
-        // streaming stores (no level kernel reads them, and 8n bytes left in
-        // the caches would evict what the levels read), entry by entry when
-        // the caller's arrays are not 16-byte aligned.  Without the fill, the
-        // source's dist is the one entry written here
-        typedef int v4i __attribute__((ext_vector_type(4)));
-        const int fill = P.fill_dist;
-        const bool al = (((fill ? reinterpret_cast<uintptr_t>(P.dist) : 0) |
-                          (P.parent ? reinterpret_cast<uintptr_t>(P.parent) : 0)) & 15) == 0;
-        const int lim = (fill || P.parent) && al ? (P.n >> 2) : 0;
         v4i *d4 = reinterpret_cast<v4i *>(P.dist);
         v4i *p4 = reinterpret_cast<v4i *>(P.parent);
         for (int i = tid; i < lim; i += nth) {
@@ -1388,49 +1548,63 @@ __global__ __launch_bounds__(BLOCK) void bfs_init_kernel(Params P) {
         b0[wp] = sbit;
         b1[wp] = 0ull;
     }
-    if (blockIdx.x == 0) {
-        // every counter of every slot, then the source as the level-0 frontier
-        for (int i = threadIdx.x; i < NSLOTS * NCTR; i += BLOCK)
-            P.ctr[(size_t)i * CTR_STRIDE] = 0ull;
-        if (threadIdx.x == 0) {
-            P.ctl->done = 0; P.ctl->L = 0; P.ctl->err = 0; P.ctl->err_info = 0;
-            for (int i = 0; i < RAN_CAP; ++i) P.ctl->ran[i] = 0;
-            P.ctl->lvl[0] = 0; P.ctl->lvl[1] = 0;
-            P.ctl->kmask = 0u;
-            for (int k = 0; k < NSLOTS; ++k) {
-                P.ctl->slot[k].dir = 0; P.ctl->slot[k].wbits = 0; P.ctl->slot[k].wcf = 0;
-                P.ctl->slot[k].input_bm = 0; P.ctl->slot[k].fsize = 0; P.ctl->slot[k].noq = 0;
-                P.ctl->slot[k].reached_before = 0; P.ctl->slot[k].edges_before = 0;
+    const Level0 l0 = level0_here(P, d);
+    if (!l0.on) return;
+    // level 0's changes to what this workgroup wrote: an entry is rewritten
+    // by the workgroup of the thread that wrote it (entry e of a grid-stride
+    // loop: thread e % nth), once its own stores are ordered before by the
+    // barrier (each thread's fill stores complete before it)
+    for (int j = threadIdx.x; j < d; j += BLOCK) nsrc[j] = P.col_idx[sb + j];
+    // (a wait for this thread's stores, not an agent-scope release: that
+    // would write back the whole L2 of the workgroup's die)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int me = blockIdx.x;
+    auto mine = [&](int64_t e) { return (int)((e % nth) / BLOCK) == me; };
+    for (int j = threadIdx.x; j < d; j += BLOCK) {
+        const int v = nsrc[j];
+        if ((uint32_t)v >= (uint32_t)P.n) continue;
+        const int pv = j > 0 ? nsrc[j - 1] : -1;
+        if (v != s && pv != v) {
+            // dist and parent: quad v/4 of the vector loop, else entry v - 4*lim of the scalar one
+            const int64_t e = ((v >> 2) < lim) ? (int64_t)(v >> 2) : (int64_t)v - 4LL * lim;
+            if ((fill || P.parent) && mine(e)) {
+                if (fill) P.dist[v] = 1;
+                if (P.parent) P.parent[v] = s;
             }
+#ifdef FBFS_COUNT_ENQUEUES
+            if (P.enq && mine(v)) P.enq[v] = 1;   // level 0's winner, enqueued once
+#endif
         }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            Ctx c;
-            c.P = &P; c.sh = nullptr; c.level = -1; c.wg = 0; c.G = 1; c.stripe = 0; c.nslot = 0; c.wbits = 0;
-            c.nbm = nullptr; c.ncf = nullptr; c.wcf = 0; c.noq = 0; c.nq = P.q0; c.nt = P.t0; c.nts = P.ts0; c.fcnt = 0; c.fdeg = 0;
-            c.region = nullptr; c.converting = 0;
-            const int beg = P.row_ptr[s];
-            const int len = P.row_ptr[s + 1] - beg;
-            const int l = list_of(len);
-            if (l >= 0) {
-                const int nseg = (l == L_TILE) ? (len + TILE - 1) / TILE : 1;
-                P.ctr[(size_t)(l * STRIPES) * CTR_STRIDE] =
-                    ((unsigned long long)nseg << 32) | (unsigned)len;
-                write_vertex_segments(c, l, s, beg, len, 0, 0);
+        // the visited and next-frontier word of v, from the first entry in it
+        const int wp = v >> 6;
+        if ((j == 0 || (pv >> 6) != wp || pv < 0) && mine(wp)) {
+            uint64_t nb = 0ull;
+            for (int jj = j; jj < d && nsrc[jj] >= 0 && (nsrc[jj] >> 6) == wp; ++jj)
+                if (nsrc[jj] != s && nsrc[jj] < P.n) nb |= 1ull << (nsrc[jj] & 63);
+            const uint64_t sbit = (wp == (s >> 6)) ? (1ull << (s & 63)) : 0ull;
+            vis64[wp] = init64[wp] | sbit | nb;
+            if (l0.wb) b1[wp] = nb;
+        }
+        // level 1's coarse map word (map 1), from the first entry in it
+        if (l0.wcf) {
+            const int cw = (int)(((uint32_t)v >> P.cf_sh) >> 5);
+            const bool first = j == 0 || pv < 0 || (int)(((uint32_t)pv >> P.cf_sh) >> 5) != cw;
+            if (first && mine(CF_WORDS + cw)) {
+                uint32_t w = 0u;
+                for (int jj = j; jj < d && nsrc[jj] >= 0 && (int)(((uint32_t)nsrc[jj] >> P.cf_sh) >> 5) == cw; ++jj)
+                    if (nsrc[jj] != s && nsrc[jj] < P.n) w |= 1u << (((uint32_t)nsrc[jj] >> P.cf_sh) & 31u);
+                P.cf[CF_WORDS + cw] = w;
             }
-            P.ctr[(size_t)VC_BASE * CTR_STRIDE] = (1ull << 32) | (unsigned)len;
         }
     }
+    // level 0's frontier bitmap is read only when level 0 pulls: the source's bit goes
+    if (threadIdx.x == 0 && mine(s >> 6)) b0[s >> 6] = 0ull;
 }
 
 // Decision for level k, taken by wavefront 0 of every workgroup from the
 // counters the previous level left (identical in every workgroup); the
 // caller synchronises before reading it.
-// A top-down level whose frontier has fewer edges than this never turns to
-// pull: a pull level passes over every vertex, which costs more than pushing
-// a few edges, even when the edges left unexplored are fewer still (the last
-// levels of a long search; on the grid they flipped direction every level).
-__device__ __forceinline__ int64_t pull_floor(const Params &P) { return (int64_t)P.n >> 14; }
 
 __device__ __forceinline__ void decide(const Params &P, LevelCommon &sh, int k) {
     const int lane = lane_id();
@@ -2169,7 +2343,8 @@ hipError_t launch_facts_reset(GraphFacts *f, hipStream_t s) {
 }
 
 hipError_t launch_init(const Params &P, int grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-    hipExtLaunchKernelGGL(bfs_init_kernel, dim3(grid), dim3(BLOCK), 0, s, start, stop, 0, P);
+    // grid fill workgroups and the control one
+    hipExtLaunchKernelGGL(bfs_init_kernel, dim3(grid + 1), dim3(BLOCK), 0, s, start, stop, 0, P);
     return hipGetLastError();
 }
 

@@ -169,6 +169,7 @@ struct Params {
                               // control block's kmask) instead of storing their dist; the
                               // finishing pass then writes dist once, in vertex order
     int32_t fill_dist;        // the init kernel fills dist with -1 (paths without the finishing pass)
+    int32_t l0_init;          // rows are sorted: the init kernel may run level 0 itself
     uint32_t *fbm0, *fbm1;    // frontier bitmaps, 2*nwp words each
     Seg *q0, *q1;             // queue storage, queue_segs(n) segments each (chunks of 2^qk_sh)
     Seg *t0, *t1;             // STRIPES regions of tcap tiles
