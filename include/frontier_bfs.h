@@ -147,7 +147,11 @@ int32_t bfs_last_error_code(void);
 /* Level loop.  Level launches go to a top-down kernel or a bottom-up kernel;
  * each reads the level to run and the frontier from device memory, runs that
  * level if its direction is the kernel's own and otherwise leaves it to the
- * next launch.
+ * next launch.  Level 0 itself runs in the initialisation launch when the
+ * graph's rows are sorted, the source has at most 256 entries and that level
+ * is top-down under the policy (its winners are the source's distinct
+ * out-neighbours, so no claim is needed); the first level launch then starts
+ * at level 1.
  *   DEVICE (default): launches are enqueued ahead in batches and the host
  *     waits once per batch; the first batch follows the handle's record of
  *     its recent searches' launches (else 12 alternating launches), later
@@ -246,7 +250,8 @@ int32_t bfs_set_timing(bfs_graph *g, int32_t on);
 
 /*
  * Milliseconds of the last timed bfs_run (host memory, any may be NULL):
- * init_ms = the initialisation launch and the finishing passes (the launch
+ * init_ms = the initialisation launch (with level 0 when it runs there, see
+ * the level loop above) and the finishing passes (the launch
  * after each batch of level launches that writes dist from the levels' kept
  * bitmaps once the search is done); level_ms = the level launches, each
  * timed alone (host waits between batches excluded); level_launches = level
@@ -287,7 +292,8 @@ int32_t bfs_last_run_launch_timing(const bfs_graph *g, int32_t cap, float *ms, u
  * Validator V5 of a debug build: copies to counts_out (device, n entries) how
  * many times each vertex was written into a next frontier during the last
  * bfs_run on this handle (a queue segment, a bitmap-only winner of a wide
- * top-down level, a bottom-up find); the source, the initial frontier, reads
+ * top-down level, a bottom-up find, a level-0 winner written by the
+ * initialisation launch); the source, the initial frontier, reads
  * 0.  On a correct search every other reached vertex reads exactly 1 and
  * every unreached vertex 0: a frontier with duplicates ("Day 38 - Graph
  * traversal on a GPU", Pitfalls; Chapter 22, section 22.1, where a naive
