@@ -148,7 +148,7 @@ int32_t bfs_last_error_code(void);
  * each reads the level to run and the frontier from device memory, runs that
  * level if its direction is the kernel's own and otherwise leaves it to the
  * next launch.  Level 0 itself runs in the initialisation launch when the
- * graph's rows are sorted, the source has at most 256 entries and that level
+ * graph's rows are sorted, the source has at most 512 entries and that level
  * is top-down under the policy (its winners are the source's distinct
  * out-neighbours, so no claim is needed); the first level launch then starts
  * at level 1.

@@ -1,12 +1,13 @@
-"""Level 0 in the init kernel: on sorted rows, a source of at most 256 entries
-whose level is top-down has its distinct out-neighbours written as level 0's
-winners by the init launch (the first level launch starts at level 1).  The
-cases around it: exactly 256 distinct neighbours (taken there) and 257 (a
-level launch takes level 0), a row with a self-loop and repeated entries, a
-neighbour of degree over 4096 (its queue pieces), a source with no
-out-edges, and unsorted rows (never taken there); each bit-exact against the
-oracle, with the default fill of dist and with the finishing pass.  Graphs of
-at least 3,585 vertices, so that the multi-workgroup path runs."""
+"""Level 0 in the init kernel: on sorted rows, a source of at most 512 entries
+(one per thread of a workgroup) whose level is top-down has its distinct
+out-neighbours written as level 0's winners by the init launch (the first
+level launch starts at level 1).  The cases around it: exactly 512 entries
+(taken there) and 513 (a level launch takes level 0), a row with a
+self-loop and repeated entries, a neighbour of degree over 2,048 (its queue
+pieces), a source with no out-edges, and unsorted rows (never taken there);
+each bit-exact against the oracle, with the default fill of dist and with
+the finishing pass.  Graphs of at least 3,585 vertices, so that the
+multi-workgroup path runs."""
 import contextlib
 import os
 
@@ -45,22 +46,22 @@ def _graph(name, n, edges, symmetric_closure, sources):
 def _level0_graph():
     n = 6000
     e = []
-    e += [(0, v) for v in range(1, 257)]            # source 0: 256 distinct neighbours
-    e += [(300, v) for v in range(301, 558)]        # source 300: 257
-    e += [(600, 600)]                               # source 600: a self-loop ...
-    e += [(600, v) for v in range(601, 611)]
-    e += [(600, v) for v in (601, 602, 603)]        # ... and repeated entries
-    e += [(1, v) for v in range(1000, 6000)]        # neighbour 1 of source 0: 5,000 edges
-    e += [(5999, 700)] + [(700 + i, 701 + i) for i in range(50)]   # a tail of levels
-    e += [(610, 2000), (556, 3000)]
-    return _graph("level0", n, e, True, [0, 300, 600, 1, 5, 700, 2500])
+    e += [(0, v) for v in range(1, 513)]            # source 0: 512 distinct neighbours
+    e += [(1000, v) for v in range(1001, 1514)]     # source 1000: 513
+    e += [(2000, 2000)]                             # source 2000: a self-loop ...
+    e += [(2000, v) for v in range(2001, 2011)]
+    e += [(2000, v) for v in (2001, 2002, 2003)]    # ... and repeated entries
+    e += [(1, v) for v in range(3000, 6000)]        # neighbour 1 of source 0: 3,000 edges
+    e += [(5999, 2500)] + [(2500 + i, 2501 + i) for i in range(50)]   # a tail of levels
+    e += [(2010, 3000), (1513, 4000)]
+    return _graph("level0", n, e, True, [0, 1000, 2000, 1, 5, 2500, 4500])
 
 
 @pytest.mark.parametrize("finish", [False, True])
 def test_level0_in_init(finish):
     g = _level0_graph()
     assert g.symmetric
-    assert np.diff(g.row_ptr)[0] == 256 and np.diff(g.row_ptr)[300] == 257
+    assert np.diff(g.row_ptr)[0] == 512 and np.diff(g.row_ptr)[1000] == 513
     ctx = finish_from(0) if finish else contextlib.nullcontext()
     with ctx:
         check_graph(g, label=f"level0 finish={finish}")
@@ -90,7 +91,7 @@ def test_level0_unsorted_rows():
     g = _level0_graph()
     col = g.col_idx.copy()
     rng = np.random.default_rng(3)
-    for u in (0, 600, 5):
+    for u in (0, 2000, 5):
         a, b = g.row_ptr[u], g.row_ptr[u + 1]
         col[a:b] = rng.permutation(col[a:b])
     h = gg.Graph("level0 unsorted", g.row_ptr, col, False, g.sources)
