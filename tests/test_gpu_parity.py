@@ -91,12 +91,12 @@ def test_c4_workload():
     check_graph(g, policies=["auto", "push_edge"])
 
 
-def test_c5_workload_sampled():
+def test_c5_workload_all_sources():
     """R-MAT scale 24 at full size, in the benchmark's configuration (auto
-    policy, parents and level sizes written), on the first 16 of its 64
-    sources; the other policies on two more."""
+    policy, parents and level sizes written), on all 64 of its sources (the
+    oracle on 16 host threads); the other policies on two of them."""
     g = gg.c5_rmat24(nsrc=64)
-    assert check_sources_parallel(g, g.sources[:16]) == 16
+    assert check_sources_parallel(g, g.sources, chunk=16, workers=16) == 64
     check_graph(g, sources=g.sources[16:18], policies=["push_binned", "push_edge", "pull", "auto_chain"])
 
 
